@@ -1,0 +1,131 @@
+"""CPU oracle for the sparse MoE block forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline`` leg may
+import this package. It is the plain per-token definition in C with double accumulation
+(``moe_oracle.c`` states each step and the passage it follows) behind a ctypes wrapper, and it
+shares no code with the GPU library.
+
+Arrays are numpy: float32 for fp32 data, uint16 bf16 bit patterns for bf16 data.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32, BF16 = 0, 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        lib.moe_oracle_router.argtypes = [i64, i32, i32, i32, i32, i32, p, p, p, p, p, p, p]
+        lib.moe_oracle_router.restype = ctypes.c_int
+        lib.moe_oracle_forward.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32, p, p, p,
+                                           p, p, p, p, p, p, p, p, p, p]
+        lib.moe_oracle_forward.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _dtype_of(a):
+    a = np.asarray(a)
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle arrays are float32 or uint16 (bf16 bits), got %s" % a.dtype)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def router(x, w_router, k, renorm=True, bias=None):
+    """Router, top-k and routing weights.
+
+    Returns (topk_idx int32 [T,k] by descending logit, topk_w float64 [T,k], gap float64 [T],
+    logits float32 [T,E])."""
+    dt = _dtype_of(x)
+    x = _c(x, np.float32 if dt == F32 else np.uint16)
+    w_router = _c(w_router, np.float32)
+    T, d = x.shape
+    E = w_router.shape[1]
+    assert w_router.shape == (d, E)
+    b = None if bias is None else _c(bias, np.float32)
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    gap = np.empty(T, np.float64)
+    logits = np.empty((T, E), np.float32)
+    rc = _load().moe_oracle_router(T, d, E, k, int(bool(renorm)), dt, x.ctypes.data, w_router.ctypes.data,
+                                   None if b is None else b.ctypes.data, logits.ctypes.data, idx.ctypes.data,
+                                   w.ctypes.data, gap.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("moe_oracle_router failed: %d" % rc)
+    return idx, w, gap, logits
+
+
+def forward(x, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renorm=True, bias=None):
+    """Whole MoE block for every row of x.
+
+    wg, wu, wd: either full arrays [E,d,I] / [E,I,d] or sequences of E per-expert 2-D arrays where
+    an entry may be None when no token of x selects that expert. wg_s/wu_s/wd_s: shared expert
+    ([d,Is], [d,Is], [Is,d]) or None for no shared expert.
+
+    Returns (out float64 [T,d], topk_idx, topk_w, gap)."""
+    dt = _dtype_of(x)
+    npdt = np.float32 if dt == F32 else np.uint16
+    x = _c(x, npdt)
+    w_router = _c(w_router, np.float32)
+    T, d = x.shape
+    E = w_router.shape[1]
+    keep = []
+
+    def per_expert(w):
+        ptrs = (ctypes.c_void_p * E)()
+        for e in range(E):
+            m = w[e]
+            if m is None:
+                ptrs[e] = None
+            else:
+                m = _c(m, npdt)
+                keep.append(m)
+                ptrs[e] = m.ctypes.data
+        return ptrs
+
+    I = next(m for m in wg if m is not None).shape[1]
+    pg, pu, pd = per_expert(wg), per_expert(wu), per_expert(wd)
+    if wg_s is None:
+        Is, sg, su, sd = 0, None, None, None
+    else:
+        wg_s, wu_s, wd_s = _c(wg_s, npdt), _c(wu_s, npdt), _c(wd_s, npdt)
+        Is = wg_s.shape[1]
+        assert wg_s.shape == (d, Is) and wu_s.shape == (d, Is) and wd_s.shape == (Is, d)
+        sg, su, sd = wg_s.ctypes.data, wu_s.ctypes.data, wd_s.ctypes.data
+    b = None if bias is None else _c(bias, np.float32)
+    out = np.empty((T, d), np.float64)
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    gap = np.empty(T, np.float64)
+    rc = _load().moe_oracle_forward(T, d, E, k, I, Is, int(bool(renorm)), dt, x.ctypes.data, w_router.ctypes.data,
+                                    None if b is None else b.ctypes.data, pg, pu, pd, sg, su, sd,
+                                    out.ctypes.data, idx.ctypes.data, w.ctypes.data, gap.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("moe_oracle_forward failed: %d" % rc)
+    return out, idx, w, gap
+
+
+TIE_BAND = 1e-5
+
+
+def flagged(gap):
+    """Tokens whose k-th and (k+1)-th fp32 logits are closer than the tie band; their expert set
+    is not unique to within rounding, so they are excluded from index and output comparisons."""
+    return np.asarray(gap) < TIE_BAND

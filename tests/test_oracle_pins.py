@@ -1,0 +1,303 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test checks the oracle against a library routine used independently (numpy float64 dense
+algebra, scipy's softmax), a brute-force enumeration, a closed form worked by hand, or an
+invariant the definition implies. A plausible mistake in the oracle (a dropped term, a wrong sign,
+a swapped index or operand, softmax over the wrong set, a wrong tie rule) fails at least one.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+import oracle
+import synthetic as syn
+
+
+def rand_layer(rng, T, d, E, I, Is, scale_r=None):
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = (rng.standard_normal((d, E)) * (scale_r or 1 / math.sqrt(d))).astype(np.float32)
+    wg = (rng.standard_normal((E, d, I)) / math.sqrt(d)).astype(np.float32)
+    wu = (rng.standard_normal((E, d, I)) / math.sqrt(d)).astype(np.float32)
+    wd = (rng.standard_normal((E, I, d)) / math.sqrt(I)).astype(np.float32)
+    if Is:
+        wgs = (rng.standard_normal((d, Is)) / math.sqrt(d)).astype(np.float32)
+        wus = (rng.standard_normal((d, Is)) / math.sqrt(d)).astype(np.float32)
+        wds = (rng.standard_normal((Is, d)) / math.sqrt(Is)).astype(np.float32)
+    else:
+        wgs = wus = wds = None
+    return x, wr, wg, wu, wd, wgs, wus, wds
+
+
+def dense_swiglu(x, wg, wu, wd):
+    """numpy float64 dense SwiGLU FFN, (silu(x Wg) * (x Wu)) Wd."""
+    x = x.astype(np.float64)
+    g = x @ wg.astype(np.float64)
+    u = x @ wu.astype(np.float64)
+    h = g / (1.0 + np.exp(-g)) * u
+    return h @ wd.astype(np.float64)
+
+
+# --------------------------------------------------------------------------------------------
+# router
+# --------------------------------------------------------------------------------------------
+def test_logits_match_numpy_float64():
+    rng = np.random.default_rng(1)
+    x, wr, *_ = rand_layer(rng, 33, 96, 24, 8, 0)
+    bias = rng.standard_normal(24).astype(np.float32)
+    idx, w, gap, logits = oracle.router(x, wr, 3, bias=bias)
+    ref = (x.astype(np.float64) @ wr.astype(np.float64) + bias.astype(np.float64)).astype(np.float32)
+    # both sum in double and round once; only the summation order may differ
+    ulp = np.spacing(np.abs(ref))
+    assert np.all(np.abs(logits.astype(np.float64) - ref) <= ulp)
+    assert np.mean(logits == ref) > 0.99
+
+
+def brute_force_topk(l, k):
+    """Exhaustive search over all k-subsets: the selected set is the one whose logits, sorted
+    descending, are lexicographically largest; among equal logit multisets the one with the
+    lexicographically smallest sorted index tuple."""
+    E = len(l)
+    best = None
+    for S in itertools.combinations(range(E), k):
+        key = (tuple(sorted((float(l[e]) for e in S), reverse=True)), tuple(-e for e in S))
+        if best is None or key > best[0]:
+            best = (key, S)
+    return set(best[1])
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (2, 1), (4, 2), (6, 3), (8, 3), (8, 8), (5, 4)])
+def test_topk_matches_brute_force(E, k):
+    rng = np.random.default_rng(100 + E * 10 + k)
+    x, wr, *_ = rand_layer(rng, 16, 8, E, 4, 0)
+    idx, w, gap, logits = oracle.router(x, wr, k)
+    for t in range(16):
+        assert set(idx[t].tolist()) == brute_force_topk(logits[t], k)
+        # listed by descending logit
+        assert np.all(np.diff(logits[t][idx[t]]) <= 0)
+        if k < E:
+            rest = np.delete(logits[t], idx[t])
+            assert gap[t] == pytest.approx(float(logits[t][idx[t][-1]]) - float(rest.max()), abs=0)
+        else:
+            assert math.isinf(gap[t])
+
+
+def test_topk_ties_go_to_lower_index():
+    # duplicate router columns give exactly equal logits
+    rng = np.random.default_rng(7)
+    d, E = 8, 6
+    base = rng.standard_normal((d, 3)).astype(np.float32)
+    wr = np.concatenate([base, base], axis=1)  # expert e and e+3 tie exactly
+    x = rng.standard_normal((20, d)).astype(np.float32)
+    for k in (1, 2, 3, 4, 5):
+        idx, w, gap, logits = oracle.router(x, wr, k)
+        for t in range(20):
+            assert set(idx[t].tolist()) == brute_force_topk(logits[t], k)
+    idx, w, gap, logits = oracle.router(x, wr, 1)
+    assert np.all(idx[:, 0] < 3)  # the lower of each tied pair wins
+    assert np.all(gap == 0.0)  # and the runner-up ties it exactly
+
+
+def test_weights_sum_to_one_with_renorm():
+    rng = np.random.default_rng(2)
+    x, wr, *_ = rand_layer(rng, 50, 32, 16, 4, 0)
+    idx, w, gap, logits = oracle.router(x, wr, 4, renorm=True)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(w > 0)
+    assert np.all(np.diff(w, axis=1) <= 0)  # weights follow the descending logits
+
+
+def test_weights_equal_softmax_of_kept_logits():
+    rng = np.random.default_rng(3)
+    x, wr, *_ = rand_layer(rng, 40, 32, 16, 4, 0)
+    idx, w, gap, logits = oracle.router(x, wr, 5, renorm=True)
+    kept = np.take_along_axis(logits.astype(np.float64), idx, axis=1)
+    np.testing.assert_allclose(w, softmax(kept, axis=1), rtol=1e-12, atol=0)
+
+
+def test_k_equals_E_is_full_softmax():
+    rng = np.random.default_rng(4)
+    x, wr, *_ = rand_layer(rng, 30, 16, 7, 4, 0)
+    idx, w, gap, logits = oracle.router(x, wr, 7, renorm=True)
+    p = softmax(logits.astype(np.float64), axis=1)
+    np.testing.assert_allclose(w, np.take_along_axis(p, idx, axis=1), rtol=1e-12)
+    assert np.all(np.isinf(gap))
+
+
+def test_no_renorm_gives_full_softmax_probabilities():
+    rng = np.random.default_rng(5)
+    x, wr, *_ = rand_layer(rng, 30, 16, 12, 4, 0, scale_r=1.0)
+    idx, w, gap, logits = oracle.router(x, wr, 3, renorm=False)
+    p = softmax(logits.astype(np.float64), axis=1)
+    np.testing.assert_allclose(w, np.take_along_axis(p, idx, axis=1), rtol=1e-12)
+    assert np.all(w.sum(axis=1) < 1.0)
+
+
+def test_indices_distinct_and_in_range():
+    cfg = syn.CONFIGS["tiny"]
+    x, wr = syn.host_x(cfg), syn.host_router(cfg)
+    idx, w, gap, logits = oracle.router(x, wr, cfg.k)
+    assert idx.min() >= 0 and idx.max() < cfg.E
+    assert all(len(set(r.tolist())) == cfg.k for r in idx)
+
+
+def test_constant_bias_changes_nothing_material():
+    rng = np.random.default_rng(6)
+    x, wr, *_ = rand_layer(rng, 64, 32, 16, 4, 0)
+    idx0, w0, gap0, _ = oracle.router(x, wr, 3)
+    idx1, w1, gap1, _ = oracle.router(x, wr, 3, bias=np.full(16, 0.375, np.float32))
+    ok = ~oracle.flagged(gap0)
+    assert ok.sum() > 50
+    np.testing.assert_array_equal(idx0[ok], idx1[ok])
+    np.testing.assert_allclose(w0[ok], w1[ok], rtol=1e-5)
+
+
+# --------------------------------------------------------------------------------------------
+# experts, shared expert, combine
+# --------------------------------------------------------------------------------------------
+def test_single_expert_is_dense_swiglu_plus_shared():
+    rng = np.random.default_rng(8)
+    x, wr, wg, wu, wd, wgs, wus, wds = rand_layer(rng, 12, 40, 1, 24, 16)
+    out, idx, w, gap = oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, k=1)
+    ref = dense_swiglu(x, wg[0], wu[0], wd[0]) + dense_swiglu(x, wgs, wus, wds)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    assert np.all(idx == 0) and np.all(w == 1.0)
+
+
+def test_routed_part_matches_per_token_numpy():
+    rng = np.random.default_rng(9)
+    T, d, E, k, I = 10, 24, 6, 2, 16
+    x, wr, wg, wu, wd, *_ = rand_layer(rng, T, d, E, I, 0)
+    out, idx, w, gap = oracle.forward(x, wr, wg, wu, wd, None, None, None, k=k)
+    for t in range(T):
+        ref = sum(w[t, j] * dense_swiglu(x[t:t + 1], wg[idx[t, j]], wu[idx[t, j]], wd[idx[t, j]])[0]
+                  for j in range(k))
+        np.testing.assert_allclose(out[t], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_identical_experts_ignore_routing():
+    rng = np.random.default_rng(10)
+    T, d, E, I, Is = 9, 16, 5, 8, 8
+    x, wr, wg, wu, wd, wgs, wus, wds = rand_layer(rng, T, d, E, I, Is)
+    wg[:] = wg[0]
+    wu[:] = wu[0]
+    wd[:] = wd[0]
+    out, *_ = oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, k=3)
+    ref = dense_swiglu(x, wg[0], wu[0], wd[0]) + dense_swiglu(x, wgs, wus, wds)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_down_projections():
+    rng = np.random.default_rng(11)
+    T, d, E, I, Is = 7, 16, 4, 8, 12
+    x, wr, wg, wu, wd, wgs, wus, wds = rand_layer(rng, T, d, E, I, Is)
+    out, *_ = oracle.forward(x, wr, wg, wu, np.zeros_like(wd), wgs, wus, wds, k=2)
+    np.testing.assert_allclose(out, dense_swiglu(x, wgs, wus, wds), rtol=1e-12, atol=1e-14)
+    out_routed, *_ = oracle.forward(x, wr, wg, wu, wd, None, None, None, k=2)
+    out_zero_shared, *_ = oracle.forward(x, wr, wg, wu, wd, wgs, wus, np.zeros_like(wds), k=2)
+    np.testing.assert_allclose(out_zero_shared, out_routed, rtol=1e-14, atol=0)
+
+
+def test_linear_in_down_projections():
+    rng = np.random.default_rng(12)
+    T, d, E, I, Is = 7, 16, 4, 8, 8
+    x, wr, wg, wu, wd, wgs, wus, wds = rand_layer(rng, T, d, E, I, Is)
+    out1, *_ = oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, k=2)
+    out2, *_ = oracle.forward(x, wr, wg, wu, 2 * wd, wgs, wus, 2 * wds, k=2)
+    np.testing.assert_allclose(out2, 2 * out1, rtol=1e-13, atol=1e-15)
+
+
+def test_hand_worked_example():
+    """d=2, E=2, k=1, I=1, shared I=1, all by hand.
+    x = (1, 0); W_r = [[2, 0], [0, 0]] gives logits (2, 0), so expert 0 with weight 1.
+    Expert 0: W_g = (1, 0)^T, W_u = (3, 0)^T, W_d = (1, -1): g = 1, u = 3,
+      h = silu(1) * 3 = 3 / (1 + e^-1), y = (h, -h).
+    Shared: W_g = (0, 0)^T gives g = 0 and silu(0) = 0, so it adds nothing.
+    Without renormalisation the weight is softmax(2, 0)[0] = 1 / (1 + e^-2)."""
+    x = np.array([[1.0, 0.0]], np.float32)
+    wr = np.array([[2.0, 0.0], [0.0, 0.0]], np.float32)
+    wg = np.array([[[1.0], [0.0]], [[5.0], [5.0]]], np.float32)
+    wu = np.array([[[3.0], [0.0]], [[5.0], [5.0]]], np.float32)
+    wd = np.array([[[1.0, -1.0]], [[7.0, 7.0]]], np.float32)
+    wgs = np.zeros((2, 1), np.float32)
+    wus = np.ones((2, 1), np.float32)
+    wds = np.ones((1, 2), np.float32)
+    h = 3.0 / (1.0 + math.exp(-1.0))
+    out, idx, w, gap = oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, k=1, renorm=True)
+    assert idx[0, 0] == 0 and w[0, 0] == 1.0 and gap[0] == 2.0
+    np.testing.assert_allclose(out[0], [h, -h], rtol=1e-15)
+    out, idx, w, gap = oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, k=1, renorm=False)
+    p0 = 1.0 / (1.0 + math.exp(-2.0))
+    np.testing.assert_allclose(w[0, 0], p0, rtol=1e-15)
+    np.testing.assert_allclose(out[0], [p0 * h, -p0 * h], rtol=1e-15)
+
+
+# --------------------------------------------------------------------------------------------
+# whole-block invariants
+# --------------------------------------------------------------------------------------------
+def test_token_permutation_equivariance_bitwise():
+    cfg = syn.CONFIGS["tiny"]
+    x = syn.host_x(cfg)
+    wr = syn.host_router(cfg)
+    wg, wu, wd = syn.host_all_experts(cfg)
+    wgs, wus, wds = syn.host_shared(cfg)
+    out, idx, w, gap = oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, k=cfg.k)
+    perm = np.random.default_rng(13).permutation(cfg.T)
+    out_p, idx_p, w_p, gap_p = oracle.forward(x[perm], wr, wg, wu, wd, wgs, wus, wds, k=cfg.k)
+    assert np.array_equal(out_p, out[perm])
+    assert np.array_equal(idx_p, idx[perm])
+
+
+def test_expert_relabelling_invariance():
+    rng = np.random.default_rng(14)
+    T, d, E, I, Is = 20, 16, 8, 8, 8
+    x, wr, wg, wu, wd, wgs, wus, wds = rand_layer(rng, T, d, E, I, Is)
+    out, idx, w, gap = oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, k=3)
+    pi = rng.permutation(E)  # new expert e' holds old expert pi[e']
+    out2, idx2, w2, gap2 = oracle.forward(x, wr[:, pi], wg[pi], wu[pi], wd[pi], wgs, wus, wds, k=3)
+    ok = ~oracle.flagged(gap)
+    assert np.array_equal(pi[idx2[ok]], idx[ok])
+    # the softmax denominator is summed in expert order, so only rounding may differ
+    np.testing.assert_allclose(out2[ok], out[ok], rtol=1e-13, atol=1e-14)
+
+
+def test_zero_token_gives_zero_output():
+    rng = np.random.default_rng(15)
+    x, wr, wg, wu, wd, wgs, wus, wds = rand_layer(rng, 4, 16, 6, 8, 8)
+    x[2] = 0.0
+    out, idx, w, gap = oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, k=2)
+    assert np.all(out[2] == 0.0)
+    assert gap[2] == 0.0 and oracle.flagged(gap)[2]  # every logit is 0: all tie
+    assert list(idx[2]) == [0, 1]
+
+
+def test_bf16_inputs_equal_widened_fp32():
+    cfg = syn.CONFIGS["tiny"].with_(dtype=syn.BF16, T=16)
+    x = syn.host_x(cfg)
+    wr = syn.host_router(cfg)
+    wg, wu, wd = syn.host_all_experts(cfg)
+    wgs, wus, wds = syn.host_shared(cfg)
+    w = syn.bf16_bits_to_f32
+    a = oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, k=cfg.k)
+    b = oracle.forward(w(x), wr, w(wg), w(wu), w(wd), w(wgs), w(wus), w(wds), k=cfg.k)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_per_expert_pointers_allow_missing_unselected_experts():
+    cfg = syn.CONFIGS["tiny"]
+    x = syn.host_x(cfg)[:5]
+    wr = syn.host_router(cfg)
+    wg, wu, wd = syn.host_all_experts(cfg)
+    wgs, wus, wds = syn.host_shared(cfg)
+    full, idx, *_ = oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, k=cfg.k)
+    used = set(idx.ravel().tolist())
+    sel = lambda a: [a[e] if e in used else None for e in range(cfg.E)]  # noqa: E731
+    part, *_ = oracle.forward(x, wr, sel(wg), sel(wu), sel(wd), wgs, wus, wds, k=cfg.k)
+    assert np.array_equal(part, full)
+    missing = [None] * cfg.E
+    missing[0] = wg[0]
+    with pytest.raises(RuntimeError):
+        oracle.forward(x, wr, missing, missing, missing, wgs, wus, wds, k=cfg.k)
