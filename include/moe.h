@@ -1,0 +1,162 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts block.
+ *
+ * One MoE block maps each token's hidden vector x_t (length d) to an output
+ * vector of the same length. The block is the one the Qwen3.6 / Qwen3.8-Max
+ * pages describe:
+ *   - a linear router gives one score (logit) per expert ("a small linear
+ *     network that takes the token embedding and produces one score per
+ *     expert": Qwen3.6 neural-network explorer page, section on the MoE router);
+ *   - a softmax over the experts and a per-token top-k keep the k most probable
+ *     experts (same section), optionally renormalising their k probabilities to
+ *     sum to one;
+ *   - each kept expert is a SwiGLU feed-forward network
+ *     y = (silu(x Wg) * (x Wu)) Wd without biases (hidden_act "silu",
+ *     moe_intermediate_size: Qwen3.8-Max architecture page, config.json
+ *     listing; the overview page's parameter table counts three d x I matrices
+ *     per expert), and the k outputs are summed with their routing weights;
+ *   - one shared expert of size shared_expert_intermediate_size runs on every
+ *     token and is added with no weight (explorer page, router section;
+ *     Qwen3-Next article on hyper.ai).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, owned by the caller, row-major
+ *     and densely packed. The library never allocates, frees or synchronises;
+ *     all work is enqueued in order on `stream` and its results are valid once
+ *     the stream reaches them. Device faults surface at the caller's next sync.
+ *   - Floating tensors of x, the expert weights, y and out have element type
+ *     dims->dtype (MOE_F32 = float, MOE_BF16 = bfloat16 bits); the router weight,
+ *     router bias, routing weights and gaps are always float; indices int32.
+ *   - Arguments are validated on the host before any launch. On failure the
+ *     call returns a non-zero moe_status, enqueues nothing, and
+ *     moe_last_error() describes the problem (thread-local text).
+ *   - Limits: T >= 0 (T = 0 is a no-op); 1 <= E <= 1024; 1 <= k <= min(E, 16);
+ *     T*k + T < 2^31; d, I multiples of 8 (>= 8); I_shared = 0 (no shared
+ *     expert) or a multiple of 8; renormalize 0 or 1. Float/bf16 tensors must be
+ *     16-byte aligned, int32/float vectors 4-byte aligned, the workspace 256-byte
+ *     aligned.
+ *   - `ws` is a caller-owned device scratch buffer of at least
+ *     moe_workspace_size() bytes. Any step may be given the same buffer; its
+ *     contents need no initialisation and are not meaningful to the caller.
+ *     Calls that share a workspace must not overlap in time (use one stream).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* bad pointer, size, alignment or dtype */
+  MOE_ERR_UNSUPPORTED = 2, /* valid in principle but beyond this library's limits */
+  MOE_ERR_WORKSPACE = 3,   /* ws missing or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4          /* a HIP launch failed; moe_last_error() has the HIP error text */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Shapes of one call. Names follow the model configuration: d = hidden_size,
+ * E = num_experts, k = num_experts_per_tok, I = moe_intermediate_size,
+ * I_shared = shared_expert_intermediate_size. */
+typedef struct {
+  int64_t T;           /* tokens in the batch */
+  int32_t d;           /* hidden size */
+  int32_t E;           /* routed experts */
+  int32_t k;           /* experts kept per token */
+  int32_t I;           /* routed expert intermediate size */
+  int32_t I_shared;    /* shared expert intermediate size, 0 = none */
+  int32_t dtype;       /* moe_dtype of x, expert weights, y and out */
+  int32_t renormalize; /* 1: the k routing weights are renormalised to sum to 1 */
+} moe_dims;
+
+/* Bytes of device workspace every entry point below needs for these dims. */
+moe_status moe_workspace_size(const moe_dims* dims, size_t* bytes);
+
+/* Router and softmax top-k (explorer page, router section).
+ *   x          [T, d]   dtype
+ *   w_router   [d, E]   float; logits l = x w_router (+ router_bias) in fp32
+ *   router_bias[E]      float or NULL
+ * Outputs:
+ *   topk_idx   [T, k]   int32, the k experts with the largest logits, by
+ *                       descending logit, ties to the lower index
+ *   topk_w     [T, k]   float, softmax probabilities over all E experts of the
+ *                       kept ones; divided by their sum when renormalize = 1
+ *   topk_gap   [T]      float or NULL: l_(k) - l_(k+1) (+inf when k = E), the
+ *                       margin that decides the selection */
+moe_status moe_router_topk(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
+                           int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* Dispatch: group the T*k (token, expert) pairs by expert.
+ *   topk_idx        [T, k]  int32 (from moe_router_topk)
+ * Outputs:
+ *   expert_offsets  [E + 1] int32, expert e owns sorted slots
+ *                           [expert_offsets[e], expert_offsets[e+1]); offsets[E] = T*k
+ *   sorted_token    [T*k]   int32, token of each sorted slot; within an expert,
+ *                           tokens ascend (stable)
+ *   slot_of         [T*k]   int32, slot_of[t*k + j] = sorted slot of (t, topk_idx[t, j]) */
+moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets,
+                       int32_t* sorted_token, int32_t* slot_of, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Routed and shared SwiGLU experts, each row once, unweighted.
+ *   x               [T, d]      dtype
+ *   expert_offsets, sorted_token: from moe_permute
+ *   wg, wu          [E, d, I]   dtype; wd [E, I, d] dtype
+ *   wg_s, wu_s      [d, I_shared], wd_s [I_shared, d] (ignored when I_shared = 0)
+ * Output:
+ *   y  [T*k + T, d] dtype (T*k rows when I_shared = 0): row s < T*k is expert
+ *      e's output for token sorted_token[s], where s lies in e's slot range;
+ *      row T*k + t is the shared expert's output for token t. */
+moe_status moe_grouped_ffn(const moe_dims* dims, const void* x, const int32_t* expert_offsets,
+                           const int32_t* sorted_token, const void* wg, const void* wu, const void* wd,
+                           const void* wg_s, const void* wu_s, const void* wd_s, void* y, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* Weighted combine plus shared expert:
+ *   out[t] = sum_j topk_w[t, j] * y[slot_of[t*k + j]]  +  y[T*k + t] (if I_shared > 0)
+ * summed in fp32 in the order j = 0..k-1 then the shared row; out [T, d] dtype. */
+moe_status moe_combine(const moe_dims* dims, const void* y, const int32_t* slot_of, const float* topk_w, void* out,
+                       hipStream_t stream);
+
+/* The whole block in one call: router/top-k, dispatch, experts, combine.
+ * topk_idx, topk_w, topk_gap may be NULL (then kept in the workspace). */
+moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
+                       const void* wg, const void* wu, const void* wd, const void* wg_s, const void* wu_s,
+                       const void* wd_s, void* out, int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Instrumentation for timing one kernel of the path while the whole path runs.
+ * The next moe_forward call made by the calling thread records `start` on its
+ * stream immediately before launching the selected kernel and `stop` right
+ * after it (hipEventRecord), then the request is cleared. Both events are
+ * caller-owned (hipEventCreate); pass kernel = MOE_KERNEL_NONE to cancel.
+ * Returns MOE_ERR_INVALID_ARG for an unknown kernel id or a NULL event. */
+typedef enum {
+  MOE_KERNEL_NONE = 0,
+  MOE_KERNEL_ROUTER = 1,       /* router logits GEMM (+ top-k kernel) */
+  MOE_KERNEL_PERMUTE = 2,      /* the three dispatch kernels */
+  MOE_KERNEL_FFN_GATE_UP = 3,  /* grouped gate/up GEMM with fused silu*mul */
+  MOE_KERNEL_FFN_DOWN = 4,     /* grouped down GEMM */
+  MOE_KERNEL_COMBINE = 5       /* weighted combine + shared add */
+} moe_kernel_id;
+
+moe_status moe_profile_next_forward(int32_t kernel, hipEvent_t start, hipEvent_t stop);
+
+/* Static name of a status code. */
+const char* moe_status_string(moe_status status);
+
+/* Detail text of the calling thread's last non-OK return ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

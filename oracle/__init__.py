@@ -31,6 +31,8 @@ def _load():
         lib.moe_oracle_forward.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32, p, p, p,
                                            p, p, p, p, p, p, p, p, p, p]
         lib.moe_oracle_forward.restype = ctypes.c_int
+        lib.moe_oracle_threads.argtypes = []
+        lib.moe_oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -120,6 +122,11 @@ def forward(x, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renorm=True, bias=None
     if rc != 0:
         raise RuntimeError("moe_oracle_forward failed: %d" % rc)
     return out, idx, w, gap
+
+
+def threads():
+    """Host threads the oracle's parallel loops use."""
+    return int(_load().moe_oracle_threads())
 
 
 TIE_BAND = 1e-5

@@ -37,6 +37,7 @@
  * supply only the experts the given tokens select (NULL for the others).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -233,3 +234,6 @@ int moe_oracle_forward(int64_t T, int32_t d, int32_t E, int32_t k, int32_t I, in
   }
   return err;
 }
+
+/* Threads the parallel regions above use (OpenMP's current maximum). */
+int moe_oracle_threads(void) { return omp_get_max_threads(); }

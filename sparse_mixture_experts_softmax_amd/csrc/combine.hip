@@ -1,0 +1,88 @@
+// Combine: the kept experts' outputs are summed with their routing weights
+// (Qwen3.6 neural-network explorer page, router section: the experts with the
+// highest weights process the token) and the always-active shared expert is
+// added with no weight (same section; Qwen3-Next article on hyper.ai).
+//
+//   out[t] = sum_{j<k} w[t,j] * y[slot_of[t*k+j]]  +  y[T*k + t]
+//
+// One 256-thread workgroup per token; each thread owns 8 consecutive hidden
+// elements (16-byte bf16 or 2x16-byte fp32 loads), accumulates in fp32 in the
+// fixed order j = 0..k-1 then the shared row, and rounds once on store.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ void load8(const bf16_t* p, float* v) {
+  const uint4 w = *(const uint4*)p;
+  v[0] = bf16lo_to_f32(w.x); v[1] = bf16hi_to_f32(w.x);
+  v[2] = bf16lo_to_f32(w.y); v[3] = bf16hi_to_f32(w.y);
+  v[4] = bf16lo_to_f32(w.z); v[5] = bf16hi_to_f32(w.z);
+  v[6] = bf16lo_to_f32(w.w); v[7] = bf16hi_to_f32(w.w);
+}
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const float4 a = *(const float4*)p;
+  const float4 b = *(const float4*)(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float* v) {
+  uint4 w;
+  w.x = pack_bf16x2(v[0], v[1]);
+  w.y = pack_bf16x2(v[2], v[3]);
+  w.z = pack_bf16x2(v[4], v[5]);
+  w.w = pack_bf16x2(v[6], v[7]);
+  *(uint4*)p = w;
+}
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+  *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <typename ET>
+__global__ void __launch_bounds__(256)
+combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, const float* __restrict__ topk_w,
+               ET* __restrict__ out, int64_t T, int d, int k, int has_shared) {
+  __shared__ int s_slot[16];
+  __shared__ float s_w[16];
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x < k) {
+    s_slot[threadIdx.x] = slot_of[t * k + threadIdx.x];
+    s_w[threadIdx.x] = topk_w[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  const int64_t shared_row = T * k + t;
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      float v[8];
+      load8(y + (int64_t)s_slot[j] * d + c, v);
+      const float w = s_w[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+    }
+    if (has_shared) {
+      float v[8];
+      load8(y + shared_row * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    store8(out + t * d + c, acc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_dims& dm, const void* y, const int32_t* slot_of, const float* topk_w,
+                          void* out, hipStream_t s) {
+  const int hs = dm.I_shared > 0 ? 1 : 0;
+  if (dm.dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3((unsigned)dm.T), dim3(256), 0, s, (const bf16_t*)y, slot_of,
+                       topk_w, (bf16_t*)out, dm.T, dm.d, dm.k, hs);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)dm.T), dim3(256), 0, s, (const float*)y, slot_of, topk_w,
+                       (float*)out, dm.T, dm.d, dm.k, hs);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,524 @@
+// Routed and shared SwiGLU experts as grouped GEMMs.
+//
+// Each expert is a feed-forward network with the silu activation and three
+// bias-free matrices, gate and up [d, I] and down [I, d] (Qwen3.8-Max
+// architecture page, config.json listing: hidden_act, moe_intermediate_size,
+// shared_expert_intermediate_size; the overview page's parameter table counts
+// 3*d*I per expert). For the rows of group g (expert g's sorted slots, or all T
+// tokens for the shared expert, g = E):
+//
+//   ffn1:  H = silu(A Wg) * (A Wu),  A = x gathered through sorted_token
+//   ffn2:  Y = H Wd
+//
+// bf16 path (gfx950 MFMA): 256-thread workgroups (4 wavefronts in 2x2) compute a
+// 128-row tile with v_mfma_f32_32x32x16_bf16, fp32 accumulation, K step 32,
+// double-buffered LDS. The weights are stored N-contiguous ([K, N] row-major),
+// while MFMA wants 8 consecutive K values per lane for both operands, so each
+// thread loads a 4(K) x 8(N) block of B with 16-byte loads, transposes it in
+// registers and writes it K-contiguous into LDS. ffn1 keeps the gate and up
+// accumulators of the same (row, column) in the same lane, so silu(g)*u is
+// applied in registers and H is written once in bf16.
+//
+// fp32 path: 64x64 tiles on the vector ALUs, 4x4 outputs per thread.
+//
+// Row tiles come from a device-built tile list (group, first row), so the host
+// launches an upper bound of tiles without knowing the routing; surplus
+// workgroups exit at once.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+struct Group {
+  int64_t row0;  // first sorted slot of the group
+  int rows;      // rows in the group
+  int n_inter;   // intermediate size of the group (I or I_shared)
+  bool shared;
+};
+
+__device__ __forceinline__ Group group_info(int g, const int32_t* offsets, int64_t T, int k, int E, int I, int Is) {
+  Group G;
+  if (g < E) {
+    G.row0 = offsets[g];
+    G.rows = offsets[g + 1] - offsets[g];
+    G.n_inter = I;
+    G.shared = false;
+  } else {
+    G.row0 = T * (int64_t)k;
+    G.rows = (int)T;
+    G.n_inter = Is;
+    G.shared = true;
+  }
+  return G;
+}
+
+// ------------------------------------------------------------------------------------------
+// tile list: for each group with n rows, ceil(n / BM) tiles (group, first row)
+// ------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024)
+build_tiles_kernel(const int32_t* __restrict__ offsets, int64_t T, int E, int has_shared, int BM,
+                   int32_t* __restrict__ tile_group, int32_t* __restrict__ tile_m0, int32_t* __restrict__ tile_count) {
+  __shared__ int s_val[2048];
+  __shared__ int s_tmp[1024];
+  const int tid = threadIdx.x;
+  const int G = E + has_shared;
+  for (int g = tid; g < G; g += 1024) {
+    const int64_t n = g < E ? (int64_t)(offsets[g + 1] - offsets[g]) : T;
+    s_val[g] = (int)((n + BM - 1) / BM);
+  }
+  __syncthreads();
+  // exclusive scan of G <= 1025 values, two per thread
+  const int a = 2 * tid < G ? s_val[2 * tid] : 0;
+  const int b = 2 * tid + 1 < G ? s_val[2 * tid + 1] : 0;
+  s_tmp[tid] = a + b;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? s_tmp[tid - off] : 0;
+    __syncthreads();
+    s_tmp[tid] += v;
+    __syncthreads();
+  }
+  const int excl = s_tmp[tid] - (a + b);
+  const int starts[2] = {excl, excl + a};
+  const int cnts[2] = {a, b};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int g = 2 * tid + h;
+    if (g < G) {
+      for (int i = 0; i < cnts[h]; ++i) {
+        tile_group[starts[h] + i] = g;
+        tile_m0[starts[h] + i] = i * BM;
+      }
+    }
+  }
+  if (tid == 1023) *tile_count = s_tmp[1023];
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16 MFMA grouped GEMM
+// ------------------------------------------------------------------------------------------
+constexpr int BM = kMfmaBM;  // 128 rows
+constexpr int BK = 32;       // K step
+constexpr int LDK = BK + 8;  // LDS row stride in bf16 (80 bytes) to spread banks
+constexpr int BNL = 256;     // LDS B tile columns: gate 128 + up 128, or 256 down columns
+
+struct MfmaArgs {
+  const bf16_t* a_src;  // ffn1: x [T, d]; ffn2: H [rows_total, ldh]
+  const int32_t* offsets;
+  const int32_t* sorted_token;
+  const bf16_t* w0;  // ffn1: Wg [E, d, I]; ffn2: Wd [E, I, d]
+  const bf16_t* w1;  // ffn1: Wu; ffn2: unused
+  const bf16_t* w0_s;
+  const bf16_t* w1_s;
+  bf16_t* out;  // ffn1: H; ffn2: Y
+  const int32_t* tile_group;
+  const int32_t* tile_m0;
+  const int32_t* tile_count;
+  int64_t T;
+  int d, E, k, I, Is, ldh;
+  int n_ntiles;
+};
+
+// Transpose a 4(K) x 8(N) block of bf16 (rows r[0..3], each 8 N-consecutive
+// values in a uint4) into 8 columns of 4 K-consecutive values (uint2 each).
+__device__ __forceinline__ void transpose4x8(const uint4 r[4], uint2 c[8]) {
+  const uint32_t* r0 = (const uint32_t*)&r[0];
+  const uint32_t* r1 = (const uint32_t*)&r[1];
+  const uint32_t* r2 = (const uint32_t*)&r[2];
+  const uint32_t* r3 = (const uint32_t*)&r[3];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    // columns 2p (low halves) and 2p+1 (high halves)
+    c[2 * p].x = (r0[p] & 0xFFFFu) | (r1[p] << 16);
+    c[2 * p].y = (r2[p] & 0xFFFFu) | (r3[p] << 16);
+    c[2 * p + 1].x = (r0[p] >> 16) | (r1[p] & 0xFFFF0000u);
+    c[2 * p + 1].y = (r2[p] >> 16) | (r3[p] & 0xFFFF0000u);
+  }
+}
+
+template <bool GATED>
+__global__ void __launch_bounds__(256, 2)
+ffn_mfma_kernel(MfmaArgs p) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM][LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BNL][LDK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;  // wave row block: rows wm*64 .. +64
+  const int wn = wave & 1;   // wave column block
+
+  const int mt = blockIdx.x / p.n_ntiles;
+  const int nt = blockIdx.x % p.n_ntiles;
+  if (mt >= *p.tile_count) return;
+  const int g = p.tile_group[mt];
+  const int m0 = p.tile_m0[mt];
+  const Group G = group_info(g, p.offsets, p.T, p.k, p.E, p.I, p.Is);
+
+  // problem sizes of this GEMM
+  const int K = GATED ? p.d : G.n_inter;
+  const int N = GATED ? G.n_inter : p.d;
+  const int n0 = nt * (GATED ? kMfmaBN1 : kMfmaBN2);
+  if (n0 >= N) return;
+
+  const bf16_t* W0;
+  const bf16_t* W1 = nullptr;
+  if (GATED) {
+    W0 = G.shared ? p.w0_s : p.w0 + (size_t)g * p.d * p.I;
+    W1 = G.shared ? p.w1_s : p.w1 + (size_t)g * p.d * p.I;
+  } else {
+    W0 = G.shared ? p.w0_s : p.w0 + (size_t)g * p.I * p.d;
+  }
+
+  // ---- A loader: rows tid/4 and tid/4 + 64, 8 K values at (tid%4)*8
+  const int a_kq = (tid & 3) * 8;
+  const bf16_t* a_ptr[2];
+  bool a_ok[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = (tid >> 2) + 64 * h;
+    a_ok[h] = m0 + r < G.rows;
+    int64_t src_row;
+    if (GATED)
+      src_row = G.shared ? (int64_t)(m0 + r) : (int64_t)p.sorted_token[G.row0 + m0 + (a_ok[h] ? r : 0)];
+    else
+      src_row = G.row0 + m0 + (a_ok[h] ? r : 0);
+    if (GATED && G.shared && !a_ok[h]) src_row = 0;
+    a_ptr[h] = p.a_src + src_row * (GATED ? (int64_t)p.d : (int64_t)p.ldh);
+  }
+  // ---- B loader: block (kb, nb): rows 4*kb .. +4, 8 columns
+  const int b_nb = tid & 31;
+  const int b_kb = tid >> 5;  // 0..7
+  const bf16_t* b_base;
+  int b_col;  // global column of this thread's 8-column block
+  int b_lds_n;
+  if (GATED) {
+    b_base = (b_nb < 16) ? W0 : W1;
+    b_col = n0 + (b_nb & 15) * 8;
+    b_lds_n = (b_nb >> 4) * 128 + (b_nb & 15) * 8;
+  } else {
+    b_base = W0;
+    b_col = n0 + b_nb * 8;
+    b_lds_n = b_nb * 8;
+  }
+  const bool b_col_ok = b_col < N;
+
+  uint4 ra[2];
+  uint4 rb[4];
+  auto load_tiles = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kk = k0 + a_kq;
+      ra[h] = (a_ok[h] && kk < K) ? *(const uint4*)(a_ptr[h] + kk) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int kk = k0 + b_kb * 4 + r;
+      rb[r] = (b_col_ok && kk < K) ? *(const uint4*)(b_base + (int64_t)kk * N + b_col) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tiles = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) *(uint4*)&As[buf][(tid >> 2) + 64 * h][a_kq] = ra[h];
+    uint2 c[8];
+    transpose4x8(rb, c);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *(uint2*)&Bs[buf][b_lds_n + j][b_kb * 4] = c[j];
+  };
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // LDS columns of the wave's four 32-wide B sub-tiles
+  int bcol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bcol[j] = GATED ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+
+  const int nk = (K + BK - 1) / BK;
+  load_tiles(0);
+  store_tiles(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_tiles((kt + 1) * BK);
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int kofs = s * 16 + (lane >> 5) * 8;
+      bf16x8_t a[2], b[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = *(const bf16x8_t*)&As[buf][wm * 64 + i * 32 + (lane & 31)][kofs];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8_t*)&Bs[buf][bcol[j] + (lane & 31)][kofs];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tiles(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue. 32x32 accumulator: lane holds column (lane & 31); register r
+  // holds row 8*(r/4) + 4*(lane/32) + (r%4).
+  const int col_in = lane & 31;
+  const int row_hi = (lane >> 5) * 4;
+  if (GATED) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int col = n0 + wn * 64 + jj * 32 + col_in;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          if (m0 + row < G.rows) {
+            const float gv = acc[i][jj][r];
+            const float uv = acc[i][jj + 2][r];
+            p.out[(G.row0 + m0 + row) * (int64_t)p.ldh + col] = f32_to_bf16(silu_f32(gv) * uv);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 128 + j * 32 + col_in;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          if (m0 + row < G.rows) p.out[(G.row0 + m0 + row) * (int64_t)p.d + col] = f32_to_bf16(acc[i][j][r]);
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// fp32 grouped GEMM (vector ALUs)
+// ------------------------------------------------------------------------------------------
+struct F32Args {
+  const float* a_src;
+  const int32_t* offsets;
+  const int32_t* sorted_token;
+  const float* w0;
+  const float* w1;
+  const float* w0_s;
+  const float* w1_s;
+  float* out;
+  const int32_t* tile_group;
+  const int32_t* tile_m0;
+  const int32_t* tile_count;
+  int64_t T;
+  int d, E, k, I, Is, ldh;
+  int n_ntiles;
+};
+
+template <bool GATED>
+__global__ void __launch_bounds__(256)
+ffn_f32_kernel(F32Args p) {
+  constexpr int TM = kF32BM, TN = kF32BN, TK = 16;
+  constexpr int NB = GATED ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) float As[TK][TM + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[NB][TK][TN + 4];
+
+  const int tid = threadIdx.x;
+  const int mt = blockIdx.x / p.n_ntiles;
+  const int nt = blockIdx.x % p.n_ntiles;
+  if (mt >= *p.tile_count) return;
+  const int g = p.tile_group[mt];
+  const int m0 = p.tile_m0[mt];
+  const Group G = group_info(g, p.offsets, p.T, p.k, p.E, p.I, p.Is);
+  const int K = GATED ? p.d : G.n_inter;
+  const int N = GATED ? G.n_inter : p.d;
+  const int n0 = nt * TN;
+  if (n0 >= N) return;
+
+  const float* Wb[2];
+  if (GATED) {
+    Wb[0] = G.shared ? p.w0_s : p.w0 + (size_t)g * p.d * p.I;
+    Wb[1] = G.shared ? p.w1_s : p.w1 + (size_t)g * p.d * p.I;
+  } else {
+    Wb[0] = G.shared ? p.w0_s : p.w0 + (size_t)g * p.I * p.d;
+    Wb[1] = nullptr;
+  }
+
+  const int al_r = tid / 4, al_k = (tid % 4) * 4;
+  const bool al_ok = m0 + al_r < G.rows;
+  int64_t src_row;
+  if (GATED)
+    src_row = G.shared ? (al_ok ? (int64_t)(m0 + al_r) : 0)
+                       : (int64_t)p.sorted_token[G.row0 + m0 + (al_ok ? al_r : 0)];
+  else
+    src_row = G.row0 + m0 + (al_ok ? al_r : 0);
+  const float* a_row = p.a_src + src_row * (GATED ? (int64_t)p.d : (int64_t)p.ldh);
+  const int bl_k = tid / 16, bl_c = (tid % 16) * 4;
+  const bool bl_ok = n0 + bl_c < N;
+
+  const int ty = tid / 16, tx = tid % 16;
+  float acc[NB][4][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[b][i][j] = 0.f;
+
+  for (int k0 = 0; k0 < K; k0 += TK) {
+    {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (al_ok && k0 + al_k < K) v = *(const float4*)(a_row + k0 + al_k);
+      As[al_k + 0][al_r] = v.x;
+      As[al_k + 1][al_r] = v.y;
+      As[al_k + 2][al_r] = v.z;
+      As[al_k + 3][al_r] = v.w;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (bl_ok && k0 + bl_k < K) v = *(const float4*)(Wb[b] + (int64_t)(k0 + bl_k) * N + n0 + bl_c);
+      *(float4*)&Bs[b][bl_k][bl_c] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TK; ++kk) {
+      const float4 a = *(const float4*)&As[kk][ty * 4];
+      const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float4 w = *(const float4*)&Bs[b][kk][tx * 4];
+        const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[b][i][j] = fmaf(av[i], wv[j], acc[b][i][j]);
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = ty * 4 + i;
+    if (m0 + row >= G.rows) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx * 4 + j;
+      if (col >= N) continue;
+      if (GATED)
+        p.out[(G.row0 + m0 + row) * (int64_t)p.ldh + col] = silu_f32(acc[0][i][j]) * acc[NB - 1][i][j];
+      else
+        p.out[(G.row0 + m0 + row) * (int64_t)p.d + col] = acc[0][i][j];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
+                              const int32_t* sorted_token, const void* wg, const void* wu, const void* wd,
+                              const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
+                              hipStream_t s, const Prof* prof) {
+  const Prof none;
+  if (!prof) prof = &none;
+  int32_t* tg = (int32_t*)(ws + L.tile_group);
+  int32_t* tm = (int32_t*)(ws + L.tile_m0);
+  int32_t* tc = (int32_t*)(ws + L.tile_count);
+  const int has_shared = dm.I_shared > 0 ? 1 : 0;
+  const int bm = dm.dtype == MOE_F32 ? kF32BM : kMfmaBM;
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, dm.T, dm.E, has_shared, bm, tg, tm, tc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // upper bound on row tiles: sum over groups of ceil(n_g / bm) <= (T*k)/bm + E + T/bm + 1
+  const int64_t max_mt = (dm.T * dm.k) / bm + dm.E + (has_shared ? dm.T / bm + 1 : 0);
+  const int nmax = dm.I > dm.I_shared ? dm.I : dm.I_shared;
+  char* H = ws + L.H;
+
+  if (dm.dtype == MOE_BF16) {
+    MfmaArgs a;
+    a.offsets = offsets;
+    a.sorted_token = sorted_token;
+    a.tile_group = tg;
+    a.tile_m0 = tm;
+    a.tile_count = tc;
+    a.T = dm.T;
+    a.d = dm.d;
+    a.E = dm.E;
+    a.k = dm.k;
+    a.I = dm.I;
+    a.Is = dm.I_shared;
+    a.ldh = L.ldh;
+    // ffn1: gate/up
+    a.a_src = (const bf16_t*)x;
+    a.w0 = (const bf16_t*)wg;
+    a.w1 = (const bf16_t*)wu;
+    a.w0_s = (const bf16_t*)wg_s;
+    a.w1_s = (const bf16_t*)wu_s;
+    a.out = (bf16_t*)H;
+    a.n_ntiles = (nmax + kMfmaBN1 - 1) / kMfmaBN1;
+    if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(ffn_mfma_kernel<true>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = prof->end(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
+    // ffn2: down
+    a.a_src = (const bf16_t*)H;
+    a.w0 = (const bf16_t*)wd;
+    a.w1 = nullptr;
+    a.w0_s = (const bf16_t*)wd_s;
+    a.w1_s = nullptr;
+    a.out = (bf16_t*)y;
+    a.n_ntiles = (dm.d + kMfmaBN2 - 1) / kMfmaBN2;
+    if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(ffn_mfma_kernel<false>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return prof->end(MOE_KERNEL_FFN_DOWN, s);
+  }
+
+  F32Args a;
+  a.offsets = offsets;
+  a.sorted_token = sorted_token;
+  a.tile_group = tg;
+  a.tile_m0 = tm;
+  a.tile_count = tc;
+  a.T = dm.T;
+  a.d = dm.d;
+  a.E = dm.E;
+  a.k = dm.k;
+  a.I = dm.I;
+  a.Is = dm.I_shared;
+  a.ldh = L.ldh;
+  a.a_src = (const float*)x;
+  a.w0 = (const float*)wg;
+  a.w1 = (const float*)wu;
+  a.w0_s = (const float*)wg_s;
+  a.w1_s = (const float*)wu_s;
+  a.out = (float*)H;
+  a.n_ntiles = (nmax + kF32BN - 1) / kF32BN;
+  if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(ffn_f32_kernel<true>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = prof->end(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
+  a.a_src = (const float*)H;
+  a.w0 = (const float*)wd;
+  a.w1 = nullptr;
+  a.w0_s = (const float*)wd_s;
+  a.w1_s = nullptr;
+  a.out = (float*)y;
+  a.n_ntiles = (dm.d + kF32BN - 1) / kF32BN;
+  if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(ffn_f32_kernel<false>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return prof->end(MOE_KERNEL_FFN_DOWN, s);
+}
+
+}  // namespace moe

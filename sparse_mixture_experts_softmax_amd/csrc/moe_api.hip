@@ -1,0 +1,291 @@
+// C ABI front end: argument validation, workspace layout and launch order.
+// Every check runs on the host before anything is enqueued; nothing here
+// allocates, frees or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+thread_local std::string g_last_error;
+thread_local Prof g_prof;  // one-shot request from moe_profile_next_forward
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_dims(const moe_dims* dm) {
+  if (!dm) return fail(MOE_ERR_INVALID_ARG, "dims is NULL");
+  if (dm->T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld < 0", (long long)dm->T);
+  if (dm->dtype != MOE_F32 && dm->dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "dtype %d is neither MOE_F32 (0) nor MOE_BF16 (1)", dm->dtype);
+  if (dm->renormalize != 0 && dm->renormalize != 1)
+    return fail(MOE_ERR_INVALID_ARG, "renormalize must be 0 or 1, got %d", dm->renormalize);
+  if (dm->E < 1) return fail(MOE_ERR_INVALID_ARG, "E = %d < 1", dm->E);
+  if (dm->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E = %d > 1024", dm->E);
+  if (dm->k < 1 || dm->k > dm->E) return fail(MOE_ERR_INVALID_ARG, "k = %d outside [1, E = %d]", dm->k, dm->E);
+  if (dm->k > 16) return fail(MOE_ERR_UNSUPPORTED, "k = %d > 16", dm->k);
+  if (dm->d < 8 || dm->d % 8) return fail(MOE_ERR_INVALID_ARG, "d = %d is not a positive multiple of 8", dm->d);
+  if (dm->I < 8 || dm->I % 8) return fail(MOE_ERR_INVALID_ARG, "I = %d is not a positive multiple of 8", dm->I);
+  if (dm->I_shared < 0 || dm->I_shared % 8)
+    return fail(MOE_ERR_INVALID_ARG, "I_shared = %d is not 0 or a positive multiple of 8", dm->I_shared);
+  const long long rows = (long long)dm->T * dm->k + dm->T;
+  if (dm->T > 0 && rows >= (1LL << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*k + T = %lld does not fit in int32", rows);
+  return MOE_OK;
+}
+
+moe_status check_ptr(const void* p, size_t align, const char* name, bool required = true) {
+  if (!p) return required ? fail(MOE_ERR_INVALID_ARG, "%s is NULL", name) : MOE_OK;
+  if (!aligned(p, align)) return fail(MOE_ERR_INVALID_ARG, "%s = %p is not %zu-byte aligned", name, p, align);
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                   \
+  do {                                  \
+    moe_status _st = (expr);            \
+    if (_st != MOE_OK) return _st;      \
+  } while (0)
+
+moe_status check_ws(const moe_dims& dm, const Layout& L, const void* ws, size_t ws_bytes) {
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+  if (!aligned(ws, 256)) return fail(MOE_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  (void)dm;
+  return MOE_OK;
+}
+
+}  // namespace
+
+Layout make_layout(const moe_dims& dm) {
+  Layout L;
+  const int64_t T = dm.T;
+  const int64_t Tk = T * dm.k;
+  const size_t esz = dm.dtype == MOE_F32 ? 4 : 2;
+  // Router: split the hidden dimension when the (token x expert) tiles alone
+  // would leave most of the 256 CUs idle.
+  const int64_t base_tiles = ((T + kRouterTileT - 1) / kRouterTileT) * ((dm.E + kRouterTileE - 1) / kRouterTileE);
+  int64_t splits = base_tiles > 0 ? (512 + base_tiles - 1) / base_tiles : 1;
+  const int64_t max_splits = dm.d / 256 > 0 ? dm.d / 256 : 1;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int64_t kchunk = (dm.d + splits - 1) / splits;
+  kchunk = (kchunk + kRouterKStep - 1) / kRouterKStep * kRouterKStep;
+  splits = (dm.d + kchunk - 1) / kchunk;
+  L.router_splits = (int)splits;
+  L.router_kchunk = (int)kchunk;
+  L.nchunks = (T + kPermuteChunk - 1) / kPermuteChunk;
+  const int smallest_bm = kF32BM;
+  L.max_tiles = Tk / smallest_bm + dm.E + T / smallest_bm + 2;
+  L.ldh = dm.I > dm.I_shared ? dm.I : dm.I_shared;
+  L.rows_total = Tk + (dm.I_shared > 0 ? T : 0);
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  L.logits = take((size_t)splits * T * dm.E * 4);
+  L.topk_idx = take((size_t)Tk * 4);
+  L.topk_w = take((size_t)Tk * 4);
+  L.topk_gap = take((size_t)T * 4);
+  L.chunk_counts = take((size_t)L.nchunks * dm.E * 4);
+  L.offsets = take((size_t)(dm.E + 2) * 4);
+  L.sorted_token = take((size_t)Tk * 4);
+  L.slot_of = take((size_t)Tk * 4);
+  L.tile_group = take((size_t)L.max_tiles * 4);
+  L.tile_m0 = take((size_t)L.max_tiles * 4);
+  L.tile_count = take(4);
+  L.H = take((size_t)L.rows_total * L.ldh * esz);
+  L.Y = take((size_t)L.rows_total * dm.d * esz);
+  L.total = off;
+  return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_profile_next_forward(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
+  if (kernel == MOE_KERNEL_NONE) {
+    g_prof = Prof();
+    return MOE_OK;
+  }
+  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_COMBINE)
+    return fail(MOE_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
+  if (!start || !stop) return fail(MOE_ERR_INVALID_ARG, "profile events must not be NULL");
+  g_prof.kernel = kernel;
+  g_prof.start = start;
+  g_prof.stop = stop;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_size(const moe_dims* dims, size_t* bytes) {
+  MOE_TRY(check_dims(dims));
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = make_layout(*dims).total;
+  return MOE_OK;
+}
+
+moe_status moe_router_topk(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
+                           int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& dm = *dims;
+  if (dm.T == 0) return MOE_OK;
+  MOE_TRY(check_ptr(x, 16, "x"));
+  MOE_TRY(check_ptr(w_router, 4, "w_router"));
+  MOE_TRY(check_ptr(router_bias, 4, "router_bias", false));
+  MOE_TRY(check_ptr(topk_idx, 4, "topk_idx"));
+  MOE_TRY(check_ptr(topk_w, 4, "topk_w"));
+  MOE_TRY(check_ptr(topk_gap, 4, "topk_gap", false));
+  const Layout L = make_layout(dm);
+  MOE_TRY(check_ws(dm, L, ws, ws_bytes));
+  hipError_t e = launch_router(dm, L, x, w_router, router_bias, topk_idx, topk_w, topk_gap, (char*)ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_router_topk");
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets, int32_t* sorted_token,
+                       int32_t* slot_of, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& dm = *dims;
+  if (dm.T == 0) return MOE_OK;
+  MOE_TRY(check_ptr(topk_idx, 4, "topk_idx"));
+  MOE_TRY(check_ptr(expert_offsets, 4, "expert_offsets"));
+  MOE_TRY(check_ptr(sorted_token, 4, "sorted_token"));
+  MOE_TRY(check_ptr(slot_of, 4, "slot_of"));
+  const Layout L = make_layout(dm);
+  MOE_TRY(check_ws(dm, L, ws, ws_bytes));
+  hipError_t e = launch_permute(dm, L, topk_idx, expert_offsets, sorted_token, slot_of, (char*)ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_permute");
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn(const moe_dims* dims, const void* x, const int32_t* expert_offsets,
+                           const int32_t* sorted_token, const void* wg, const void* wu, const void* wd,
+                           const void* wg_s, const void* wu_s, const void* wd_s, void* y, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& dm = *dims;
+  if (dm.T == 0) return MOE_OK;
+  MOE_TRY(check_ptr(x, 16, "x"));
+  MOE_TRY(check_ptr(expert_offsets, 4, "expert_offsets"));
+  MOE_TRY(check_ptr(sorted_token, 4, "sorted_token"));
+  MOE_TRY(check_ptr(wg, 16, "wg"));
+  MOE_TRY(check_ptr(wu, 16, "wu"));
+  MOE_TRY(check_ptr(wd, 16, "wd"));
+  const bool hs = dm.I_shared > 0;
+  MOE_TRY(check_ptr(wg_s, 16, "wg_s", hs));
+  MOE_TRY(check_ptr(wu_s, 16, "wu_s", hs));
+  MOE_TRY(check_ptr(wd_s, 16, "wd_s", hs));
+  MOE_TRY(check_ptr(y, 16, "y"));
+  const Layout L = make_layout(dm);
+  MOE_TRY(check_ws(dm, L, ws, ws_bytes));
+  hipError_t e = launch_grouped_ffn(dm, L, x, expert_offsets, sorted_token, wg, wu, wd, wg_s, wu_s, wd_s, y,
+                                    (char*)ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_grouped_ffn");
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_dims* dims, const void* y, const int32_t* slot_of, const float* topk_w, void* out,
+                       hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& dm = *dims;
+  if (dm.T == 0) return MOE_OK;
+  MOE_TRY(check_ptr(y, 16, "y"));
+  MOE_TRY(check_ptr(slot_of, 4, "slot_of"));
+  MOE_TRY(check_ptr(topk_w, 4, "topk_w"));
+  MOE_TRY(check_ptr(out, 16, "out"));
+  hipError_t e = launch_combine(dm, y, slot_of, topk_w, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_combine");
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
+                       const void* wg, const void* wu, const void* wd, const void* wg_s, const void* wu_s,
+                       const void* wd_s, void* out, int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& dm = *dims;
+  if (dm.T == 0) return MOE_OK;
+  MOE_TRY(check_ptr(x, 16, "x"));
+  MOE_TRY(check_ptr(w_router, 4, "w_router"));
+  MOE_TRY(check_ptr(router_bias, 4, "router_bias", false));
+  MOE_TRY(check_ptr(wg, 16, "wg"));
+  MOE_TRY(check_ptr(wu, 16, "wu"));
+  MOE_TRY(check_ptr(wd, 16, "wd"));
+  const bool hs = dm.I_shared > 0;
+  MOE_TRY(check_ptr(wg_s, 16, "wg_s", hs));
+  MOE_TRY(check_ptr(wu_s, 16, "wu_s", hs));
+  MOE_TRY(check_ptr(wd_s, 16, "wd_s", hs));
+  MOE_TRY(check_ptr(out, 16, "out"));
+  MOE_TRY(check_ptr(topk_idx, 4, "topk_idx", false));
+  MOE_TRY(check_ptr(topk_w, 4, "topk_w", false));
+  MOE_TRY(check_ptr(topk_gap, 4, "topk_gap", false));
+  const Layout L = make_layout(dm);
+  MOE_TRY(check_ws(dm, L, ws, ws_bytes));
+  char* w = (char*)ws;
+  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(w + L.topk_idx);
+  float* tw = topk_w ? topk_w : (float*)(w + L.topk_w);
+  int32_t* offsets = (int32_t*)(w + L.offsets);
+  int32_t* sorted = (int32_t*)(w + L.sorted_token);
+  int32_t* slot = (int32_t*)(w + L.slot_of);
+  void* y = w + L.Y;
+  const Prof prof = g_prof;
+  g_prof = Prof();
+  hipError_t e;
+  if ((e = prof.begin(MOE_KERNEL_ROUTER, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  e = launch_router(dm, L, x, w_router, router_bias, idx, tw, topk_gap, w, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/router");
+  if ((e = prof.end(MOE_KERNEL_ROUTER, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  if ((e = prof.begin(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  e = launch_permute(dm, L, idx, offsets, sorted, slot, w, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/permute");
+  if ((e = prof.end(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  e = launch_grouped_ffn(dm, L, x, offsets, sorted, wg, wu, wd, wg_s, wu_s, wd_s, y, w, stream, &prof);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/grouped_ffn");
+  if ((e = prof.begin(MOE_KERNEL_COMBINE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  e = launch_combine(dm, y, slot, tw, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
+  if ((e = prof.end(MOE_KERNEL_COMBINE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Internal declarations shared by the MoE library's translation units:
+// workspace layout, element helpers and kernel launchers. Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------------------------------
+// element helpers
+// ------------------------------------------------------------------------------------------
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// round to nearest even; the values here are finite
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// ------------------------------------------------------------------------------------------
+// tiling constants shared by host and device
+// ------------------------------------------------------------------------------------------
+constexpr int kPermuteChunk = 256;     // tokens per permute workgroup
+constexpr int kRouterTileT = 64;       // router logits tile: tokens
+constexpr int kRouterTileE = 64;       // router logits tile: experts
+constexpr int kRouterKStep = 16;       // router K step
+constexpr int kMfmaBM = 128;           // bf16 grouped GEMM tile rows
+constexpr int kMfmaBN1 = 128;          // gate/up tile: intermediate columns (x2 for gate and up)
+constexpr int kMfmaBN2 = 256;          // down tile: hidden columns
+constexpr int kF32BM = 64;             // fp32 grouped GEMM tile rows
+constexpr int kF32BN = 64;             // fp32 grouped GEMM tile columns
+
+// ------------------------------------------------------------------------------------------
+// workspace layout: a pure function of the dims
+// ------------------------------------------------------------------------------------------
+struct Layout {
+  int router_splits;    // K splits of the router logits GEMM
+  int router_kchunk;    // hidden rows per split
+  int64_t nchunks;      // permute chunks
+  int64_t max_tiles;    // upper bound on grouped-GEMM row tiles (any BM >= 64)
+  int ldh;              // row stride of H = max(I, I_shared)
+  int64_t rows_total;   // T*k + (I_shared ? T : 0)
+  size_t logits, topk_idx, topk_w, topk_gap, chunk_counts, offsets, sorted_token, slot_of;
+  size_t tile_group, tile_m0, tile_count, H, Y;
+  size_t total;
+};
+
+Layout make_layout(const moe_dims& dm);
+
+// ------------------------------------------------------------------------------------------
+// optional event pair around one kernel (moe_profile_next_forward)
+// ------------------------------------------------------------------------------------------
+struct Prof {
+  int kernel = MOE_KERNEL_NONE;
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+  hipError_t begin(int which, hipStream_t s) const {
+    return kernel == which ? hipEventRecord(start, s) : hipSuccess;
+  }
+  hipError_t end(int which, hipStream_t s) const {
+    return kernel == which ? hipEventRecord(stop, s) : hipSuccess;
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// launchers (enqueue only; return hipSuccess or the launch error)
+// ------------------------------------------------------------------------------------------
+hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, const float* w_router,
+                         const float* bias, int32_t* topk_idx, float* topk_w, float* topk_gap, char* ws,
+                         hipStream_t s);
+
+hipError_t launch_permute(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, int32_t* offsets,
+                          int32_t* sorted_token, int32_t* slot_of, char* ws, hipStream_t s);
+
+hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
+                              const int32_t* sorted_token, const void* wg, const void* wu, const void* wd,
+                              const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
+                              hipStream_t s, const Prof* prof = nullptr);
+
+hipError_t launch_combine(const moe_dims& dm, const void* y, const int32_t* slot_of, const float* topk_w,
+                          void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,141 @@
+// Dispatch: the token is sent to each of its k selected experts (Qwen3.6
+// neural-network explorer page, router section). Here that becomes a stable
+// grouping of the T*k (token, expert) pairs by expert, so every expert's rows
+// are contiguous for the grouped GEMM:
+//
+//   permute_count   one workgroup per chunk of 256 tokens (one wavefront per 64).
+//                   Each wavefront builds, in LDS, a 64-bit mask per expert of
+//                   which of its lanes chose it (LDS atomic OR). A pair's rank in
+//                   the chunk is the popcount of the masks of earlier wavefronts
+//                   plus that of its own mask below its lane -- token order is
+//                   kept without any sort. Per-chunk expert counts go to HBM.
+//   permute_scan    one workgroup: per expert, an exclusive scan over chunks;
+//                   then an exclusive scan over experts gives expert_offsets.
+//   permute_scatter slot = chunk base of the expert + rank; writes slot_of and
+//                   sorted_token.
+// All integer work; results are deterministic.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = kPermuteChunk / 64;
+
+__global__ void __launch_bounds__(kPermuteChunk)
+permute_count_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int k, int32_t* __restrict__ rank,
+                     int32_t* __restrict__ chunk_counts) {
+  extern __shared__ unsigned long long mask[];  // [kWaves][E]
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kWaves * E; i += kPermuteChunk) mask[i] = 0ull;
+  __syncthreads();
+
+  const int64_t t = (int64_t)blockIdx.x * kPermuteChunk + tid;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[t * k + j];
+      if ((unsigned)e < (unsigned)E) atomicOr(&mask[w * E + e], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (t < T) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[t * k + j];
+      int r = 0;
+      if ((unsigned)e < (unsigned)E) {
+        for (int w2 = 0; w2 < w; ++w2) r += __popcll(mask[w2 * E + e]);
+        r += __popcll(mask[w * E + e] & below);
+      }
+      rank[t * k + j] = r;
+    }
+  }
+  for (int e = tid; e < E; e += kPermuteChunk) {
+    int c = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) c += __popcll(mask[w2 * E + e]);
+    chunk_counts[(int64_t)blockIdx.x * E + e] = c;
+  }
+}
+
+// Exclusive scan of n (<= 2048) values held two per thread across 1024 threads.
+__device__ void block_exclusive_scan_1024(int* s_val, int n, int* s_tmp, int* total) {
+  const int tid = threadIdx.x;
+  const int a = 2 * tid < n ? s_val[2 * tid] : 0;
+  const int b = 2 * tid + 1 < n ? s_val[2 * tid + 1] : 0;
+  s_tmp[tid] = a + b;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? s_tmp[tid - off] : 0;
+    __syncthreads();
+    s_tmp[tid] += v;
+    __syncthreads();
+  }
+  const int incl = s_tmp[tid];
+  const int excl = incl - (a + b);
+  if (2 * tid < n) s_val[2 * tid] = excl;
+  if (2 * tid + 1 < n) s_val[2 * tid + 1] = excl + a;
+  if (tid == 1023) *total = incl;
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(1024)
+permute_scan_kernel(int32_t* __restrict__ chunk_counts, int64_t nchunks, int E, int32_t* __restrict__ offsets) {
+  __shared__ int s_val[2048];
+  __shared__ int s_tmp[1024];
+  __shared__ int s_total;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) {
+    int run = 0;
+    for (int64_t c = 0; c < nchunks; ++c) {
+      const int v = chunk_counts[c * E + e];
+      chunk_counts[c * E + e] = run;
+      run += v;
+    }
+    s_val[e] = run;
+  }
+  __syncthreads();
+  block_exclusive_scan_1024(s_val, E, s_tmp, &s_total);
+  for (int e = tid; e < E; e += 1024) {
+    const int base = s_val[e];
+    offsets[e] = base;
+    for (int64_t c = 0; c < nchunks; ++c) chunk_counts[c * E + e] += base;
+  }
+  if (tid == 0) offsets[E] = s_total;
+}
+
+__global__ void __launch_bounds__(kPermuteChunk)
+permute_scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int k,
+                       const int32_t* __restrict__ chunk_counts, int32_t* __restrict__ slot_of,
+                       int32_t* __restrict__ sorted_token) {
+  const int64_t t = (int64_t)blockIdx.x * kPermuteChunk + threadIdx.x;
+  if (t >= T) return;
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[t * k + j];
+    if ((unsigned)e >= (unsigned)E) continue;
+    const int slot = chunk_counts[(int64_t)blockIdx.x * E + e] + slot_of[t * k + j];  // slot_of holds the rank
+    slot_of[t * k + j] = slot;
+    sorted_token[slot] = (int32_t)t;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, int32_t* offsets,
+                          int32_t* sorted_token, int32_t* slot_of, char* ws, hipStream_t s) {
+  int32_t* cc = (int32_t*)(ws + L.chunk_counts);
+  const size_t lds = sizeof(unsigned long long) * kWaves * (size_t)dm.E;
+  hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)L.nchunks), dim3(kPermuteChunk), lds, s, topk_idx, dm.T,
+                     dm.E, dm.k, slot_of, cc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, cc, L.nchunks, dm.E, offsets);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)L.nchunks), dim3(kPermuteChunk), 0, s, topk_idx, dm.T,
+                     dm.E, dm.k, cc, slot_of, sorted_token);
+  return hipGetLastError();
+}
+
+}  // namespace moe

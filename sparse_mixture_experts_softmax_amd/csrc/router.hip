@@ -1,0 +1,251 @@
+// Router and softmax top-k.
+//
+// The router is a linear map from the token's hidden vector to one score per
+// expert; a softmax over all experts gives each a probability and the k most
+// probable are kept (Qwen3.6 neural-network explorer page, section on the MoE
+// router). Selection is made on the fp32 logits (same order as the
+// probabilities), ties go to the lower expert index, and the kept
+// probabilities are optionally renormalised to sum to one.
+//
+// Two kernels:
+//   router_logits: fp32 GEMM  part[s][t][e] = sum_{i in split s} x[t,i] W_r[i,e]
+//                  64x64 (token x expert) tiles, 4x4 outputs per thread, LDS-staged,
+//                  split over the hidden dimension when there are too few tiles to
+//                  fill the chip (decode-sized batches);
+//   router_topk:   one 64-lane wavefront per token: sums the splits (+ bias) in a
+//                  fixed order, then k (+1 for the gap) rounds of a wave-wide
+//                  argmax built from cross-lane shuffles, then the softmax
+//                  normaliser as a wave-wide sum.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <typename XT>
+__device__ __forceinline__ void load_x4(const XT* p, float* v);
+
+template <>
+__device__ __forceinline__ void load_x4<float>(const float* p, float* v) {
+  float4 f = *(const float4*)p;
+  v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+}
+
+template <>
+__device__ __forceinline__ void load_x4<bf16_t>(const bf16_t* p, float* v) {
+  uint2 w = *(const uint2*)p;
+  v[0] = bf16lo_to_f32(w.x); v[1] = bf16hi_to_f32(w.x);
+  v[2] = bf16lo_to_f32(w.y); v[3] = bf16hi_to_f32(w.y);
+}
+
+// grid: (expert tiles, token tiles, splits); 256 threads
+template <typename XT>
+__global__ void __launch_bounds__(256)
+router_logits_kernel(const XT* __restrict__ x, const float* __restrict__ wr, float* __restrict__ part,
+                     int64_t T, int d, int E, int kchunk) {
+  constexpr int TT = kRouterTileT, TE = kRouterTileE, KS = kRouterKStep;
+  __shared__ float xs[KS][TT + 4];
+  __shared__ float wsm[KS][TE + 4];
+
+  const int tid = threadIdx.x;
+  const int e0 = blockIdx.x * TE;
+  const int64_t t0 = (int64_t)blockIdx.y * TT;
+  const int split = blockIdx.z;
+  const int kbeg = split * kchunk;
+  const int kend = min(d, kbeg + kchunk);
+
+  const int tx = tid % 16;  // experts tx*4 .. +4
+  const int ty = tid / 16;  // tokens  ty*4 .. +4
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+  // x tile loader: token tid/4, hidden kq = (tid%4)*4 .. +4
+  const int xl_t = tid / 4;
+  const int xl_k = (tid % 4) * 4;
+  const bool xl_ok = t0 + xl_t < T;
+  const XT* xrow = x + (xl_ok ? (t0 + xl_t) : 0) * (int64_t)d;
+  // W tile loader: hidden row tid/16, experts (tid%16)*4 .. +4
+  const int wl_k = tid / 16;
+  const int wl_e = (tid % 16) * 4;
+
+  for (int k0 = kbeg; k0 < kend; k0 += KS) {
+    {
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (xl_ok && k0 + xl_k < kend) load_x4<XT>(xrow + k0 + xl_k, v);  // d % 8 == 0: 4 in or all out
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[xl_k + i][xl_t] = v[i];
+    }
+    {
+      const int kk = k0 + wl_k;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + wl_e + i;
+        wsm[wl_k][wl_e + i] = (kk < kend && e < E) ? wr[(int64_t)kk * E + e] : 0.f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const float4 a = *(const float4*)&xs[kk][ty * 4];
+      const float4 b = *(const float4*)&wsm[kk][tx * 4];
+      const float av[4] = {a.x, a.y, a.z, a.w};
+      const float bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  float* out = part + (int64_t)split * T * E;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) out[t * E + e] = acc[i][j];
+    }
+  }
+}
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// One wavefront per token, 4 tokens per 256-thread workgroup.
+// NJ = ceil(E / 64) logits per lane (lane l holds experts l, l+64, ...).
+template <int NJ>
+__global__ void __launch_bounds__(256)
+router_topk_kernel(const float* __restrict__ part, int splits, const float* __restrict__ bias, int64_t T, int E,
+                   int k, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                   float* __restrict__ topk_gap) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave leaves together; no block-wide barrier below
+
+  float v[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E) {
+      float s = 0.f;
+      for (int sp = 0; sp < splits; ++sp) s += part[((int64_t)sp * T + t) * E + e];
+      if (bias) s += bias[e];
+      v[j] = s;
+    } else {
+      v[j] = -INFINITY;
+    }
+  }
+
+  const int rounds = k < E ? k + 1 : k;
+  uint32_t taken = 0;
+  float sel_v[17];
+  int sel_i[17];
+#pragma unroll
+  for (int r = 0; r < 17; ++r) {
+    sel_v[r] = -INFINITY;
+    sel_i[r] = 0x7fffffff;
+  }
+#pragma unroll
+  for (int r = 0; r < 17; ++r) {
+    if (r < rounds) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) {
+          bv = v[j];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      sel_v[r] = bv;
+      sel_i[r] = bi;
+    }
+  }
+
+  const float m = sel_v[0];
+  float z = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    if (lane + 64 * j < E) z += expf(v[j] - m);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+
+  float denom = z;
+  if (renorm) {
+    denom = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (r < k) denom += expf(sel_v[r] - m);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (r < k) {
+        topk_idx[t * k + r] = sel_i[r];
+        topk_w[t * k + r] = expf(sel_v[r] - m) / denom;
+      }
+    }
+    if (topk_gap) {
+      float g = INFINITY;
+#pragma unroll
+      for (int r = 1; r < 17; ++r)
+        if (r == k && k < E) g = sel_v[r - 1] - sel_v[r];
+      topk_gap[t] = g;
+    }
+  }
+}
+
+template <int NJ>
+hipError_t launch_topk(const float* part, int splits, const float* bias, int64_t T, int E, int k, int renorm,
+                       int32_t* idx, float* w, float* gap, hipStream_t s) {
+  const unsigned grid = (unsigned)((T + 3) / 4);
+  hipLaunchKernelGGL(router_topk_kernel<NJ>, dim3(grid), dim3(256), 0, s, part, splits, bias, T, E, k, renorm, idx,
+                     w, gap);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, const float* w_router,
+                         const float* bias, int32_t* topk_idx, float* topk_w, float* topk_gap, char* ws,
+                         hipStream_t s) {
+  float* part = (float*)(ws + L.logits);
+  const dim3 grid((unsigned)((dm.E + kRouterTileE - 1) / kRouterTileE),
+                  (unsigned)((dm.T + kRouterTileT - 1) / kRouterTileT), (unsigned)L.router_splits);
+  if (dm.dtype == MOE_F32)
+    hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, s, (const float*)x, w_router, part, dm.T,
+                       dm.d, dm.E, L.router_kchunk);
+  else
+    hipLaunchKernelGGL(router_logits_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x, w_router, part, dm.T,
+                       dm.d, dm.E, L.router_kchunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nj = (dm.E + 63) / 64;
+  const int sp = L.router_splits;
+  if (nj <= 1) return launch_topk<1>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, s);
+  if (nj <= 2) return launch_topk<2>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, s);
+  if (nj <= 4) return launch_topk<4>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, s);
+  if (nj <= 8) return launch_topk<8>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, s);
+  return launch_topk<16>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, s);
+}
+
+}  // namespace moe

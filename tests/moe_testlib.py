@@ -1,0 +1,124 @@
+"""Helpers for the GPU parity tests: inputs, oracle references on token samples, comparisons.
+
+The comparison rule: expert index sets must match exactly except for tokens the oracle flags
+(k-th and (k+1)-th fp32 logits closer than 1e-5); outputs must satisfy
+max|out - ref| <= tol * max|ref| over the non-flagged tokens, tol = 2e-2 for bf16 and 1e-5 for fp32.
+"""
+import numpy as np
+
+import oracle
+import synthetic as syn
+
+TOL = {syn.F32: 1e-5, syn.BF16: 2e-2}
+WEIGHT_ATOL = 1e-5
+
+
+def torch_dtype(cfg):
+    import torch
+    return torch.float32 if cfg.dtype == syn.F32 else torch.bfloat16
+
+
+def to_device(a, dtype, device="cuda"):
+    """numpy float32 or uint16 (bf16 bits) -> device tensor of the given torch dtype."""
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        assert dtype == torch.bfloat16
+        return torch.from_numpy(a.view(np.int16).copy()).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device).to(dtype)
+
+
+def to_host(t):
+    """Device tensor -> numpy (bf16 returned as float32 values)."""
+    import torch
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy()
+
+
+def host_inputs(cfg):
+    """All inputs on the host (small configs): dict of numpy arrays in the config's dtype."""
+    wg, wu, wd = syn.host_all_experts(cfg)
+    wgs, wus, wds = syn.host_shared(cfg)
+    return dict(x=syn.host_x(cfg), w_router=syn.host_router(cfg), bias=syn.router_bias(cfg), wg=wg, wu=wu, wd=wd,
+                wg_s=wgs, wu_s=wus, wd_s=wds)
+
+
+def device_from_host(h, cfg, device="cuda"):
+    import torch
+    dt = torch_dtype(cfg)
+    out = {}
+    for key, a in h.items():
+        if a is None:
+            out[key] = None
+        elif key in ("w_router", "bias"):
+            out[key] = to_device(a, torch.float32, device)
+        else:
+            out[key] = to_device(a, dt, device)
+    return out
+
+
+def run_forward(dev, cfg, ws=None):
+    import sparse_mixture_experts_softmax_amd as moe
+    return moe.moe_forward(dev["x"], dev["w_router"], dev["wg"], dev["wu"], dev["wd"], dev["wg_s"], dev["wu_s"],
+                           dev["wd_s"], cfg.k, renormalize=bool(cfg.renorm), router_bias=dev["bias"],
+                           return_routing=True, ws=ws)
+
+
+def oracle_full(h, cfg):
+    return oracle.forward(h["x"], h["w_router"], h["wg"], h["wu"], h["wd"], h["wg_s"], h["wu_s"], h["wd_s"], cfg.k,
+                          renorm=bool(cfg.renorm), bias=h["bias"])
+
+
+def oracle_sample(cfg, tokens):
+    """Oracle outputs for the given token rows of a config, generating only the x rows, the router
+    and the experts those tokens select on the host."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    x = syn.host_x(cfg, rows=tokens)
+    wr = syn.host_router(cfg)
+    bias = syn.router_bias(cfg)
+    idx, _, _, _ = oracle.router(x, wr, cfg.k, renorm=bool(cfg.renorm), bias=bias)
+    need = sorted(set(idx.ravel().tolist()))
+    wg = [None] * cfg.E
+    wu = [None] * cfg.E
+    wd = [None] * cfg.E
+    for e in need:
+        wg[e], wu[e], wd[e] = syn.host_expert(cfg, e)
+    wgs, wus, wds = syn.host_shared(cfg)
+    return oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, cfg.k, renorm=bool(cfg.renorm), bias=bias)
+
+
+def compare(cfg, out, idx, w, ref_out, ref_idx, ref_w, ref_gap, label=""):
+    """Checks one set of GPU rows against the oracle's. Returns a stats dict."""
+    out = np.asarray(out, dtype=np.float64)
+    idx = np.asarray(idx)
+    w = np.asarray(w, dtype=np.float64)
+    T, k = ref_idx.shape
+    flagged = oracle.flagged(ref_gap)
+    ok = ~flagged
+    # validity everywhere
+    assert idx.min() >= 0 and idx.max() < cfg.E, label
+    assert all(len(set(r.tolist())) == k for r in idx), label + ": repeated expert in a token"
+    if cfg.renorm:
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, atol=1e-5, err_msg=label)
+    # exact expert sets on non-flagged tokens
+    gi = np.sort(idx[ok], axis=1)
+    ri = np.sort(ref_idx[ok], axis=1)
+    bad = np.nonzero(np.any(gi != ri, axis=1))[0]
+    assert bad.size == 0, "%s: %d token(s) with a different expert set, first %s" % (label, bad.size, bad[:5])
+    # weights, matched by expert
+    go = np.argsort(idx[ok], axis=1)
+    ro = np.argsort(ref_idx[ok], axis=1)
+    gw = np.take_along_axis(w[ok], go, axis=1)
+    rw = np.take_along_axis(ref_w[ok], ro, axis=1)
+    werr = float(np.max(np.abs(gw - rw))) if gw.size else 0.0
+    assert werr <= WEIGHT_ATOL, "%s: routing weight error %g" % (label, werr)
+    # outputs
+    ref_max = float(np.max(np.abs(ref_out[ok]))) if ok.any() else 0.0
+    err = float(np.max(np.abs(out[ok] - ref_out[ok]))) if ok.any() else 0.0
+    tol = TOL[cfg.dtype]
+    assert err <= tol * ref_max, "%s: max|out-ref| = %g > %g * max|ref| = %g" % (label, err, tol, tol * ref_max)
+    return dict(flagged=int(flagged.sum()), max_err=err, max_ref=ref_max, rel=err / ref_max if ref_max else 0.0,
+                weight_err=werr)

@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+from moe_testlib import (compare, device_from_host, host_inputs, oracle_full, oracle_sample, run_forward, to_host,
+                         torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    assert _t.cuda.is_available(), "GPU tests need a GPU"
+    import sparse_mixture_experts_softmax_amd as moe
+    moe.load_library()
+    return _t
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------------------------------------
+# input generator: device fill equals host fill bit for bit
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [syn.F32, syn.BF16])
+def test_device_generator_matches_host(torch, dtype):
+    n, off = 3 * 1000003, 123457
+    tdt = torch.float32 if dtype == syn.F32 else torch.bfloat16
+    t = torch.empty(n, dtype=tdt, device="cuda")
+    syn.device_fill(t, 7, syn.TID_WG, 0.0123, offset=off)
+    h = syn.host_fill(n, dtype, 7, syn.TID_WG, 0.0123, offset=off)
+    g = t.view(torch.int32 if dtype == syn.F32 else torch.int16).cpu().numpy()
+    assert np.array_equal(g.view(h.dtype), h)
+
+
+# --------------------------------------------------------------------------------------------
+# whole block on small shapes, every token against the oracle
+# --------------------------------------------------------------------------------------------
+def _full_check(torch, cfg, label):
+    _say("case", label, cfg)
+    h = host_inputs(cfg)
+    dev = device_from_host(h, cfg)
+    out, idx, w, gap = run_forward(dev, cfg)
+    torch.cuda.synchronize()
+    ref_out, ref_idx, ref_w, ref_gap = oracle_full(h, cfg)
+    st = compare(cfg, to_host(out), to_host(idx), to_host(w), ref_out, ref_idx, ref_w, ref_gap, label)
+    # the GPU gap agrees with the oracle's where it matters
+    g = to_host(gap)
+    fin = np.isfinite(ref_gap)
+    assert np.all(np.isinf(g[~fin]))
+    assert np.max(np.abs(g[fin] - ref_gap[fin]), initial=0.0) < 1e-4
+    _say(label, st)
+    return st
+
+
+def test_tiny_fp32_config(torch):
+    st = _full_check(torch, syn.CONFIGS["tiny"], "tiny")
+    assert st["rel"] <= 1e-5
+
+
+SMALL_CASES = [
+    # name, T, d, E, k, I, Is, dtype, renorm, zipf
+    ("e1k1_dense", 37, 64, 1, 1, 32, 32, syn.BF16, 1, 0.0),
+    ("k_eq_E", 50, 128, 4, 4, 64, 0, syn.BF16, 1, 0.0),
+    ("ragged_bf16", 300, 264, 40, 3, 136, 72, syn.BF16, 1, 0.0),
+    ("ragged_f32", 300, 264, 40, 3, 136, 72, syn.F32, 1, 0.0),
+    ("no_renorm", 129, 256, 64, 6, 128, 128, syn.BF16, 0, 0.0),
+    ("no_shared_f32", 77, 96, 13, 5, 40, 0, syn.F32, 0, 0.0),
+    ("one_token", 1, 512, 32, 4, 256, 256, syn.BF16, 1, 0.0),
+    ("many_tiles", 700, 512, 16, 4, 384, 256, syn.BF16, 1, 0.0),
+    ("skewed_small", 512, 128, 64, 8, 64, 64, syn.BF16, 1, 1.2),
+    ("E65_k16", 200, 64, 65, 16, 24, 8, syn.F32, 1, 0.0),
+    ("wide_E", 96, 64, 1024, 16, 16, 16, syn.BF16, 1, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_small_shapes(torch, case):
+    name, T, d, E, k, I, Is, dt, rn, za = case
+    cfg = syn.MoEConfig(name, T=T, d=d, E=E, k=k, I=I, Is=Is, dtype=dt, renorm=rn, seed=11, zipf_alpha=za)
+    _full_check(torch, cfg, name)
+
+
+def test_zero_tokens_is_a_no_op(torch):
+    import sparse_mixture_experts_softmax_amd as moe
+    cfg = syn.CONFIGS["tiny"].with_(T=3)
+    dev = device_from_host(host_inputs(cfg), cfg)
+    x0 = dev["x"][:0]
+    out = torch.full((0, cfg.d), 7.0, device="cuda")
+    res = moe.moe_forward(x0, dev["w_router"], dev["wg"], dev["wu"], dev["wd"], dev["wg_s"], dev["wu_s"], dev["wd_s"],
+                          cfg.k, out=out)
+    torch.cuda.synchronize()
+    assert res.shape == (0, cfg.d)
+
+
+# --------------------------------------------------------------------------------------------
+# the four step entry points compose to moe_forward, bit for bit; permute is a stable sort
+# --------------------------------------------------------------------------------------------
+def test_steps_compose_and_permute_is_stable_sort(torch):
+    import sparse_mixture_experts_softmax_amd as moe
+    cfg = syn.MoEConfig("steps", T=600, d=256, E=48, k=6, I=128, Is=64, dtype=syn.BF16, seed=3)
+    h = host_inputs(cfg)
+    dev = device_from_host(h, cfg)
+    dims = moe.dims_for(dev["x"], dev["w_router"], dev["wg"], dev["wg_s"], cfg.k, True)
+    ws = moe.workspace(dims, "cuda")
+    idx, w, gap = moe.moe_router_topk(dims, dev["x"], dev["w_router"], None, ws)
+    offs, sorted_token, slot_of = moe.moe_permute(dims, idx, ws)
+    y = moe.moe_grouped_ffn(dims, dev["x"], offs, sorted_token, dev["wg"], dev["wu"], dev["wd"], dev["wg_s"],
+                            dev["wu_s"], dev["wd_s"], ws)
+    out = moe.moe_combine(dims, y, slot_of, w)
+    out2, idx2, w2, gap2 = run_forward(dev, cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(idx, idx2) and torch.equal(w, w2)
+
+    # dispatch against a host stable sort by (expert, token)
+    ih = to_host(idx).astype(np.int64)
+    flat_e = ih.reshape(-1)
+    flat_t = np.repeat(np.arange(cfg.T), cfg.k)
+    order = np.lexsort((flat_t, flat_e))  # expert major, token ascending
+    counts = np.bincount(flat_e, minlength=cfg.E)
+    exp_offs = np.concatenate([[0], np.cumsum(counts)])
+    exp_sorted = flat_t[order]
+    exp_slot = np.empty(cfg.T * cfg.k, np.int64)
+    exp_slot[order] = np.arange(cfg.T * cfg.k)
+    assert np.array_equal(to_host(offs), exp_offs)
+    assert np.array_equal(to_host(sorted_token), exp_sorted)
+    assert np.array_equal(to_host(slot_of), exp_slot)
+
+
+def test_deterministic_and_token_permutation_equivariant(torch):
+    cfg = syn.MoEConfig("perm", T=333, d=192, E=24, k=4, I=96, Is=64, dtype=syn.BF16, seed=5)
+    h = host_inputs(cfg)
+    dev = device_from_host(h, cfg)
+    out1, idx1, w1, _ = run_forward(dev, cfg)
+    out2, idx2, w2, _ = run_forward(dev, cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(idx1, idx2)
+    perm = torch.from_numpy(np.random.default_rng(0).permutation(cfg.T)).cuda()
+    dev_p = dict(dev)
+    dev_p["x"] = dev["x"][perm].contiguous()
+    out_p, idx_p, w_p, _ = run_forward(dev_p, cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out1[perm]) and torch.equal(idx_p, idx1[perm])
+
+
+# --------------------------------------------------------------------------------------------
+# the full-size configurations, in the launch configuration the benchmark times
+# --------------------------------------------------------------------------------------------
+def _device_inputs(cfg, cache={}):
+    """Device inputs; the three d=8192 configurations share identical weights (same seed and shapes)."""
+    key = (cfg.d, cfg.E, cfg.I, cfg.Is, cfg.dtype, cfg.seed)
+    if cache.get("key") != key:
+        cache.clear()
+        cache["key"] = key
+        cache["w"] = syn.device_inputs(cfg, with_x=False)
+    import torch
+    dev = dict(cache["w"])
+    dev["x"] = syn.device_fill(torch.empty(cfg.T, cfg.d, dtype=torch_dtype(cfg), device="cuda"), cfg.seed, syn.TID_X,
+                               1.0)
+    b = syn.router_bias(cfg)
+    dev["bias"] = None if b is None else torch.from_numpy(b).cuda()
+    return dev
+
+
+def _full_size_check(torch, name, n_sample):
+    cfg = syn.CONFIGS[name]
+    _say("config", cfg)
+    dev = _device_inputs(cfg)
+    out, idx, w, gap = run_forward(dev, cfg)
+    torch.cuda.synchronize()
+    idx_h, w_h = to_host(idx), to_host(w)
+    # properties on every token
+    assert idx_h.min() >= 0 and idx_h.max() < cfg.E
+    s = np.sort(idx_h, axis=1)
+    assert np.all(s[:, 1:] != s[:, :-1]), "repeated expert within a token"
+    np.testing.assert_allclose(w_h.sum(axis=1), 1.0, atol=1e-5)
+    assert np.all(np.isfinite(to_host(out)))
+    # oracle on a seeded token sample
+    rng = np.random.default_rng(1234)
+    tokens = np.sort(rng.choice(cfg.T, size=min(n_sample, cfg.T), replace=False))
+    ref_out, ref_idx, ref_w, ref_gap = oracle_sample(cfg, tokens)
+    st = compare(cfg, to_host(out)[tokens], idx_h[tokens], w_h[tokens], ref_out, ref_idx, ref_w, ref_gap, name)
+    load = np.bincount(idx_h.ravel(), minlength=cfg.E)
+    _say(name, st, "touched experts", int((load > 0).sum()), "max load", int(load.max()))
+    return cfg, idx_h, load
+
+
+def test_mid_config_router_all_tokens_and_sampled_outputs(torch):
+    cfg, idx_h, load = _full_size_check(torch, "mid", 384)
+    # router + top-k on every token against the oracle
+    x = syn.host_x(cfg)
+    ref_idx, _, ref_gap, _ = oracle.router(x, syn.host_router(cfg), cfg.k)
+    ok = ~oracle.flagged(ref_gap)
+    assert np.array_equal(np.sort(idx_h[ok], axis=1), np.sort(ref_idx[ok], axis=1))
+    _say("mid flagged tokens", int((~ok).sum()))
+
+
+def test_decode_config(torch):
+    cfg, idx_h, load = _full_size_check(torch, "decode", 8)
+    assert (load > 0).sum() > 150
+
+
+def test_prefill_config(torch):
+    _full_size_check(torch, "prefill", 8)
+
+
+def test_skew_config(torch):
+    cfg, idx_h, load = _full_size_check(torch, "skew", 8)
+    L = syn.zipf_targets(cfg.T, cfg.E, cfg.k, cfg.zipf_alpha)
+    # the heaviest experts take (almost) every token, the tail is light
+    assert load[0] >= 0.95 * cfg.T and load[1] >= 0.95 * cfg.T
+    assert np.corrcoef(np.log(load + 1), np.log(L + 1))[0, 1] > 0.95
