@@ -274,29 +274,41 @@ def zipf_targets(T, E, k, alpha):
 _bias_cache = {}
 
 
-def router_bias(cfg, iters=40, mc_seed=20240601):
+def router_bias(cfg, iters=30, mc_seed=20240601):
     """Per-expert fp32 router bias for Zipf-skewed loads, or None when cfg.zipf_alpha == 0.
 
-    Calibrated by Monte Carlo under the model the synthetic inputs obey: given a token, its logits
-    x.W_r[:, e] are i.i.d. N(0, |x|^2/d ~ 1) across experts. Starting from b = -alpha*ln(rank),
-    b is moved by half the log-ratio of target to simulated load; experts whose target is every
-    token get a fixed +10 (ten standard deviations above the rest)."""
+    Model of the synthetic inputs: a token's logit for expert e is s_t * sigma_e * z with z ~ N(0, 1)
+    independent across experts and tokens, sigma_e = |W_r[:, e]| (the generated router column's
+    norm) and s_t = |x_t| / sqrt(d). If every token kept exactly the experts above one common
+    threshold tau, expert e's share of tokens would be Q(tau - b_e), so the bias starts at
+    b_e = Phi^-1(L_e / T) for target load L_e; experts whose target is every token get +10.
+    Monte Carlo refinement on 4*T model tokens then moves each bias by the log-ratio of target to
+    simulated load divided by the local sensitivity d ln(load)/d b (the normal hazard rate), damped."""
     if cfg.zipf_alpha <= 0:
         return None
-    key = (cfg.T, cfg.E, cfg.k, cfg.zipf_alpha)
+    key = (cfg.T, cfg.d, cfg.E, cfg.k, cfg.zipf_alpha, cfg.seed)
     if key in _bias_cache:
         return _bias_cache[key]
+    from scipy.stats import norm
+
     T, E, k = cfg.T, cfg.E, cfg.k
     L = zipf_targets(T, E, k, cfg.zipf_alpha)
     capped = L >= T * (1 - 1e-12)
-    rng = np.random.default_rng(mc_seed)
-    Z = rng.standard_normal((T, E), dtype=np.float32)
-    b = -cfg.zipf_alpha * np.log(np.arange(1, E + 1, dtype=np.float64))
+    p = np.clip(L / T, 1e-9, 1 - 1e-9)
+    b = norm.ppf(p)
     b[capped] = 10.0
+    sigma = np.sqrt((host_router(cfg).astype(np.float64) ** 2).sum(axis=0))
+    rng = np.random.default_rng(mc_seed)
+    M = 4 * T
+    s = np.sqrt(rng.chisquare(cfg.d, size=(M, 1)) / cfg.d)
+    Z = (rng.standard_normal((M, E)) * sigma[None, :] * s).astype(np.float32)
     for _ in range(iters):
         sel = np.argpartition(-(Z + b.astype(np.float32)), k - 1, axis=1)[:, :k]
-        load = np.bincount(sel.ravel(), minlength=E).astype(np.float64)
-        step = 0.5 * np.log(L / np.maximum(load, 0.5))
+        load = np.bincount(sel.ravel(), minlength=E) * (T / M)
+        q = np.clip(load / T, 1e-6, 1 - 1e-6)
+        zq = norm.isf(q)
+        hazard = norm.pdf(zq) / q
+        step = 0.7 * np.log(L / np.maximum(load, 0.25)) / np.maximum(hazard, 0.2)
         b[~capped] += step[~capped]
     out = b.astype(np.float32)
     _bias_cache[key] = out

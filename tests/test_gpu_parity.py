@@ -211,6 +211,8 @@ def test_prefill_config(torch):
 def test_skew_config(torch):
     cfg, idx_h, load = _full_size_check(torch, "skew", 8)
     L = syn.zipf_targets(cfg.T, cfg.E, cfg.k, cfg.zipf_alpha)
-    # the heaviest experts take (almost) every token, the tail is light
-    assert load[0] >= 0.95 * cfg.T and load[1] >= 0.95 * cfg.T
-    assert np.corrcoef(np.log(load + 1), np.log(L + 1))[0, 1] > 0.95
+    # the two heaviest experts take (almost) every token; popularity bands follow the Zipf targets
+    assert load[0] >= 0.99 * cfg.T and load[1] >= 0.99 * cfg.T
+    for a, b in [(0, 10), (10, 50), (50, 200), (200, cfg.E)]:
+        assert abs(load[a:b].sum() / L[a:b].sum() - 1) < 0.05, (a, b)
+    assert np.corrcoef(np.log(load + 1), np.log(L + 1))[0, 1] > 0.97
