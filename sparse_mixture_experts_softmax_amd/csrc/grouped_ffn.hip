@@ -24,15 +24,14 @@
 // Row tiles come from a device-built tile list (group, first row), so the host
 // launches an upper bound of tiles without knowing the routing; surplus
 // workgroups exit at once.
-#include <type_traits>
-
 #include "moe_internal.h"
+#include "stream_gemm.h"
 
 namespace moe {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+using stream::bf16x8_t;
+using stream::f32x16_t;
 
 struct Group {
   int64_t row0;  // first sorted slot of the group
@@ -306,73 +305,18 @@ ffn_mfma_kernel(MfmaArgs p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16 MFMA grouped GEMM, streaming variant for aligned shapes (K % 32 == 0, N % tile == 0).
+// bf16 MFMA grouped GEMM, streaming variant for aligned shapes (K % 32 == 0, N % tile == 0):
+// the shared DMA/LDS-transpose mainloop of stream_gemm.h on 128 x 256 tiles.
 //
-// Operands move HBM -> LDS with gfx950's direct global-to-LDS loads (16 bytes per lane;
-// lane l's bytes land at the instruction's LDS base + 16*l), so no registers hold tiles in
-// flight and three 24 KB stages are in flight per workgroup. Each lane picks its source
-// address so that the LDS tile comes out XOR-swizzled at 16-byte granularity:
-//   A tile [128 rows][32 K] (64 B per row): chunk c of row m sits at slot c ^ ((m >> 2) & 3);
-//   B tile [32 K][256 N] (512 B per row, N-contiguous as stored in HBM): 16-byte chunk c of
-//   row k sits at slot c ^ (2 * (k & 3)).
-// A fragments are ds_read_b128 of 8 consecutive K values. B fragments come straight from the
-// N-contiguous tile with ds_read_b64_tr_b16: within each 16-lane group, lane 4j+q points at
-// row kb+j, columns nb+4q..nb+4q+3, and lane i receives column nb+i at rows kb..kb+3; two such
-// reads give the 8 K values of one column that v_mfma_f32_32x32x16_bf16 takes per lane. Both
-// swizzles keep the 16 lanes of a B read and each 8 lanes of an A read on distinct banks.
+// Tiles are ordered expert-major -- (group, column tile, row tile) -- and the workgroup index
+// is remapped so that consecutive tiles run on the same XCD: an expert's row tiles share its
+// weight panels and its column tiles share its gathered rows through that XCD's L2.
 // ------------------------------------------------------------------------------------------
-namespace stream {
-
-constexpr int SBM = 128;
-constexpr int SBK = 32;
-constexpr int SBN = 256;                 // LDS tile columns (gate 128 + up 128, or 256 down)
-constexpr int A_BYTES = SBM * SBK * 2;    // 8 KB
-constexpr int B_BYTES = SBK * SBN * 2;    // 16 KB
-constexpr int STAGE = A_BYTES + B_BYTES;
-constexpr int A_DMA = A_BYTES / 1024 / 4;  // DMA instructions per wave per stage: 2
-constexpr int B_DMA = B_BYTES / 1024 / 4;  // 4
-constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
-
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-// The DMA, the wait on it and the workgroup barrier are written as asm statements with a
-// memory clobber. Through the builtins the compiler cannot tell which LDS stage a DMA writes
-// and drains every DMA in flight (vmcnt(0)) before each LDS read; here ordering comes only from
-// the explicit vmcnt waits below. The DMA has no destination register, so nothing the compiler
-// allocates is written behind its back.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void barrier_lds_only() { asm volatile("s_barrier" ::: "memory"); }
-
-// 16 bytes per lane from src to LDS byte address dst_base + 16 * lane (dst_base wave-uniform)
-__device__ __forceinline__ void dma16(const void* src, uint32_t dst_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst_base) : "memory", "m0");
-}
-
-__device__ __forceinline__ bf16x8_t read_a(const lds_char* st, int m, int c) {
-  const int off = m * 64 + ((c ^ ((m >> 2) & 3)) << 4);
-  return *(const __attribute__((address_space(3))) bf16x8_t*)(st + off);
-}
-
-__device__ __forceinline__ s16x4_t read_b_tr(const lds_char* st, int k, int n) {
-  const int off = A_BYTES + k * 512 + ((((n >> 3) ^ (2 * (k & 3)))) << 4) + ((n & 7) << 1);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(st + off));
-}
-
-}  // namespace stream
-
 template <bool GATED>
 __global__ void __launch_bounds__(256, 2)
 ffn_mfma_stream_kernel(MfmaArgs p) {
   using namespace stream;
-  __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
-  __shared__ __attribute__((aligned(1024))) char smem2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[3 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -380,12 +324,18 @@ ffn_mfma_stream_kernel(MfmaArgs p) {
   const int wm = wave >> 1;
   const int wn = wave & 1;
 
-  const int mt = blockIdx.x / p.n_ntiles;
-  const int nt = blockIdx.x % p.n_ntiles;
-  if (mt >= *p.tile_count) return;
-  const int g = p.tile_group[mt];
-  const int m0 = p.tile_m0[mt];
+  // logical tile -> (group, column tile, row tile)
+  const int L = xcd_remap(blockIdx.x, *p.tile_count * p.n_ntiles);
+  if (L < 0) return;
+  const int probe = L / p.n_ntiles;
+  const int g = p.tile_group[probe];
+  const int first = probe - p.tile_m0[probe] / SBM;  // the group's first row tile
   const Group G = group_info(g, p.offsets, p.T, p.k, p.E, p.I, p.Is);
+  const int cnt = (G.rows + SBM - 1) / SBM;
+  const int local = L - p.n_ntiles * first;
+  const int nt = local / cnt;
+  const int m0 = (local % cnt) * SBM;
+
   const int K = GATED ? p.d : G.n_inter;
   const int N = GATED ? G.n_inter : p.d;
   const int n0 = nt * (GATED ? kMfmaBN1 : kMfmaBN2);
@@ -400,115 +350,44 @@ ffn_mfma_stream_kernel(MfmaArgs p) {
     W0 = G.shared ? p.w0_s : p.w0 + (size_t)g * p.I * p.d;
   }
 
-  // ---- DMA source addresses (advanced by SBK columns / rows per stage)
-  const bf16_t* a_src[A_DMA];
+  // DMA sources: uniform bases per k-step, 32-bit per-lane byte offsets
+  const int64_t a_pitch = (GATED ? (int64_t)p.d : (int64_t)p.ldh) * 2;
+  uint32_t a_off[A_DMA];
 #pragma unroll
   for (int i = 0; i < A_DMA; ++i) {
-    const int m = (wave * A_DMA + i) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((m >> 2) & 3);
+    const int m = a_dma_row(wave, i, lane);
     const int r = (m0 + m < G.rows) ? m : 0;  // rows past the group re-read its first row
     int64_t src_row;
     if (GATED)
       src_row = G.shared ? (int64_t)(m0 + r) : (int64_t)p.sorted_token[G.row0 + m0 + r];
     else
       src_row = G.row0 + m0 + r;
-    a_src[i] = p.a_src + src_row * (GATED ? (int64_t)p.d : (int64_t)p.ldh) + c * 8;
+    a_off[i] = (uint32_t)(src_row * a_pitch) + a_dma_chunk_bytes(lane);
   }
-  const bf16_t* b_src[B_DMA];
-#pragma unroll
-  for (int i = 0; i < B_DMA; ++i) {
-    const int k = (wave * B_DMA + i) * 2 + (lane >> 5);
-    const int cn = (lane & 31) ^ (2 * (k & 3));
-    const bf16_t* base;
-    int col;
-    if (GATED) {
-      base = cn < 16 ? W0 : W1;
-      col = n0 + (cn & 15) * 8;
-    } else {
-      base = W0;
-      col = n0 + cn * 8;
-    }
-    b_src[i] = base + (int64_t)k * N + col;
-  }
-  const int64_t b_step = (int64_t)SBK * N;
+  const char* a_src = (const char*)p.a_src;
+  auto a_base = [=](int kt) { return a_src + kt * (SBK * 2); };
 
-  auto issue = [&](int kt, lds_char* st) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)st);
-#pragma unroll
-    for (int i = 0; i < A_DMA; ++i) dma16(a_src[i] + kt * SBK, base + (wave * A_DMA + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < B_DMA; ++i) dma16(b_src[i] + kt * b_step, base + A_BYTES + (wave * B_DMA + i) * 1024);
-  };
-
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int64_t b_pitch = (int64_t)N * 2;
+  const int half = b_dma_half(wave);
+  const char* b_mat;
+  if (GATED)
+    b_mat = (const char*)(half == 0 ? W0 : W1) + (int64_t)n0 * 2;
+  else
+    b_mat = (const char*)W0 + (int64_t)(n0 + 128 * half) * 2;
+  auto b_base = [=](int kt, int i) { return b_mat + (int64_t)(kt * SBK + b_dma_row0(wave, i)) * b_pitch; };
+  const uint32_t b_off = b_dma_lane_offset(lane, (uint32_t)b_pitch);
 
   int bcol[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) bcol[j] = GATED ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
-  // 32-row sub-tiles entirely past the group's rows are skipped
-  bool live[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) live[i] = m0 + wm * 64 + i * 32 < G.rows;
+  const int nlive = (m0 + wm * 64 < G.rows) + (m0 + wm * 64 + 32 < G.rows);
 
-  const int g16 = lane >> 4;   // 16-lane group
-  const int i16 = lane & 15;
-  // NI = number of live 32-row sub-tiles of this wave (1 or 2); branch once per stage
-  auto compute_n = [&](const lds_char* st, auto NI_c) {
-    constexpr int NI = decltype(NI_c)::value;
-#pragma unroll
-    for (int s = 0; s < SBK / 16; ++s) {
-      bf16x8_t a[NI], b[4];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) a[i] = read_a(st, wm * 64 + i * 32 + (lane & 31), 2 * s + (lane >> 5));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kb = 16 * s + 8 * (g16 >> 1) + (i16 >> 2);
-        const int n = bcol[j] + 16 * (g16 & 1) + 4 * (i16 & 3);
-        const s16x4_t lo = read_b_tr(st, kb, n);
-        const s16x4_t hi = read_b_tr(st, kb + 4, n);
-        b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  };
-  auto compute = [&](const lds_char* st) {
-    if (live[1]) compute_n(st, std::integral_constant<int, 2>());
-    else if (live[0]) compute_n(st, std::integral_constant<int, 1>());
-  };
+  f32x16_t acc[2][4];
+  zero(acc);
+  mainloop(K / SBK, nlive, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
 
-  lds_char* st0 = (lds_char*)smem0;
-  lds_char* st1 = (lds_char*)smem1;
-  lds_char* st2 = (lds_char*)smem2;
-  const int nk = K / SBK;
-  issue(0, st0);
-  if (nk > 1) issue(1, st1);
-  // step kt: stage kt is complete once at most one later stage's DMAs are outstanding. The
-  // barrier is a bare s_barrier: a __syncthreads() fence would drain every stage in flight.
-  // Each wave waits for its own DMAs first, so after the barrier stage kt is whole; and every
-  // wave has finished reading stage kt-1, which the DMAs issued next overwrite.
-  auto step = [&](int kt, lds_char* cur, lds_char* fill) {
-    if (kt + 1 < nk) wait_vmcnt<DMA_PER_STAGE>();
-    else wait_vmcnt<0>();
-    barrier_lds_only();
-    if (kt + 2 < nk) issue(kt + 2, fill);
-    compute(cur);
-  };
-  for (int kt = 0; kt < nk; kt += 3) {
-    step(kt, st0, st2);
-    if (kt + 1 < nk) step(kt + 1, st1, st0);
-    if (kt + 2 < nk) step(kt + 2, st2, st1);
-  }
-
-  // ---- epilogue (same accumulator layout as the generic kernel)
+  // epilogue: 32x32 accumulator -- lane holds column (lane & 31); register r holds row
+  // 8*(r/4) + 4*(lane/32) + (r%4)
   const int col_in = lane & 31;
   const int row_hi = (lane >> 5) * 4;
   if (GATED) {
@@ -683,7 +562,10 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
 
   if (dm.dtype == MOE_BF16) {
     // the streaming kernel needs whole tiles along N and whole 32-wide K steps
-    const bool stream_ok = dm.d % 256 == 0 && dm.I % 128 == 0 && dm.I_shared % 128 == 0;
+    // (and 32-bit byte offsets for the gathered rows of x and of H)
+    const bool stream_ok = dm.d % 256 == 0 && dm.I % 128 == 0 && dm.I_shared % 128 == 0 &&
+                           (uint64_t)dm.T * dm.d * 2 < (1ull << 32) &&
+                           (uint64_t)L.rows_total * L.ldh * 2 < (1ull << 32);
     MfmaArgs a;
     a.offsets = offsets;
     a.sorted_token = sorted_token;
