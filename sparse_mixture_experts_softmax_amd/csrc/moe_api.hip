@@ -82,16 +82,31 @@ Layout make_layout(const moe_dims& dm) {
   const int64_t T = dm.T;
   const int64_t Tk = T * dm.k;
   const size_t esz = dm.dtype == MOE_F32 ? 4 : 2;
-  // Router: split the hidden dimension when the (token x expert) tiles alone
-  // would leave most of the 256 CUs idle.
-  const int64_t base_tiles = ((T + kRouterTileT - 1) / kRouterTileT) * ((dm.E + kRouterTileE - 1) / kRouterTileE);
-  int64_t splits = base_tiles > 0 ? (512 + base_tiles - 1) / base_tiles : 1;
-  const int64_t max_splits = dm.d / 256 > 0 ? dm.d / 256 : 1;
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
-  int64_t kchunk = (dm.d + splits - 1) / splits;
-  kchunk = (kchunk + kRouterKStep - 1) / kRouterKStep * kRouterKStep;
-  splits = (dm.d + kchunk - 1) / kchunk;
+  // Router. bf16 x with enough tokens: MFMA on 128 x 256 tiles over K' = 3d (W_r split into
+  // three bf16 parts). Otherwise fp32 vector ALUs on 64 x 64 tiles. Either way the K dimension
+  // is split when the (token x expert) tiles alone would leave most of the 256 CUs idle.
+  L.router_mfma = dm.dtype == MOE_BF16 && T >= 256 && dm.E % 256 == 0 && dm.d % 32 == 0 &&
+                  (uint64_t)T * dm.d * 2 < (1ull << 32);
+  int64_t splits, kchunk;
+  if (L.router_mfma) {
+    const int64_t base_tiles = ((T + 127) / 128) * (dm.E / 256);
+    const int64_t ksteps = 3 * (int64_t)dm.d / 32;
+    splits = (256 + base_tiles - 1) / base_tiles;
+    if (splits > 8) splits = 8;
+    if (splits > ksteps / 8) splits = ksteps / 8 > 0 ? ksteps / 8 : 1;
+    if (splits < 1) splits = 1;
+    kchunk = (ksteps + splits - 1) / splits;
+    splits = (ksteps + kchunk - 1) / kchunk;
+  } else {
+    const int64_t base_tiles = ((T + kRouterTileT - 1) / kRouterTileT) * ((dm.E + kRouterTileE - 1) / kRouterTileE);
+    splits = base_tiles > 0 ? (512 + base_tiles - 1) / base_tiles : 1;
+    const int64_t max_splits = dm.d / 256 > 0 ? dm.d / 256 : 1;
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    kchunk = (dm.d + splits - 1) / splits;
+    kchunk = (kchunk + kRouterKStep - 1) / kRouterKStep * kRouterKStep;
+    splits = (dm.d + kchunk - 1) / kchunk;
+  }
   L.router_splits = (int)splits;
   L.router_kchunk = (int)kchunk;
   L.nchunks = (T + kPermuteChunk - 1) / kPermuteChunk;
@@ -106,6 +121,7 @@ Layout make_layout(const moe_dims& dm) {
     off = align_up(off + bytes, 256);
     return at;
   };
+  L.router_planes = take(L.router_mfma ? (size_t)3 * dm.d * dm.E * 2 : 0);
   L.logits = take((size_t)splits * T * dm.E * 4);
   L.topk_idx = take((size_t)Tk * 4);
   L.topk_w = take((size_t)Tk * 4);

@@ -48,13 +48,14 @@ constexpr int kF32BN = 64;             // fp32 grouped GEMM tile columns
 // workspace layout: a pure function of the dims
 // ------------------------------------------------------------------------------------------
 struct Layout {
-  int router_splits;    // K splits of the router logits GEMM
-  int router_kchunk;    // hidden rows per split
+  int router_mfma;      // 1: bf16 x with the 3-way bf16 split of W_r on MFMA; 0: fp32 vector ALUs
+  int router_splits;    // K splits of the router logits GEMM (partial sums summed by top-k)
+  int router_kchunk;    // vector path: hidden rows per split; MFMA path: 32-wide K steps per split
   int64_t nchunks;      // permute chunks
   int64_t max_tiles;    // upper bound on grouped-GEMM row tiles (any BM >= 64)
   int ldh;              // row stride of H = max(I, I_shared)
   int64_t rows_total;   // T*k + (I_shared ? T : 0)
-  size_t logits, topk_idx, topk_w, topk_gap, chunk_counts, offsets, sorted_token, slot_of;
+  size_t router_planes, logits, topk_idx, topk_w, topk_gap, chunk_counts, offsets, sorted_token, slot_of;
   size_t tile_group, tile_m0, tile_count, H, Y;
   size_t total;
 };

@@ -7,21 +7,115 @@
 // probabilities), ties go to the lower expert index, and the kept
 // probabilities are optionally renormalised to sum to one.
 //
-// Two kernels:
-//   router_logits: fp32 GEMM  part[s][t][e] = sum_{i in split s} x[t,i] W_r[i,e]
-//                  64x64 (token x expert) tiles, 4x4 outputs per thread, LDS-staged,
-//                  split over the hidden dimension when there are too few tiles to
-//                  fill the chip (decode-sized batches);
-//   router_topk:   one 64-lane wavefront per token: sums the splits (+ bias) in a
-//                  fixed order, then k (+1 for the gap) rounds of a wave-wide
-//                  argmax built from cross-lane shuffles, then the softmax
-//                  normaliser as a wave-wide sum.
+// Logits, two ways (both fp32-accurate, both optionally split over K with the
+// partial sums added by the top-k kernel in a fixed order):
+//   router_mfma:   bf16 x and enough tokens. W_r (fp32) is split into three
+//                  bf16 parts hi + mid + lo = W_r exactly (each part is the
+//                  round-to-nearest bf16 of the remainder; 24 significand bits
+//                  fit in three 8-bit ones), stacked along K, so
+//                  x W_r = x hi + x mid + x lo with every product exact in fp32;
+//                  the streaming bf16 MFMA mainloop runs over K' = 3d.
+//   router_logits: fp32 GEMM on the vector ALUs, 64x64 (token x expert) tiles,
+//                  4x4 outputs per thread, LDS-staged.
+// router_topk: one 64-lane wavefront per token: sums the splits (+ bias) in a
+// fixed order, then k (+1 for the gap) rounds of a wave-wide argmax built from
+// cross-lane shuffles, then the softmax normaliser as a wave-wide sum.
 #include <math.h>
 
 #include "moe_internal.h"
+#include "stream_gemm.h"
 
 namespace moe {
 namespace {
+
+// W_r [d, E] fp32 -> three bf16 planes [3][d][E]: hi = bf16(w), mid = bf16(w - hi),
+// lo = bf16(w - hi - mid); both differences are exact in fp32 and lo is exact in bf16.
+__global__ void __launch_bounds__(256)
+router_split_kernel(const float* __restrict__ w, bf16_t* __restrict__ planes, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;  // n = d * E is a multiple of 4 (d % 8 == 0)
+  const float x[4] = {w[i], w[i + 1], w[i + 2], w[i + 3]};  // w_router is only 4-byte aligned
+  uint32_t p0[2], p1[2], p2[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    bf16_t a[2], b[2], c[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float wv = x[2 * h + j];
+      a[j] = f32_to_bf16(wv);
+      const float r1 = wv - bf16_to_f32(a[j]);
+      b[j] = f32_to_bf16(r1);
+      const float r2 = r1 - bf16_to_f32(b[j]);
+      c[j] = f32_to_bf16(r2);
+    }
+    p0[h] = (uint32_t)a[0] | ((uint32_t)a[1] << 16);
+    p1[h] = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
+    p2[h] = (uint32_t)c[0] | ((uint32_t)c[1] << 16);
+  }
+  *(uint2*)(planes + i) = make_uint2(p0[0], p0[1]);
+  *(uint2*)(planes + n + i) = make_uint2(p1[0], p1[1]);
+  *(uint2*)(planes + 2 * n + i) = make_uint2(p2[0], p2[1]);
+}
+
+// Logits on MFMA: 128 tokens x 256 experts per workgroup, K' = 3d split into `splits` chunks of
+// `ksteps` 32-wide steps. grid = splits * token tiles * expert tiles.
+__global__ void __launch_bounds__(256, 2)
+router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ planes, float* __restrict__ part,
+                   int64_t T, int d, int E, int ksteps) {
+  using namespace stream;
+  __shared__ __attribute__((aligned(1024))) char smem[3 * STAGE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int n_et = E / 256;
+  const int n_mt = (int)((T + 127) / 128);
+  const int et = blockIdx.x % n_et;
+  const int mt = (blockIdx.x / n_et) % n_mt;
+  const int split = blockIdx.x / (n_et * n_mt);
+  const int64_t t0 = (int64_t)mt * 128;
+  const int e0 = et * 256;
+  const int dk = d / 32;  // K steps per plane
+  const int kt0 = split * ksteps;
+  const int nk = min(ksteps, 3 * dk - kt0);
+
+  uint32_t a_off[A_DMA];
+#pragma unroll
+  for (int i = 0; i < A_DMA; ++i) {
+    const int64_t row = min(t0 + a_dma_row(wave, i, lane), T - 1);
+    a_off[i] = (uint32_t)(row * d * 2) + a_dma_chunk_bytes(lane);
+  }
+  const char* xb = (const char*)x;
+  auto a_base = [=](int kt) { return xb + ((kt0 + kt) % dk) * (SBK * 2); };
+  const char* pb = (const char*)planes + (int64_t)(e0 + 128 * b_dma_half(wave)) * 2;
+  const int64_t pitch = (int64_t)E * 2;
+  auto b_base = [=](int kt, int i) { return pb + ((int64_t)(kt0 + kt) * SBK + b_dma_row0(wave, i)) * pitch; };
+  const uint32_t b_off = b_dma_lane_offset(lane, (uint32_t)pitch);
+  int bcol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bcol[j] = wn * 128 + j * 32;
+  const int nlive = (t0 + wm * 64 < T) + (t0 + wm * 64 + 32 < T);
+
+  f32x16_t acc[2][4];
+  zero(acc);
+  mainloop(nk, nlive, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+
+  float* out = part + (int64_t)split * T * E;
+  const int col_in = lane & 31;
+  const int row_hi = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + wn * 128 + j * 32 + col_in;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t t = t0 + wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+        if (t < T) out[t * E + e] = acc[i][j][r];
+      }
+    }
+}
 
 template <typename XT>
 __device__ __forceinline__ void load_x4(const XT* p, float* v);
@@ -135,8 +229,16 @@ router_topk_kernel(const float* __restrict__ part, int splits, const float* __re
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     if (e < E) {
+      // partial sums added in split order; loads issued 8 at a time
       float s = 0.f;
-      for (int sp = 0; sp < splits; ++sp) s += part[((int64_t)sp * T + t) * E + e];
+      for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+        float q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = sp0 + u < splits ? part[((int64_t)(sp0 + u) * T + t) * E + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (sp0 + u < splits) s += q[u];
+      }
       if (bias) s += bias[e];
       v[j] = s;
     } else {
@@ -229,6 +331,18 @@ hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, con
                          const float* bias, int32_t* topk_idx, float* topk_w, float* topk_gap, char* ws,
                          hipStream_t s) {
   float* part = (float*)(ws + L.logits);
+  if (L.router_mfma) {
+    bf16_t* planes = (bf16_t*)(ws + L.router_planes);
+    const int64_t n = (int64_t)dm.d * dm.E;
+    hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, w_router, planes,
+                       n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t tiles = ((dm.T + 127) / 128) * (dm.E / 256);
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((unsigned)(tiles * L.router_splits)), dim3(256), 0, s,
+                       (const bf16_t*)x, planes, part, dm.T, dm.d, dm.E, L.router_kchunk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
   const dim3 grid((unsigned)((dm.E + kRouterTileE - 1) / kRouterTileE),
                   (unsigned)((dm.T + kRouterTileT - 1) / kRouterTileT), (unsigned)L.router_splits);
   if (dm.dtype == MOE_F32)
@@ -239,6 +353,7 @@ hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, con
                        dm.d, dm.E, L.router_kchunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  }
   const int nj = (dm.E + 63) / 64;
   const int sp = L.router_splits;
   if (nj <= 1) return launch_topk<1>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, s);

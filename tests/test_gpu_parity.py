@@ -75,6 +75,8 @@ SMALL_CASES = [
     ("skewed_small", 512, 128, 64, 8, 64, 64, syn.BF16, 1, 1.2),
     ("E65_k16", 200, 64, 65, 16, 24, 8, syn.F32, 1, 0.0),
     ("wide_E", 96, 64, 1024, 16, 16, 16, syn.BF16, 1, 0.0),
+    ("router_mfma", 300, 256, 256, 8, 128, 128, syn.BF16, 1, 0.0),
+    ("router_mfma_E512", 520, 512, 512, 10, 128, 0, syn.BF16, 0, 0.0),
 ]
 
 
