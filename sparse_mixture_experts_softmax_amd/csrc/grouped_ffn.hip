@@ -312,11 +312,12 @@ ffn_mfma_kernel(MfmaArgs p) {
 // is remapped so that consecutive tiles run on the same XCD: an expert's row tiles share its
 // weight panels and its column tiles share its gathered rows through that XCD's L2.
 // ------------------------------------------------------------------------------------------
-template <bool GATED>
-__global__ void __launch_bounds__(256, 2)
+template <bool GATED, int MT>
+__global__ void __launch_bounds__(256, MT == 1 ? 2 : 1)
 ffn_mfma_stream_kernel(MfmaArgs p) {
   using namespace stream;
-  __shared__ __attribute__((aligned(1024))) char smem[3 * STAGE];
+  constexpr int BMW = MT * SBM;  // rows per workgroup
+  __shared__ __attribute__((aligned(1024))) char smem[3 * stage_bytes<MT>()];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -329,12 +330,12 @@ ffn_mfma_stream_kernel(MfmaArgs p) {
   if (L < 0) return;
   const int probe = L / p.n_ntiles;
   const int g = p.tile_group[probe];
-  const int first = probe - p.tile_m0[probe] / SBM;  // the group's first row tile
+  const int first = probe - p.tile_m0[probe] / BMW;  // the group's first row tile
   const Group G = group_info(g, p.offsets, p.T, p.k, p.E, p.I, p.Is);
-  const int cnt = (G.rows + SBM - 1) / SBM;
+  const int cnt = (G.rows + BMW - 1) / BMW;
   const int local = L - p.n_ntiles * first;
   const int nt = local / cnt;
-  const int m0 = (local % cnt) * SBM;
+  const int m0 = (local % cnt) * BMW;
 
   const int K = GATED ? p.d : G.n_inter;
   const int N = GATED ? G.n_inter : p.d;
@@ -352,19 +353,21 @@ ffn_mfma_stream_kernel(MfmaArgs p) {
 
   // DMA sources: uniform bases per k-step, 32-bit per-lane byte offsets
   const int64_t a_pitch = (GATED ? (int64_t)p.d : (int64_t)p.ldh) * 2;
-  uint32_t a_off[A_DMA];
+  uint32_t a_off[MT][A_DMA];
 #pragma unroll
-  for (int i = 0; i < A_DMA; ++i) {
-    const int m = a_dma_row(wave, i, lane);
-    const int r = (m0 + m < G.rows) ? m : 0;  // rows past the group re-read its first row
-    int64_t src_row;
-    if (GATED)
-      src_row = G.shared ? (int64_t)(m0 + r) : (int64_t)p.sorted_token[G.row0 + m0 + r];
-    else
-      src_row = G.row0 + m0 + r;
-    a_off[i] = (uint32_t)(src_row * a_pitch) + a_dma_chunk_bytes(lane);
-  }
-  const char* a_src = (const char*)p.a_src;
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+      const int m = t * SBM + a_dma_row(wave, i, lane);
+      const int r = (m0 + m < G.rows) ? m : 0;  // rows past the group re-read its first row
+      int64_t src_row;
+      if (GATED)
+        src_row = G.shared ? (int64_t)(m0 + r) : (int64_t)p.sorted_token[G.row0 + m0 + r];
+      else
+        src_row = G.row0 + m0 + r;
+      a_off[t][i] = (uint32_t)(src_row * a_pitch) + a_dma_chunk_bytes(lane);
+    }
+  const char* a_src = uniform_ptr((const char*)p.a_src);
   auto a_base = [=](int kt) { return a_src + kt * (SBK * 2); };
 
   const int64_t b_pitch = (int64_t)N * 2;
@@ -374,49 +377,62 @@ ffn_mfma_stream_kernel(MfmaArgs p) {
     b_mat = (const char*)(half == 0 ? W0 : W1) + (int64_t)n0 * 2;
   else
     b_mat = (const char*)W0 + (int64_t)(n0 + 128 * half) * 2;
-  auto b_base = [=](int kt, int i) { return b_mat + (int64_t)(kt * SBK + b_dma_row0(wave, i)) * b_pitch; };
+  const char* b0 = uniform_ptr(b_mat + (int64_t)b_dma_row0(wave, 0) * b_pitch);
+  const int64_t b_kstep = (int64_t)SBK * b_pitch;
+  // the wave's four B instructions load consecutive 4-row blocks
+  auto b_base = [=](int kt, int i) { return b0 + kt * b_kstep + i * 4 * b_pitch; };
   const uint32_t b_off = b_dma_lane_offset(lane, (uint32_t)b_pitch);
 
   int bcol[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) bcol[j] = GATED ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
-  const int nlive = (m0 + wm * 64 < G.rows) + (m0 + wm * 64 + 32 < G.rows);
+  int ml, nl;
+  live_tiles<MT>(G.rows - m0, wm, ml, nl);
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[MT][2][4];
   zero(acc);
-  mainloop(K / SBK, nlive, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+  mainloop<MT>(K / SBK, ml, nl, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
 
   // epilogue: 32x32 accumulator -- lane holds column (lane & 31); register r holds row
   // 8*(r/4) + 4*(lane/32) + (r%4)
   const int col_in = lane & 31;
   const int row_hi = (lane >> 5) * 4;
-  if (GATED) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int t = 0; t < MT; ++t) {
+    if (GATED) {
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int col = n0 + wn * 64 + jj * 32 + col_in;
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
-          if (m0 + row < G.rows)
-            p.out[(G.row0 + m0 + row) * (int64_t)p.ldh + col] =
-                f32_to_bf16(silu_f32(acc[i][jj][r]) * acc[i][jj + 2][r]);
+        for (int jj = 0; jj < 2; ++jj) {
+          const int col = n0 + wn * 64 + jj * 32 + col_in;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = t * SBM + wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+            if (m0 + row < G.rows)
+              p.out[(G.row0 + m0 + row) * (int64_t)p.ldh + col] =
+                  f32_to_bf16(silu_f32(acc[t][i][jj][r]) * acc[t][i][jj + 2][r]);
+          }
         }
-      }
-  } else {
+    } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 128 + j * 32 + col_in;
+        for (int j = 0; j < 4; ++j) {
+          const int col = n0 + wn * 128 + j * 32 + col_in;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
-          if (m0 + row < G.rows) p.out[(G.row0 + m0 + row) * (int64_t)p.d + col] = f32_to_bf16(acc[i][j][r]);
+          for (int r = 0; r < 16; ++r) {
+            const int row = t * SBM + wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+            if (m0 + row < G.rows) p.out[(G.row0 + m0 + row) * (int64_t)p.d + col] = f32_to_bf16(acc[t][i][j][r]);
+          }
         }
-      }
+    }
   }
+}
+
+template <bool GATED>
+void launch_stream(int mt, unsigned grid, hipStream_t s, const MfmaArgs& a) {
+  (void)mt;
+  hipLaunchKernelGGL((ffn_mfma_stream_kernel<GATED, 1>), dim3(grid), dim3(256), 0, s, a);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -550,7 +566,15 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
   int32_t* tm = (int32_t*)(ws + L.tile_m0);
   int32_t* tc = (int32_t*)(ws + L.tile_count);
   const int has_shared = dm.I_shared > 0 ? 1 : 0;
-  const int bm = dm.dtype == MOE_F32 ? kF32BM : kMfmaBM;
+  // the streaming kernel needs whole tiles along N and whole 32-wide K steps
+  // (and 32-bit byte offsets for the gathered rows of x and of H)
+  const bool stream_ok = dm.dtype == MOE_BF16 && dm.d % 256 == 0 && dm.I % 128 == 0 && dm.I_shared % 128 == 0 &&
+                         (uint64_t)dm.T * dm.d * 2 < (1ull << 32) &&
+                         (uint64_t)L.rows_total * L.ldh * 2 < (1ull << 32);
+  // one 128-row tile per streaming workgroup: two such workgroups share a CU, and that
+  // occupancy hides more latency than the weight reuse of taller tiles saves
+  const int mt = 1;
+  const int bm = dm.dtype == MOE_F32 ? kF32BM : kMfmaBM * mt;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, dm.T, dm.E, has_shared, bm, tg, tm, tc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -561,11 +585,6 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
   char* H = ws + L.H;
 
   if (dm.dtype == MOE_BF16) {
-    // the streaming kernel needs whole tiles along N and whole 32-wide K steps
-    // (and 32-bit byte offsets for the gathered rows of x and of H)
-    const bool stream_ok = dm.d % 256 == 0 && dm.I % 128 == 0 && dm.I_shared % 128 == 0 &&
-                           (uint64_t)dm.T * dm.d * 2 < (1ull << 32) &&
-                           (uint64_t)L.rows_total * L.ldh * 2 < (1ull << 32);
     MfmaArgs a;
     a.offsets = offsets;
     a.sorted_token = sorted_token;
@@ -589,7 +608,7 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.n_ntiles = (nmax + kMfmaBN1 - 1) / kMfmaBN1;
     if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
     if (stream_ok)
-      hipLaunchKernelGGL(ffn_mfma_stream_kernel<true>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
+      launch_stream<true>(mt, (unsigned)(max_mt * a.n_ntiles), s, a);
     else
       hipLaunchKernelGGL(ffn_mfma_kernel<true>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -604,7 +623,7 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.n_ntiles = (dm.d + kMfmaBN2 - 1) / kMfmaBN2;
     if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
     if (stream_ok)
-      hipLaunchKernelGGL(ffn_mfma_stream_kernel<false>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
+      launch_stream<false>(mt, (unsigned)(max_mt * a.n_ntiles), s, a);
     else
       hipLaunchKernelGGL(ffn_mfma_kernel<false>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -1,26 +1,29 @@
 // Streaming bf16 MFMA tile mainloop for gfx950, shared by the grouped expert GEMMs and the
 // router GEMM.
 //
-// One 256-thread workgroup (4 wavefronts in 2x2) accumulates a 128 x 256 fp32 tile
-// acc += A[128 x K] * B[K x 256] with v_mfma_f32_32x32x16_bf16 (each wavefront 64 x 128).
+// One 256-thread workgroup (4 wavefronts in 2x2) accumulates an (MT*128) x 256 fp32 tile
+// acc += A[MT*128 x K] * B[K x 256] with v_mfma_f32_32x32x16_bf16: MT (1..3) row tiles of 128 share
+// every B tile, so a weight panel is streamed from HBM once for up to MT*128 rows. Each wavefront
+// owns 64 rows of every row tile and 128 columns.
 //
 // Operands move HBM -> LDS with gfx950's direct global-to-LDS loads (16 bytes per lane; lane
 // l's bytes land at the instruction's LDS base + 16*l), so no registers hold tiles in flight and
 // three 24 KB stages are in flight per workgroup. Each DMA instruction takes a wave-uniform
 // 64-bit base (SGPRs) plus a 32-bit per-lane byte offset, and each lane picks its offset so
 // that the LDS tile comes out XOR-swizzled at 16-byte granularity:
-//   A tile [128 rows][32 K], 64 B per row: chunk c of row m sits at slot c ^ ((m >> 2) & 3).
-//     A instruction q (0..7, wave w issues q = 2w, 2w+1) loads rows 16q .. 16q+15:
+//   A tiles [128 rows][32 K], 64 B per row: chunk c of row m sits at slot c ^ ((m >> 2) & 3).
+//     Per row tile, A instruction q (0..7, wave w issues q = 2w, 2w+1) loads rows 16q .. 16q+15:
 //     lane l takes row 16q + l/4, chunk (l & 3) ^ ((l >> 4) & 3).
 //   B tile: two halves [32 K][128 N] (N-contiguous as stored in HBM), 256 B per row: chunk c
-//     of row k sits at slot c ^ (2 * (k & 3)). B instruction q (0..15, wave w issues 4w..4w+3)
+//     of row k sits at slot c ^ (4 * (k & 3)). B instruction q (0..15, wave w issues 4w..4w+3)
 //     loads half q/8, rows 4*(q%8) .. +3: lane l takes row 4*(q%8) + l/16, chunk
-//     (l & 15) ^ (2 * ((l >> 4) & 3)) -- the same per-lane offset for every B instruction.
+//     (l & 15) ^ (4 * ((l >> 4) & 3)) -- the same per-lane offset for every B instruction.
 // A fragments are ds_read_b128 of 8 consecutive K values. B fragments come straight from the
 // N-contiguous tile with ds_read_b64_tr_b16: within each 16-lane group, lane 4j+q points at row
 // kb+j, columns nb+4q..nb+4q+3, and lane i receives column nb+i at rows kb..kb+3; two such reads
-// give the 8 K values of one column that the MFMA takes per lane. Both swizzles keep the 16
-// lanes of a B read and each 8 lanes of an A read on distinct banks.
+// give the 8 K values of one column that the MFMA takes per lane. The swizzles keep each 32 lanes
+// of a B read (4 rows x 4 chunks, 8 bytes per lane) and each 16 lanes of an A read (16 rows,
+// 16 bytes per lane) on distinct banks of the 64 x 4-byte LDS banks.
 #pragma once
 
 #include <type_traits>
@@ -40,7 +43,10 @@ constexpr int SBK = 32;
 constexpr int SBN = 256;
 constexpr int A_BYTES = SBM * SBK * 2;       // 8 KB
 constexpr int B_BYTES = SBK * SBN * 2;       // 16 KB
-constexpr int STAGE = A_BYTES + B_BYTES;     // 24 KB
+constexpr int STAGE = A_BYTES + B_BYTES;     // 24 KB for one row tile
+// stage bytes with MT row tiles: [A tile 0] .. [A tile MT-1] [B half 0] [B half 1]
+template <int MT>
+constexpr int stage_bytes() { return MT * A_BYTES + B_BYTES; }
 constexpr int A_DMA = A_BYTES / 1024 / 4;    // DMA instructions per wave per stage: 2
 constexpr int B_DMA = B_BYTES / 1024 / 4;    // 4
 constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
@@ -56,7 +62,7 @@ __device__ __forceinline__ int a_dma_chunk_bytes(int lane) { return ((lane & 3) 
 __device__ __forceinline__ int b_dma_half(int wave) { return wave >> 1; }
 __device__ __forceinline__ int b_dma_row0(int wave, int i) { return 4 * ((wave * B_DMA + i) & 7); }
 __device__ __forceinline__ uint32_t b_dma_lane_offset(int lane, uint32_t pitch) {
-  return (uint32_t)(lane >> 4) * pitch + ((((lane & 15) ^ (2 * ((lane >> 4) & 3)))) << 4);
+  return (uint32_t)(lane >> 4) * pitch + ((((lane & 15) ^ (4 * ((lane >> 4) & 3)))) << 4);
 }
 
 // The DMA, the wait on it and the workgroup barrier are asm statements with a memory clobber.
@@ -91,24 +97,37 @@ __device__ __forceinline__ bf16x8_t read_a(const lds_char* st, int m, int c) {
   return *(const __attribute__((address_space(3))) bf16x8_t*)(st + off);
 }
 
-// n is the tile column 0..255 (half n / 128)
-__device__ __forceinline__ s16x4_t read_b_tr(const lds_char* st, int k, int n) {
+// sb: start of the B region of a stage; n is the tile column 0..255 (half n / 128)
+__device__ __forceinline__ s16x4_t read_b_tr(const lds_char* sb, int k, int n) {
   const int h = n >> 7, c = n & 127;
-  const int off = A_BYTES + h * HALF_BYTES + k * 256 + (((c >> 3) ^ (2 * (k & 3))) << 4) + ((c & 7) << 1);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(st + off));
+  const int off = h * HALF_BYTES + k * 256 + (((c >> 3) ^ (4 * (k & 3))) << 4) + ((c & 7) << 1);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(sb + off));
 }
 
-// acc[i][j] += A * B over nk K-steps of 32, for a wave with NI (1 or 2) live 32-row sub-tiles.
-//   lds: the workgroup's 3 * STAGE bytes of LDS;
-//   a_base(kt): uniform base of the A rows at k-step kt; a_off[i]: this lane's byte offset for
-//     its i-th A instruction (row offset + swizzled chunk);
+// acc[t][i][j] += A * B over nk K-steps of 32.
+//   MT: row tiles held in each stage; ML (1..MT): row tiles of this workgroup holding any valid row
+//     (only those are loaded); NL: 32-row sub-tiles of this wave holding any valid row, counted in
+//     the order (tile 0: sub 0, sub 1), (tile 1: ...), ... (only those are multiplied);
+//   lds: the workgroup's 3 * stage_bytes<MT>() bytes of LDS;
+//   a_base(kt): uniform base of the A rows at k-step kt; a_off[t][i]: this lane's byte offset for
+//     its i-th A instruction of row tile t (row offset + swizzled chunk);
 //   b_base(kt, i): uniform base of this wave's i-th B instruction at k-step kt (its half, its
 //     first row); b_off: this lane's byte offset, common to all B instructions;
 //   bcol[j]: tile column of the wave's j-th 32-wide B sub-tile.
-template <int NI, class ABase, class BBase>
-__device__ __forceinline__ void mainloop_n(int nk, lds_char* lds, ABase a_base, const uint32_t (&a_off)[A_DMA],
+//
+// Schedule. Three stages hold k-steps kt, kt+1, kt+2. Fragments (the A and B operands of one
+// 16-wide K sub-step) are read from LDS one sub-step ahead of the MFMAs that use them. After the
+// MFMAs of a stage's last sub-step are issued, the wave waits for its own DMAs of the next stage
+// and meets the others at the barrier while those MFMAs run; past the barrier every wave has
+// finished reading stage kt, so the DMAs for k-step kt+3 go into it, and the first fragments of
+// stage kt+1 are read.
+template <int MT, int ML, int NL, class ABase, class BBase>
+__device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base, const uint32_t (&a_off)[MT][A_DMA],
                                            BBase b_base, uint32_t b_off, const int (&bcol)[4],
-                                           f32x16_t (&acc)[2][4]) {
+                                           f32x16_t (&acc)[MT][2][4]) {
+  constexpr int STG = stage_bytes<MT>();
+  constexpr int DMA = ML * A_DMA + B_DMA;  // DMA instructions per wave per stage
+  constexpr int NA = NL > 0 ? NL : 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1;
@@ -117,72 +136,120 @@ __device__ __forceinline__ void mainloop_n(int nk, lds_char* lds, ABase a_base, 
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
 
   auto issue = [&](int kt, int stage) {
-    const uint32_t dst = lds_base + stage * STAGE;
-    const char* ab = uniform_ptr(a_base(kt));
+    const uint32_t dst = lds_base + stage * STG;
+    const char* ab = a_base(kt);
 #pragma unroll
-    for (int i = 0; i < A_DMA; ++i) dma16(ab, a_off[i], dst + (wave * A_DMA + i) * 1024);
+    for (int t = 0; t < ML; ++t)
 #pragma unroll
-    for (int i = 0; i < B_DMA; ++i)
-      dma16(uniform_ptr(b_base(kt, i)), b_off, dst + A_BYTES + (wave * B_DMA + i) * 1024);
+      for (int i = 0; i < A_DMA; ++i) dma16(ab, a_off[t][i], dst + t * A_BYTES + (wave * A_DMA + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) dma16(b_base(kt, i), b_off, dst + MT * A_BYTES + (wave * B_DMA + i) * 1024);
   };
-
-  auto compute = [&](const lds_char* st) {
-    if constexpr (NI > 0) {
+  // fragments of sub-step s (0 or 1) of the stage at st
+  auto read = [&](const lds_char* st, int s, bf16x8_t (&a)[NA], bf16x8_t (&b)[4]) {
+    if constexpr (NL > 0) {
 #pragma unroll
-    for (int s = 0; s < SBK / 16; ++s) {
-      bf16x8_t a[NI], b[4];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) a[i] = read_a(st, wm * 64 + i * 32 + (lane & 31), 2 * s + (lane >> 5));
+      for (int u = 0; u < NL; ++u)
+        a[u] = read_a(st + (u >> 1) * A_BYTES, wm * 64 + (u & 1) * 32 + (lane & 31), 2 * s + (lane >> 5));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kb = 16 * s + 8 * (g16 >> 1) + (i16 >> 2);
         const int n = bcol[j] + 16 * (g16 & 1) + 4 * (i16 & 3);
-        const s16x4_t lo = read_b_tr(st, kb, n);
-        const s16x4_t hi = read_b_tr(st, kb + 4, n);
+        const s16x4_t lo = read_b_tr(st + MT * A_BYTES, kb, n);
+        const s16x4_t hi = read_b_tr(st + MT * A_BYTES, kb + 4, n);
         b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+  };
+  auto mma = [&](const bf16x8_t (&a)[NA], const bf16x8_t (&b)[4]) {
+    if constexpr (NL > 0) {
+#pragma unroll
+      for (int u = 0; u < NL; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[u >> 1][u & 1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[j], acc[u >> 1][u & 1][j], 0, 0, 0);
     }
   };
 
+  // prologue: three stages in flight, stage 0 complete
   issue(0, 0);
   if (nk > 1) issue(1, 1);
-  // k-step kt: stage kt is complete once at most one later stage's DMAs are outstanding. Each
-  // wave waits for its own DMAs, then the bare barrier makes stage kt whole for everyone; it
-  // also guarantees every wave finished reading stage kt-1, which the next DMAs overwrite.
+  if (nk > 2) issue(2, 2);
+  if (nk > 2) wait_vmcnt<2 * DMA>();
+  else if (nk > 1) wait_vmcnt<DMA>();
+  else wait_vmcnt<0>();
+  barrier_lds_only();
+
+  bf16x8_t a0[NA], b0[4], a1[NA], b1[4];
+  read(lds, 0, a0, b0);
   int stage = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) wait_vmcnt<DMA_PER_STAGE>();
-    else wait_vmcnt<0>();
-    barrier_lds_only();
-    if (kt + 2 < nk) issue(kt + 2, stage == 0 ? 2 : stage - 1);
-    compute(lds + stage * STAGE);
-    stage = stage == 2 ? 0 : stage + 1;
+    const lds_char* cur = lds + stage * STG;
+    const int next = stage == 2 ? 0 : stage + 1;
+    read(cur, 1, a1, b1);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      // stage kt+1 complete once at most the DMAs of k-step kt+2 are outstanding
+      if (kt + 2 < nk) wait_vmcnt<DMA>();
+      else wait_vmcnt<0>();
+      barrier_lds_only();
+      if (kt + 3 < nk) issue(kt + 3, stage);
+      read(lds + next * STG, 0, a0, b0);
+    }
+    stage = next;
   }
 }
 
-// Dispatch on the wave's live 32-row sub-tiles (0, 1 or 2) outside the K loop.
-template <class ABase, class BBase>
-__device__ __forceinline__ void mainloop(int nk, int nlive, lds_char* lds, ABase a_base,
-                                         const uint32_t (&a_off)[A_DMA], BBase b_base, uint32_t b_off,
-                                         const int (&bcol)[4], f32x16_t (&acc)[2][4]) {
-  // every wave must take part in the barriers even when it has no live rows
-  if (nlive >= 2) mainloop_n<2>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
-  else if (nlive == 1) mainloop_n<1>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
-  else mainloop_n<0>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+// Dispatch on the live row tiles (ml) and this wave's live sub-tiles (nl) outside the K loop.
+// nl is one of 2ml-2, 2ml-1, 2ml: only the last row tile can be partial.
+template <int MT, int ML, class ABase, class BBase>
+__device__ __forceinline__ void mainloop_ml(int nk, int nl, lds_char* lds, ABase a_base,
+                                            const uint32_t (&a_off)[MT][A_DMA], BBase b_base, uint32_t b_off,
+                                            const int (&bcol)[4], f32x16_t (&acc)[MT][2][4]) {
+  if (nl >= 2 * ML) mainloop_v<MT, ML, 2 * ML>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else if (nl == 2 * ML - 1) mainloop_v<MT, ML, 2 * ML - 1>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else mainloop_v<MT, ML, 2 * ML - 2>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
 }
 
-__device__ __forceinline__ void zero(f32x16_t (&acc)[2][4]) {
+template <int MT, class ABase, class BBase>
+__device__ __forceinline__ void mainloop(int nk, int ml, int nl, lds_char* lds, ABase a_base,
+                                         const uint32_t (&a_off)[MT][A_DMA], BBase b_base, uint32_t b_off,
+                                         const int (&bcol)[4], f32x16_t (&acc)[MT][2][4]) {
+  // every wave takes part in the DMAs and barriers, whatever its live rows
+  if constexpr (MT >= 3) {
+    if (ml >= 3) return mainloop_ml<MT, 3>(nk, nl, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  }
+  if constexpr (MT >= 2) {
+    if (ml == 2) return mainloop_ml<MT, 2>(nk, nl, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  }
+  mainloop_ml<MT, 1>(nk, nl, lds, a_base, a_off, b_base, b_off, bcol, acc);
+}
+
+// live row tiles of a workgroup whose first row is m0 and that may hold MT tiles, and this wave's
+// live 32-row sub-tiles (wave row block wm: rows t*128 + wm*64 + {0, 32})
+template <int MT>
+__device__ __forceinline__ void live_tiles(int rows_left, int wm, int& ml, int& nl) {
+  ml = min(MT, (rows_left + 127) / 128);
+  nl = 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < 2; ++i) nl += (t < ml && t * 128 + wm * 64 + i * 32 < rows_left) ? 1 : 0;
+}
+
+template <int MT>
+__device__ __forceinline__ void zero(f32x16_t (&acc)[MT][2][4]) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][i][j][r] = 0.f;
 }
 
 // Workgroup-index remap so that consecutive logical tiles run on the same XCD: workgroups are
@@ -190,6 +257,9 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[2][4]) {
 // [x*q + min(x, r), ...) of n = 8q + r go to XCD x, in order. Returns -1 for b >= n.
 __device__ __forceinline__ int xcd_remap(int b, int n) {
   if (b >= n) return -1;
+#ifdef MOE_VARIANT_NO_XCD_REMAP
+  return b;
+#endif
   const int q = n >> 3, r = n & 7;
   const int x = b & 7, i = b >> 3;
   return x * q + min(x, r) + i;
