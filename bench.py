@@ -25,7 +25,16 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s; % HBM BW peak (decode) / % bf16 MFMA peak (prefill)"
 KERNEL_FFN_GATE_UP = 3
-KERNEL_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_softmax_amd", "csrc", "grouped_ffn.hip")
+# sources the dominant kernel (grouped gate/up GEMM) is compiled from
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_mixture_experts_softmax_amd", "csrc", f)
+                  for f in ("grouped_ffn.hip", "stream_gemm.h", "moe_internal.h")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 class HipEvents:
@@ -70,8 +79,7 @@ def traffic_for(workload):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src_hash = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != src_hash:
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
 
@@ -104,6 +112,39 @@ def cpu_baseline(cfg, sample_tokens):
 CPU_SAMPLE = {"tiny": 64, "mid": 1024, "decode": 32, "prefill": 16, "skew": 16}
 
 
+def calibrate():
+    """Reference points on this GPU, outside the MoE path: the vendor bf16 GEMM (torch.matmul,
+    hipBLASLt) on dense shapes, including one expert's gate/up shape, and device copy bandwidth."""
+    import torch
+
+    def t_ms(fn, n=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    out = {"matmul_bf16": [], "copy": []}
+    for (M, K, N) in [(8192, 8192, 8192), (4096, 8192, 4096), (16384, 2048, 8192), (320, 8192, 4096)]:
+        A = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        B = torch.randn(K, N, device="cuda", dtype=torch.bfloat16)
+        ms = t_ms(lambda: A @ B)
+        out["matmul_bf16"].append({"M": M, "K": K, "N": N, "ms": ms, "tflops": 2 * M * K * N / ms / 1e9})
+        del A, B
+    for nbytes in [1 << 30, 4 << 30]:
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        ms = t_ms(lambda: dst.copy_(src), 10)
+        out["copy"].append({"bytes": nbytes, "ms": ms, "read_plus_write_tbps": 2 * nbytes / ms / 1e9})
+        del src, dst
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +154,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy, the reference kernel for HBM byte counters")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only measure reference points (vendor bf16 GEMM, device copy) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -120,6 +163,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d, WORLD_SIZE %d)"
               % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate:
+        calibrate()
+        return
 
     import torch
 
@@ -197,7 +244,7 @@ def main():
                 "peak": peak_flops / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_for(cfg.name)
-    roof["kernel"] = "ffn_mfma_kernel<gate/up>" if cfg.dtype == syn.BF16 else "ffn_f32_kernel<gate/up>"
+    roof["kernel"] = "ffn_mfma_stream_kernel<true, 1> (gate/up)" if cfg.dtype == syn.BF16 else "ffn_f32_kernel<true>"
     roof["kernel_ms"] = kern_avg_ms
     roof["algorithmic_bytes"] = kb
     roof["algorithmic_flops"] = kf
