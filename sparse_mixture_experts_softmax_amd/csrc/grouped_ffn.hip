@@ -306,40 +306,46 @@ ffn_mfma_kernel(MfmaArgs p) {
 
 // ------------------------------------------------------------------------------------------
 // bf16 MFMA grouped GEMM, streaming variant for aligned shapes (K % 32 == 0, N % tile == 0):
-// the shared DMA/LDS-transpose mainloop of stream_gemm.h on 128 x 256 tiles.
+// the shared DMA/LDS-transpose mainloop of stream_gemm.h on 128 x (128*WN) tiles. WN = 2: four
+// wavefronts per workgroup and two workgroups per CU, so that one workgroup's prologue and
+// epilogue overlap the other's mainloop. WN = 4: eight wavefronts and one workgroup per CU, with
+// more LDS bytes in flight per FLOP for long K loops. For the gate/up product the tile's columns
+// are half gate, half up: columns [0, 64*WN) of the tile are gate columns n0 .. and the next
+// 64*WN the up columns with the same indices, so each wavefront holds matching gate and up
+// accumulators for the fused silu(g)*u epilogue.
 //
 // Tiles are ordered expert-major -- (group, column tile, row tile) -- and the workgroup index
 // is remapped so that consecutive tiles run on the same XCD: an expert's row tiles share its
 // weight panels and its column tiles share its gathered rows through that XCD's L2.
 // ------------------------------------------------------------------------------------------
-template <bool GATED, int MT>
-__global__ void __launch_bounds__(256, MT == 1 ? 2 : 1)
-ffn_mfma_stream_kernel(MfmaArgs p) {
+template <bool GATED, int WN, int S>
+__global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_kernel(MfmaArgs p) {
   using namespace stream;
-  constexpr int BMW = MT * SBM;  // rows per workgroup
-  __shared__ __attribute__((aligned(1024))) char smem[3 * stage_bytes<MT>()];
+  using GEO = Geo<WN>;
+  constexpr int TN = GATED ? GEO::COLS / 2 : GEO::COLS;  // output columns per tile
+  __shared__ __attribute__((aligned(1024))) char smem[S * GEO::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
 
   // logical tile -> (group, column tile, row tile)
   const int L = xcd_remap(blockIdx.x, *p.tile_count * p.n_ntiles);
   if (L < 0) return;
   const int probe = L / p.n_ntiles;
   const int g = p.tile_group[probe];
-  const int first = probe - p.tile_m0[probe] / BMW;  // the group's first row tile
+  const int first = probe - p.tile_m0[probe] / SBM;  // the group's first row tile
   const Group G = group_info(g, p.offsets, p.T, p.k, p.E, p.I, p.Is);
-  const int cnt = (G.rows + BMW - 1) / BMW;
+  const int cnt = (G.rows + SBM - 1) / SBM;
   const int local = L - p.n_ntiles * first;
   const int nt = local / cnt;
-  const int m0 = (local % cnt) * BMW;
+  const int m0 = (local % cnt) * SBM;
 
   const int K = GATED ? p.d : G.n_inter;
   const int N = GATED ? G.n_inter : p.d;
-  const int n0 = nt * (GATED ? kMfmaBN1 : kMfmaBN2);
+  const int n0 = nt * TN;
   if (n0 >= N) return;
 
   const bf16_t* W0;
@@ -353,86 +359,83 @@ ffn_mfma_stream_kernel(MfmaArgs p) {
 
   // DMA sources: uniform bases per k-step, 32-bit per-lane byte offsets
   const int64_t a_pitch = (GATED ? (int64_t)p.d : (int64_t)p.ldh) * 2;
-  uint32_t a_off[MT][A_DMA];
+  uint32_t a_off[GEO::A_DMA];
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
-#pragma unroll
-    for (int i = 0; i < A_DMA; ++i) {
-      const int m = t * SBM + a_dma_row(wave, i, lane);
-      const int r = (m0 + m < G.rows) ? m : 0;  // rows past the group re-read its first row
-      int64_t src_row;
-      if (GATED)
-        src_row = G.shared ? (int64_t)(m0 + r) : (int64_t)p.sorted_token[G.row0 + m0 + r];
-      else
-        src_row = G.row0 + m0 + r;
-      a_off[t][i] = (uint32_t)(src_row * a_pitch) + a_dma_chunk_bytes(lane);
-    }
+  for (int i = 0; i < GEO::A_DMA; ++i) {
+    const int m = a_dma_row<WN>(wave, i, lane);
+    const int r = (m0 + m < G.rows) ? m : 0;  // rows past the group re-read its first row
+    int64_t src_row;
+    if (GATED)
+      src_row = G.shared ? (int64_t)(m0 + r) : (int64_t)p.sorted_token[G.row0 + m0 + r];
+    else
+      src_row = G.row0 + m0 + r;
+    a_off[i] = (uint32_t)(src_row * a_pitch) + a_dma_chunk_bytes(lane);
+  }
   const char* a_src = uniform_ptr((const char*)p.a_src);
   auto a_base = [=](int kt) { return a_src + kt * (SBK * 2); };
 
+  // B: this wave's DMAs fill one 128-column block of the tile; for gate/up, blocks 0 .. WN/2-1
+  // come from W_g and the rest from W_u, at the same columns
   const int64_t b_pitch = (int64_t)N * 2;
-  const int half = b_dma_half(wave);
+  const int blk = b_dma_block<WN>(wave);
   const char* b_mat;
   if (GATED)
-    b_mat = (const char*)(half == 0 ? W0 : W1) + (int64_t)n0 * 2;
+    b_mat = (const char*)(blk < WN / 2 ? W0 : W1) + (int64_t)(n0 + 128 * (blk % (WN / 2))) * 2;
   else
-    b_mat = (const char*)W0 + (int64_t)(n0 + 128 * half) * 2;
-  const char* b0 = uniform_ptr(b_mat + (int64_t)b_dma_row0(wave, 0) * b_pitch);
+    b_mat = (const char*)W0 + (int64_t)(n0 + 128 * blk) * 2;
+  const char* b0 = uniform_ptr(b_mat + (int64_t)b_dma_row0<WN>(wave, 0) * b_pitch);
   const int64_t b_kstep = (int64_t)SBK * b_pitch;
-  // the wave's four B instructions load consecutive 4-row blocks
+  // the wave's B instructions load consecutive 4-row groups of one block
   auto b_base = [=](int kt, int i) { return b0 + kt * b_kstep + i * 4 * b_pitch; };
   const uint32_t b_off = b_dma_lane_offset(lane, (uint32_t)b_pitch);
 
   int bcol[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bcol[j] = GATED ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
-  int ml, nl;
-  live_tiles<MT>(G.rows - m0, wm, ml, nl);
+  for (int j = 0; j < 4; ++j) bcol[j] = GATED ? (j >> 1) * TN + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+  const int nl = live_subtiles(G.rows - m0, wm);
 
-  f32x16_t acc[MT][2][4];
+  f32x16_t acc[2][4];
   zero(acc);
-  mainloop<MT>(K / SBK, ml, nl, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+  mainloop<WN, S>(K / SBK, nl, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
 
   // epilogue: 32x32 accumulator -- lane holds column (lane & 31); register r holds row
   // 8*(r/4) + 4*(lane/32) + (r%4)
   const int col_in = lane & 31;
   const int row_hi = (lane >> 5) * 4;
+  if (GATED) {
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    if (GATED) {
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int jj = 0; jj < 2; ++jj) {
+        const int col = n0 + wn * 64 + jj * 32 + col_in;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int col = n0 + wn * 64 + jj * 32 + col_in;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = t * SBM + wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
-            if (m0 + row < G.rows)
-              p.out[(G.row0 + m0 + row) * (int64_t)p.ldh + col] =
-                  f32_to_bf16(silu_f32(acc[t][i][jj][r]) * acc[t][i][jj + 2][r]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          if (m0 + row < G.rows)
+            p.out[(G.row0 + m0 + row) * (int64_t)p.ldh + col] =
+                f32_to_bf16(silu_f32(acc[i][jj][r]) * acc[i][jj + 2][r]);
         }
-    } else {
+      }
+  } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 128 + j * 32 + col_in;
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 128 + j * 32 + col_in;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = t * SBM + wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
-            if (m0 + row < G.rows) p.out[(G.row0 + m0 + row) * (int64_t)p.d + col] = f32_to_bf16(acc[t][i][j][r]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          if (m0 + row < G.rows) p.out[(G.row0 + m0 + row) * (int64_t)p.d + col] = f32_to_bf16(acc[i][j][r]);
         }
-    }
+      }
   }
 }
 
+// wn: wave columns of the streaming tile (2: 128 x 256, 4: 128 x 512)
 template <bool GATED>
-void launch_stream(int mt, unsigned grid, hipStream_t s, const MfmaArgs& a) {
-  (void)mt;
-  hipLaunchKernelGGL((ffn_mfma_stream_kernel<GATED, 1>), dim3(grid), dim3(256), 0, s, a);
+void launch_stream(int wn, unsigned grid, hipStream_t s, const MfmaArgs& a) {
+  if (wn == 4) hipLaunchKernelGGL((ffn_mfma_stream_kernel<GATED, 4, 4>), dim3(grid), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((ffn_mfma_stream_kernel<GATED, 2, 3>), dim3(grid), dim3(256), 0, s, a);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -571,10 +574,14 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
   const bool stream_ok = dm.dtype == MOE_BF16 && dm.d % 256 == 0 && dm.I % 128 == 0 && dm.I_shared % 128 == 0 &&
                          (uint64_t)dm.T * dm.d * 2 < (1ull << 32) &&
                          (uint64_t)L.rows_total * L.ldh * 2 < (1ull << 32);
-  // one 128-row tile per streaming workgroup: two such workgroups share a CU, and that
-  // occupancy hides more latency than the weight reuse of taller tiles saves
-  const int mt = 1;
-  const int bm = dm.dtype == MOE_F32 ? kF32BM : kMfmaBM * mt;
+  // 128 x 512 streaming tiles (one workgroup per CU) for long K loops, where the shape divides
+  // them: the gate/up product at d >= 4096, the down product at I >= 2048 with at least 64 rows per
+  // expert on average. Short K loops (and the near-empty row tiles of decode) run faster on
+  // 128 x 256 tiles, two workgroups per CU, whose prologues and epilogues overlap.
+  const double rows_per_expert = (double)dm.T * dm.k / dm.E;
+  const int wn1 = stream_ok && dm.I % 256 == 0 && dm.I_shared % 256 == 0 && dm.d >= 4096 ? 4 : 2;
+  const int wn2 = stream_ok && dm.d % 512 == 0 && dm.I >= 2048 && rows_per_expert >= 64.0 ? 4 : 2;
+  const int bm = dm.dtype == MOE_F32 ? kF32BM : kMfmaBM;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, dm.T, dm.E, has_shared, bm, tg, tm, tc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -605,10 +612,11 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.w0_s = (const bf16_t*)wg_s;
     a.w1_s = (const bf16_t*)wu_s;
     a.out = (bf16_t*)H;
-    a.n_ntiles = (nmax + kMfmaBN1 - 1) / kMfmaBN1;
+    const int tn1 = stream_ok ? 64 * wn1 : kMfmaBN1;
+    a.n_ntiles = (nmax + tn1 - 1) / tn1;
     if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
     if (stream_ok)
-      launch_stream<true>(mt, (unsigned)(max_mt * a.n_ntiles), s, a);
+      launch_stream<true>(wn1, (unsigned)(max_mt * a.n_ntiles), s, a);
     else
       hipLaunchKernelGGL(ffn_mfma_kernel<true>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -620,10 +628,11 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.w0_s = (const bf16_t*)wd_s;
     a.w1_s = nullptr;
     a.out = (bf16_t*)y;
-    a.n_ntiles = (dm.d + kMfmaBN2 - 1) / kMfmaBN2;
+    const int tn2 = stream_ok ? 128 * wn2 : kMfmaBN2;
+    a.n_ntiles = (dm.d + tn2 - 1) / tn2;
     if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
     if (stream_ok)
-      launch_stream<false>(mt, (unsigned)(max_mt * a.n_ntiles), s, a);
+      launch_stream<false>(wn2, (unsigned)(max_mt * a.n_ntiles), s, a);
     else
       hipLaunchKernelGGL(ffn_mfma_kernel<false>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(256, 2)
 router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ planes, float* __restrict__ part,
                    int64_t T, int d, int E, int ksteps) {
   using namespace stream;
-  __shared__ __attribute__((aligned(1024))) char smem[3 * stage_bytes<1>()];
+  __shared__ __attribute__((aligned(1024))) char smem[3 * Geo<2>::STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -80,28 +80,27 @@ router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ plan
   const int kt0 = split * ksteps;
   const int nk = min(ksteps, 3 * dk - kt0);
 
-  uint32_t a_off[1][A_DMA];
+  uint32_t a_off[Geo<2>::A_DMA];
 #pragma unroll
-  for (int i = 0; i < A_DMA; ++i) {
-    const int64_t row = min(t0 + a_dma_row(wave, i, lane), T - 1);
-    a_off[0][i] = (uint32_t)(row * d * 2) + a_dma_chunk_bytes(lane);
+  for (int i = 0; i < Geo<2>::A_DMA; ++i) {
+    const int64_t row = min(t0 + a_dma_row<2>(wave, i, lane), T - 1);
+    a_off[i] = (uint32_t)(row * d * 2) + a_dma_chunk_bytes(lane);
   }
   const char* xb = uniform_ptr((const char*)x);
   auto a_base = [=](int kt) { return xb + ((kt0 + kt) % dk) * (SBK * 2); };
   const int64_t pitch = (int64_t)E * 2;
-  const char* pb = uniform_ptr((const char*)planes + (int64_t)(e0 + 128 * b_dma_half(wave)) * 2 +
-                               ((int64_t)kt0 * SBK + b_dma_row0(wave, 0)) * pitch);
+  const char* pb = uniform_ptr((const char*)planes + (int64_t)(e0 + 128 * b_dma_block<2>(wave)) * 2 +
+                               ((int64_t)kt0 * SBK + b_dma_row0<2>(wave, 0)) * pitch);
   auto b_base = [=](int kt, int i) { return pb + (int64_t)kt * SBK * pitch + i * 4 * pitch; };
   const uint32_t b_off = b_dma_lane_offset(lane, (uint32_t)pitch);
   int bcol[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) bcol[j] = wn * 128 + j * 32;
-  int ml, nl;
-  live_tiles<1>((int)min<int64_t>(T - t0, 128), wm, ml, nl);
+  const int nl = live_subtiles((int)min<int64_t>(T - t0, 128), wm);
 
-  f32x16_t acc[1][2][4];
+  f32x16_t acc[2][4];
   zero(acc);
-  mainloop<1>(nk, ml, nl, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+  mainloop<2, 3>(nk, nl, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
 
   float* out = part + (int64_t)split * T * E;
   const int col_in = lane & 31;
@@ -114,7 +113,7 @@ router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ plan
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t t = t0 + wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
-        if (t < T) out[t * E + e] = acc[0][i][j][r];
+        if (t < T) out[t * E + e] = acc[i][j][r];
       }
     }
 }

@@ -1,23 +1,25 @@
 // Streaming bf16 MFMA tile mainloop for gfx950, shared by the grouped expert GEMMs and the
 // router GEMM.
 //
-// One 256-thread workgroup (4 wavefronts in 2x2) accumulates an (MT*128) x 256 fp32 tile
-// acc += A[MT*128 x K] * B[K x 256] with v_mfma_f32_32x32x16_bf16: MT (1..3) row tiles of 128 share
-// every B tile, so a weight panel is streamed from HBM once for up to MT*128 rows. Each wavefront
-// owns 64 rows of every row tile and 128 columns.
+// One workgroup of 2*WN wavefronts accumulates a 128 x (128*WN) fp32 tile
+// acc += A[128 x K] * B[K x 128*WN] with v_mfma_f32_32x32x16_bf16. Wavefront w owns rows
+// 64*(w / WN) .. +64 and columns 128*(w % WN) .. +128 (2 x 4 sub-tiles of 32 x 32). WN = 2 gives a
+// 128 x 256 tile of four wavefronts (two workgroups per CU); WN = 4 a 128 x 512 tile of eight (one
+// workgroup per CU, two wavefronts per SIMD, more of the CU's LDS in flight per FLOP).
 //
 // Operands move HBM -> LDS with gfx950's direct global-to-LDS loads (16 bytes per lane; lane
 // l's bytes land at the instruction's LDS base + 16*l), so no registers hold tiles in flight and
-// three 24 KB stages are in flight per workgroup. Each DMA instruction takes a wave-uniform
-// 64-bit base (SGPRs) plus a 32-bit per-lane byte offset, and each lane picks its offset so
-// that the LDS tile comes out XOR-swizzled at 16-byte granularity:
-//   A tiles [128 rows][32 K], 64 B per row: chunk c of row m sits at slot c ^ ((m >> 2) & 3).
-//     Per row tile, A instruction q (0..7, wave w issues q = 2w, 2w+1) loads rows 16q .. 16q+15:
-//     lane l takes row 16q + l/4, chunk (l & 3) ^ ((l >> 4) & 3).
-//   B tile: two halves [32 K][128 N] (N-contiguous as stored in HBM), 256 B per row: chunk c
-//     of row k sits at slot c ^ (4 * (k & 3)). B instruction q (0..15, wave w issues 4w..4w+3)
-//     loads half q/8, rows 4*(q%8) .. +3: lane l takes row 4*(q%8) + l/16, chunk
-//     (l & 15) ^ (4 * ((l >> 4) & 3)) -- the same per-lane offset for every B instruction.
+// S stages (8 KB of A + WN * 8 KB of B each) are in flight per workgroup. Each DMA instruction takes
+// a wave-uniform 64-bit base (SGPRs) plus a 32-bit per-lane byte offset, and each lane picks its
+// offset so that the LDS tile comes out XOR-swizzled at 16-byte granularity:
+//   A tile [128 rows][32 K], 64 B per row: chunk c of row m sits at slot c ^ ((m >> 2) & 3).
+//     A instruction q (0..7; wave w issues the A_DMA instructions from w*A_DMA) loads rows
+//     16q .. 16q+15: lane l takes row 16q + l/4, chunk (l & 3) ^ ((l >> 4) & 3).
+//   B tile: WN blocks [32 K][128 N] (N-contiguous as stored in HBM), 256 B per row: chunk c of
+//     row k sits at slot c ^ (4 * (k & 3)). B instruction q (0..8*WN-1; wave w issues the B_DMA
+//     instructions from w*B_DMA) loads block q/8, rows 4*(q%8) .. +3: lane l takes row
+//     4*(q%8) + l/16, chunk (l & 15) ^ (4 * ((l >> 4) & 3)) -- the same per-lane offset for every
+//     B instruction.
 // A fragments are ds_read_b128 of 8 consecutive K values. B fragments come straight from the
 // N-contiguous tile with ds_read_b64_tr_b16: within each 16-lane group, lane 4j+q points at row
 // kb+j, columns nb+4q..nb+4q+3, and lane i receives column nb+i at rows kb..kb+3; two such reads
@@ -38,29 +40,37 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int SBM = 128;
 constexpr int SBK = 32;
-constexpr int SBN = 256;
-constexpr int A_BYTES = SBM * SBK * 2;       // 8 KB
-constexpr int B_BYTES = SBK * SBN * 2;       // 16 KB
-constexpr int STAGE = A_BYTES + B_BYTES;     // 24 KB for one row tile
-// stage bytes with MT row tiles: [A tile 0] .. [A tile MT-1] [B half 0] [B half 1]
-template <int MT>
-constexpr int stage_bytes() { return MT * A_BYTES + B_BYTES; }
-constexpr int A_DMA = A_BYTES / 1024 / 4;    // DMA instructions per wave per stage: 2
-constexpr int B_DMA = B_BYTES / 1024 / 4;    // 4
-constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
+constexpr int SBM = 128;                     // tile rows
+constexpr int BLOCK_BYTES = SBK * 128 * 2;   // one 128-column block of the B tile, 8 KB
 
-constexpr int HALF_BYTES = B_BYTES / 2;     // one 128-column half of the B tile
+template <int WN>
+struct Geo {
+  static_assert(WN == 2 || WN == 4, "two or four wave columns");
+  static constexpr int NW = 2 * WN;                 // wavefronts
+  static constexpr int COLS = 128 * WN;             // tile columns
+  static constexpr int A_BYTES = SBM * SBK * 2;     // 8 KB
+  static constexpr int B_BYTES = WN * BLOCK_BYTES;  // 16 or 32 KB
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_DMA = A_BYTES / 1024 / NW;  // A DMA instructions per wave per stage
+  static constexpr int B_DMA = B_BYTES / 1024 / NW;  // B DMA instructions per wave per stage
+  static constexpr int DMA = A_DMA + B_DMA;
+};
 
 // A-tile row loaded by this lane's i-th A DMA instruction, and the lane's byte offset inside
 // that row (16-byte chunk, swizzled)
-__device__ __forceinline__ int a_dma_row(int wave, int i, int lane) { return (wave * A_DMA + i) * 16 + (lane >> 2); }
+template <int WN>
+__device__ __forceinline__ int a_dma_row(int wave, int i, int lane) {
+  return (wave * Geo<WN>::A_DMA + i) * 16 + (lane >> 2);
+}
 __device__ __forceinline__ int a_dma_chunk_bytes(int lane) { return ((lane & 3) ^ ((lane >> 4) & 3)) << 4; }
-// B: half and first row of this wave's i-th instruction (uniform), and the lane's offset
-// (row within the 4-row block, swizzled chunk) for a matrix with row pitch `pitch` bytes
-__device__ __forceinline__ int b_dma_half(int wave) { return wave >> 1; }
-__device__ __forceinline__ int b_dma_row0(int wave, int i) { return 4 * ((wave * B_DMA + i) & 7); }
+// B: 128-column block and first row of this wave's i-th instruction (uniform; a wave's
+// instructions load consecutive 4-row groups of one block), and the lane's offset (row within the
+// 4-row group, swizzled chunk) for a matrix with row pitch `pitch` bytes
+template <int WN>
+__device__ __forceinline__ int b_dma_block(int wave) { return (wave * Geo<WN>::B_DMA) >> 3; }
+template <int WN>
+__device__ __forceinline__ int b_dma_row0(int wave, int i) { return 4 * ((wave * Geo<WN>::B_DMA + i) & 7); }
 __device__ __forceinline__ uint32_t b_dma_lane_offset(int lane, uint32_t pitch) {
   return (uint32_t)(lane >> 4) * pitch + ((((lane & 15) ^ (4 * ((lane >> 4) & 3)))) << 4);
 }
@@ -77,6 +87,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 __device__ __forceinline__ void barrier_lds_only() { asm volatile("s_barrier" ::: "memory"); }
+// the wave's LDS reads have returned, then the workgroup barrier
+__device__ __forceinline__ void barrier_after_lds_reads() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // 16 bytes per lane from base + voff (base wave-uniform, voff per lane) to LDS byte address
 // dst_base + 16 * lane (dst_base wave-uniform)
@@ -97,40 +111,52 @@ __device__ __forceinline__ bf16x8_t read_a(const lds_char* st, int m, int c) {
   return *(const __attribute__((address_space(3))) bf16x8_t*)(st + off);
 }
 
-// sb: start of the B region of a stage; n is the tile column 0..255 (half n / 128)
+// sb: start of the B region of a stage; n is the tile column (block n / 128)
 __device__ __forceinline__ s16x4_t read_b_tr(const lds_char* sb, int k, int n) {
   const int h = n >> 7, c = n & 127;
-  const int off = h * HALF_BYTES + k * 256 + (((c >> 3) ^ (4 * (k & 3))) << 4) + ((c & 7) << 1);
+  const int off = h * BLOCK_BYTES + k * 256 + (((c >> 3) ^ (4 * (k & 3))) << 4) + ((c & 7) << 1);
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(sb + off));
 }
 
-// acc[t][i][j] += A * B over nk K-steps of 32.
-//   MT: row tiles held in each stage; ML (1..MT): row tiles of this workgroup holding any valid row
-//     (only those are loaded); NL: 32-row sub-tiles of this wave holding any valid row, counted in
-//     the order (tile 0: sub 0, sub 1), (tile 1: ...), ... (only those are multiplied);
-//   lds: the workgroup's 3 * stage_bytes<MT>() bytes of LDS;
-//   a_base(kt): uniform base of the A rows at k-step kt; a_off[t][i]: this lane's byte offset for
-//     its i-th A instruction of row tile t (row offset + swizzled chunk);
+// acc[i][j] += A * B over nk K-steps of 32.
+//   WN: wave columns (Geo); S: LDS stages (DMA lookahead S k-steps); NL: 32-row sub-tiles of
+//     this wave holding any valid row (0, 1 or 2; only those are multiplied);
+//   lds: the workgroup's S * Geo<WN>::STAGE bytes of LDS;
+//   a_base(kt): uniform base of the A rows at k-step kt; a_off[i]: this lane's byte offset for
+//     its i-th A instruction (row offset + swizzled chunk);
 //   b_base(kt, i): uniform base of this wave's i-th B instruction at k-step kt (its half, its
 //     first row); b_off: this lane's byte offset, common to all B instructions;
 //   bcol[j]: tile column of the wave's j-th 32-wide B sub-tile.
 //
-// Schedule. Three stages hold k-steps kt, kt+1, kt+2. Fragments (the A and B operands of one
-// 16-wide K sub-step) are read from LDS one sub-step ahead of the MFMAs that use them. After the
-// MFMAs of a stage's last sub-step are issued, the wave waits for its own DMAs of the next stage
-// and meets the others at the barrier while those MFMAs run; past the barrier every wave has
-// finished reading stage kt, so the DMAs for k-step kt+3 go into it, and the first fragments of
-// stage kt+1 are read.
-template <int MT, int ML, int NL, class ABase, class BBase>
-__device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base, const uint32_t (&a_off)[MT][A_DMA],
-                                           BBase b_base, uint32_t b_off, const int (&bcol)[4],
-                                           f32x16_t (&acc)[MT][2][4]) {
-  constexpr int STG = stage_bytes<MT>();
-  constexpr int DMA = ML * A_DMA + B_DMA;  // DMA instructions per wave per stage
+// Schedule. S stages hold k-steps kt .. kt+S-1. Fragments (the A and B operands of one 16-wide
+// K sub-step) are read from LDS one sub-step ahead of the MFMAs that use them. In each k-step the
+// second sub-step's fragments are requested, the first sub-step's MFMAs are issued, and then the
+// wave waits for its own DMAs of the next stage and for its fragment reads, and meets the others
+// at the barrier. Past the barrier every wave holds all of stage kt in registers, so the DMAs for
+// k-step kt+S go into it, and the next stage's first fragments are read while the second
+// sub-step's MFMAs run: LDS latency after the barrier hides behind MFMAs.
+
+// wait until at most n (0 .. 3) DMA groups of DMA instructions are outstanding
+template <int DMA>
+__device__ __forceinline__ void wait_groups(int n) {
+  if (n >= 3) wait_vmcnt<3 * DMA>();
+  else if (n == 2) wait_vmcnt<2 * DMA>();
+  else if (n == 1) wait_vmcnt<DMA>();
+  else wait_vmcnt<0>();
+}
+
+template <int WN, int S, int NL, class ABase, class BBase>
+__device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
+                                           const uint32_t (&a_off)[Geo<WN>::A_DMA], BBase b_base, uint32_t b_off,
+                                           const int (&bcol)[4], f32x16_t (&acc)[2][4]) {
+  static_assert(S >= 3 && S <= 5, "stages");
+  using GEO = Geo<WN>;
+  constexpr int STG = GEO::STAGE;
+  constexpr int DMA = GEO::DMA;  // DMA instructions per wave per stage
   constexpr int NA = NL > 0 ? NL : 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1;
+  const int wm = wave / WN;
   const int g16 = lane >> 4;
   const int i16 = lane & 15;
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
@@ -139,24 +165,22 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base, 
     const uint32_t dst = lds_base + stage * STG;
     const char* ab = a_base(kt);
 #pragma unroll
-    for (int t = 0; t < ML; ++t)
+    for (int i = 0; i < GEO::A_DMA; ++i) dma16(ab, a_off[i], dst + (wave * GEO::A_DMA + i) * 1024);
 #pragma unroll
-      for (int i = 0; i < A_DMA; ++i) dma16(ab, a_off[t][i], dst + t * A_BYTES + (wave * A_DMA + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < B_DMA; ++i) dma16(b_base(kt, i), b_off, dst + MT * A_BYTES + (wave * B_DMA + i) * 1024);
+    for (int i = 0; i < GEO::B_DMA; ++i)
+      dma16(b_base(kt, i), b_off, dst + GEO::A_BYTES + (wave * GEO::B_DMA + i) * 1024);
   };
   // fragments of sub-step s (0 or 1) of the stage at st
   auto read = [&](const lds_char* st, int s, bf16x8_t (&a)[NA], bf16x8_t (&b)[4]) {
     if constexpr (NL > 0) {
 #pragma unroll
-      for (int u = 0; u < NL; ++u)
-        a[u] = read_a(st + (u >> 1) * A_BYTES, wm * 64 + (u & 1) * 32 + (lane & 31), 2 * s + (lane >> 5));
+      for (int u = 0; u < NL; ++u) a[u] = read_a(st, wm * 64 + u * 32 + (lane & 31), 2 * s + (lane >> 5));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kb = 16 * s + 8 * (g16 >> 1) + (i16 >> 2);
         const int n = bcol[j] + 16 * (g16 & 1) + 4 * (i16 & 3);
-        const s16x4_t lo = read_b_tr(st + MT * A_BYTES, kb, n);
-        const s16x4_t hi = read_b_tr(st + MT * A_BYTES, kb + 4, n);
+        const s16x4_t lo = read_b_tr(st + GEO::A_BYTES, kb, n);
+        const s16x4_t hi = read_b_tr(st + GEO::A_BYTES, kb + 4, n);
         b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
@@ -166,18 +190,15 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base, 
 #pragma unroll
       for (int u = 0; u < NL; ++u)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[u >> 1][u & 1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[j], acc[u >> 1][u & 1][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[j], acc[u][j], 0, 0, 0);
     }
   };
 
-  // prologue: three stages in flight, stage 0 complete
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
-  if (nk > 2) issue(2, 2);
-  if (nk > 2) wait_vmcnt<2 * DMA>();
-  else if (nk > 1) wait_vmcnt<DMA>();
-  else wait_vmcnt<0>();
+  // prologue: S stages in flight, stage 0 complete
+#pragma unroll
+  for (int i = 0; i < S; ++i)
+    if (i < nk) issue(i, i);
+  wait_groups<DMA>(min(S - 1, nk - 1));
   barrier_lds_only();
 
   bf16x8_t a0[NA], b0[4], a1[NA], b1[4];
@@ -185,71 +206,46 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base, 
   int stage = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const lds_char* cur = lds + stage * STG;
-    const int next = stage == 2 ? 0 : stage + 1;
+    const int next = stage == S - 1 ? 0 : stage + 1;
     read(cur, 1, a1, b1);
     mma(a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < nk) {
-      // stage kt+1 complete once at most the DMAs of k-step kt+2 are outstanding
-      if (kt + 2 < nk) wait_vmcnt<DMA>();
-      else wait_vmcnt<0>();
-      barrier_lds_only();
-      if (kt + 3 < nk) issue(kt + 3, stage);
+      // stage kt+1 complete once at most the DMAs of k-steps kt+2 .. kt+S-1 are outstanding
+      wait_groups<DMA>(min(S - 2, nk - kt - 2));
+      barrier_after_lds_reads();
+      if (kt + S < nk) issue(kt + S, stage);
       read(lds + next * STG, 0, a0, b0);
     }
+    mma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
     stage = next;
   }
 }
 
-// Dispatch on the live row tiles (ml) and this wave's live sub-tiles (nl) outside the K loop.
-// nl is one of 2ml-2, 2ml-1, 2ml: only the last row tile can be partial.
-template <int MT, int ML, class ABase, class BBase>
-__device__ __forceinline__ void mainloop_ml(int nk, int nl, lds_char* lds, ABase a_base,
-                                            const uint32_t (&a_off)[MT][A_DMA], BBase b_base, uint32_t b_off,
-                                            const int (&bcol)[4], f32x16_t (&acc)[MT][2][4]) {
-  if (nl >= 2 * ML) mainloop_v<MT, ML, 2 * ML>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
-  else if (nl == 2 * ML - 1) mainloop_v<MT, ML, 2 * ML - 1>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
-  else mainloop_v<MT, ML, 2 * ML - 2>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+// Dispatch on this wave's live 32-row sub-tiles (0, 1 or 2) outside the K loop. Every wave
+// takes part in the DMAs and barriers, whatever its live rows.
+template <int WN, int S, class ABase, class BBase>
+__device__ __forceinline__ void mainloop(int nk, int nl, lds_char* lds, ABase a_base,
+                                         const uint32_t (&a_off)[Geo<WN>::A_DMA], BBase b_base, uint32_t b_off,
+                                         const int (&bcol)[4], f32x16_t (&acc)[2][4]) {
+  if (nl >= 2) mainloop_v<WN, S, 2>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else if (nl == 1) mainloop_v<WN, S, 1>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else mainloop_v<WN, S, 0>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
 }
 
-template <int MT, class ABase, class BBase>
-__device__ __forceinline__ void mainloop(int nk, int ml, int nl, lds_char* lds, ABase a_base,
-                                         const uint32_t (&a_off)[MT][A_DMA], BBase b_base, uint32_t b_off,
-                                         const int (&bcol)[4], f32x16_t (&acc)[MT][2][4]) {
-  // every wave takes part in the DMAs and barriers, whatever its live rows
-  if constexpr (MT >= 3) {
-    if (ml >= 3) return mainloop_ml<MT, 3>(nk, nl, lds, a_base, a_off, b_base, b_off, bcol, acc);
-  }
-  if constexpr (MT >= 2) {
-    if (ml == 2) return mainloop_ml<MT, 2>(nk, nl, lds, a_base, a_off, b_base, b_off, bcol, acc);
-  }
-  mainloop_ml<MT, 1>(nk, nl, lds, a_base, a_off, b_base, b_off, bcol, acc);
+// this wave's live 32-row sub-tiles (rows 64*wm + {0, 32} of the tile) given the rows left
+__device__ __forceinline__ int live_subtiles(int rows_left, int wm) {
+  return (wm * 64 < rows_left) + (wm * 64 + 32 < rows_left);
 }
 
-// live row tiles of a workgroup whose first row is m0 and that may hold MT tiles, and this wave's
-// live 32-row sub-tiles (wave row block wm: rows t*128 + wm*64 + {0, 32})
-template <int MT>
-__device__ __forceinline__ void live_tiles(int rows_left, int wm, int& ml, int& nl) {
-  ml = min(MT, (rows_left + 127) / 128);
-  nl = 0;
+__device__ __forceinline__ void zero(f32x16_t (&acc)[2][4]) {
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) nl += (t < ml && t * 128 + wm * 64 + i * 32 < rows_left) ? 1 : 0;
-}
-
-template <int MT>
-__device__ __forceinline__ void zero(f32x16_t (&acc)[MT][2][4]) {
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][i][j][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
 // Workgroup-index remap so that consecutive logical tiles run on the same XCD: workgroups are
@@ -257,9 +253,6 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[MT][2][4]) {
 // [x*q + min(x, r), ...) of n = 8q + r go to XCD x, in order. Returns -1 for b >= n.
 __device__ __forceinline__ int xcd_remap(int b, int n) {
   if (b >= n) return -1;
-#ifdef MOE_VARIANT_NO_XCD_REMAP
-  return b;
-#endif
   const int q = n >> 3, r = n & 7;
   const int x = b & 7, i = b >> 3;
   return x * q + min(x, r) + i;

@@ -77,6 +77,12 @@ SMALL_CASES = [
     ("wide_E", 96, 64, 1024, 16, 16, 16, syn.BF16, 1, 0.0),
     ("router_mfma", 300, 256, 256, 8, 128, 128, syn.BF16, 1, 0.0),
     ("router_mfma_E512", 520, 512, 512, 10, 128, 0, syn.BF16, 0, 0.0),
+    ("rows_ragged", 1000, 256, 8, 2, 128, 128, syn.BF16, 1, 0.0),
+    ("narrow_shared_smaller", 333, 1024, 16, 4, 512, 256, syn.BF16, 1, 0.0),
+    # 128 x 512 streaming tiles: gate/up at d >= 4096 (shared expert wider than the routed ones),
+    # down at I >= 2048 with >= 64 rows per expert
+    ("wide_gate_up", 200, 4096, 8, 2, 256, 512, syn.BF16, 1, 0.0),
+    ("wide_down", 300, 512, 8, 2, 2048, 0, syn.BF16, 1, 0.0),
 ]
 
 
