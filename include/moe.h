@@ -95,13 +95,16 @@ moe_status moe_router_topk(const moe_dims* dims, const void* x, const float* w_r
                            hipStream_t stream);
 
 /* Dispatch: group the T*k (token, expert) pairs by expert.
- *   topk_idx        [T, k]  int32 (from moe_router_topk)
+ *   topk_idx        [T, k]  int32 (from moe_router_topk); a token's indices in
+ *                           [0, E) must be distinct, as top-k selection makes them
  * Outputs:
  *   expert_offsets  [E + 1] int32, expert e owns sorted slots
  *                           [expert_offsets[e], expert_offsets[e+1]); offsets[E] = T*k
  *   sorted_token    [T*k]   int32, token of each sorted slot; within an expert,
  *                           tokens ascend (stable)
- *   slot_of         [T*k]   int32, slot_of[t*k + j] = sorted slot of (t, topk_idx[t, j]) */
+ *   slot_of         [T*k]   int32, slot_of[t*k + j] = sorted slot of (t, topk_idx[t, j])
+ * Pairs whose index lies outside [0, E) are skipped: their slot_of is -1 and
+ * offsets[E] counts only the others (moe_combine then leaves them out). */
 moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets,
                        int32_t* sorted_token, int32_t* slot_of, void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -121,7 +124,8 @@ moe_status moe_grouped_ffn(const moe_dims* dims, const void* x, const int32_t* e
 
 /* Weighted combine plus shared expert:
  *   out[t] = sum_j topk_w[t, j] * y[slot_of[t*k + j]]  +  y[T*k + t] (if I_shared > 0)
- * summed in fp32 in the order j = 0..k-1 then the shared row; out [T, d] dtype. */
+ * summed in fp32 in the order j = 0..k-1 then the shared row; out [T, d] dtype.
+ * Pairs with slot_of = -1 contribute nothing. */
 moe_status moe_combine(const moe_dims* dims, const void* y, const int32_t* slot_of, const float* topk_w, void* out,
                        hipStream_t stream);
 

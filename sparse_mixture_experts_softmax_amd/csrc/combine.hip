@@ -6,26 +6,37 @@
 //   out[t] = sum_{j<k} w[t,j] * y[slot_of[t*k+j]]  +  y[T*k + t]
 //
 // One 256-thread workgroup per token; each thread owns 8 consecutive hidden
-// elements (16-byte bf16 or 2x16-byte fp32 loads), accumulates in fp32 in the
-// fixed order j = 0..k-1 then the shared row, and rounds once on store.
+// elements (16-byte bf16 or 2x16-byte fp32 loads), issues the loads of all k+1
+// rows before the first add, accumulates in fp32 in the fixed order j = 0..k-1
+// then the shared row, and rounds once on store. Pairs with slot_of = -1 (an
+// expert index outside [0, E) at dispatch) contribute nothing.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-__device__ __forceinline__ void load8(const bf16_t* p, float* v) {
-  const uint4 w = *(const uint4*)p;
-  v[0] = bf16lo_to_f32(w.x); v[1] = bf16hi_to_f32(w.x);
-  v[2] = bf16lo_to_f32(w.y); v[3] = bf16hi_to_f32(w.y);
-  v[4] = bf16lo_to_f32(w.z); v[5] = bf16hi_to_f32(w.z);
-  v[6] = bf16lo_to_f32(w.w); v[7] = bf16hi_to_f32(w.w);
+// 8 consecutive elements, raw (loaded) and widened to fp32
+struct Raw8bf { uint4 w; };
+struct Raw8f { float4 a, b; };
+__device__ __forceinline__ void load_raw(const bf16_t* p, Raw8bf& r) { r.w = *(const uint4*)p; }
+__device__ __forceinline__ void load_raw(const float* p, Raw8f& r) {
+  r.a = *(const float4*)p;
+  r.b = *(const float4*)(p + 4);
 }
-__device__ __forceinline__ void load8(const float* p, float* v) {
-  const float4 a = *(const float4*)p;
-  const float4 b = *(const float4*)(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+__device__ __forceinline__ void widen(const Raw8bf& r, float* v) {
+  v[0] = bf16lo_to_f32(r.w.x); v[1] = bf16hi_to_f32(r.w.x);
+  v[2] = bf16lo_to_f32(r.w.y); v[3] = bf16hi_to_f32(r.w.y);
+  v[4] = bf16lo_to_f32(r.w.z); v[5] = bf16hi_to_f32(r.w.z);
+  v[6] = bf16lo_to_f32(r.w.w); v[7] = bf16hi_to_f32(r.w.w);
 }
+__device__ __forceinline__ void widen(const Raw8f& r, float* v) {
+  v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+  v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+}
+template <typename ET> struct RawOf;
+template <> struct RawOf<bf16_t> { typedef Raw8bf type; };
+template <> struct RawOf<float> { typedef Raw8f type; };
+
 __device__ __forceinline__ void store8(bf16_t* p, const float* v) {
   uint4 w;
   w.x = pack_bf16x2(v[0], v[1]);
@@ -43,8 +54,8 @@ template <typename ET>
 __global__ void __launch_bounds__(256)
 combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, const float* __restrict__ topk_w,
                ET* __restrict__ out, int64_t T, int d, int k, int has_shared) {
-  __shared__ int s_slot[16];
-  __shared__ float s_w[16];
+  __shared__ int s_slot[kMaxK];
+  __shared__ float s_w[kMaxK];
   const int64_t t = blockIdx.x;
   if (threadIdx.x < k) {
     s_slot[threadIdx.x] = slot_of[t * k + threadIdx.x];
@@ -52,18 +63,28 @@ combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, co
   }
   __syncthreads();
   const int64_t shared_row = T * k + t;
+  typedef typename RawOf<ET>::type Raw;
   for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      float v[8];
-      load8(y + (int64_t)s_slot[j] * d + c, v);
-      const float w = s_w[j];
+    // every row's load is issued before the first add
+    Raw raw[kMaxK + 1];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k && s_slot[j] >= 0) load_raw(y + (int64_t)s_slot[j] * d + c, raw[j]);
+    if (has_shared) load_raw(y + shared_row * d + c, raw[kMaxK]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k && s_slot[j] >= 0) {
+        float v[8];
+        widen(raw[j], v);
+        const float w = s_w[j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+      }
     }
     if (has_shared) {
       float v[8];
-      load8(y + shared_row * d + c, v);
+      widen(raw[kMaxK], v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }

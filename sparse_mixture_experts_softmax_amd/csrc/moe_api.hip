@@ -43,7 +43,7 @@ moe_status check_dims(const moe_dims* dm) {
   if (dm->E < 1) return fail(MOE_ERR_INVALID_ARG, "E = %d < 1", dm->E);
   if (dm->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E = %d > 1024", dm->E);
   if (dm->k < 1 || dm->k > dm->E) return fail(MOE_ERR_INVALID_ARG, "k = %d outside [1, E = %d]", dm->k, dm->E);
-  if (dm->k > 16) return fail(MOE_ERR_UNSUPPORTED, "k = %d > 16", dm->k);
+  if (dm->k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k = %d > %d", dm->k, kMaxK);
   if (dm->d < 8 || dm->d % 8) return fail(MOE_ERR_INVALID_ARG, "d = %d is not a positive multiple of 8", dm->d);
   if (dm->I < 8 || dm->I % 8) return fail(MOE_ERR_INVALID_ARG, "I = %d is not a positive multiple of 8", dm->I);
   if (dm->I_shared < 0 || dm->I_shared % 8)

@@ -38,6 +38,7 @@ constexpr int kPermuteChunk = 256;     // tokens per permute workgroup
 constexpr int kRouterTileT = 64;       // router logits tile: tokens
 constexpr int kRouterTileE = 64;       // router logits tile: experts
 constexpr int kRouterKStep = 16;       // router K step
+constexpr int kMaxK = 16;              // largest k (experts per token) accepted
 constexpr int kMfmaBM = 128;           // bf16 grouped GEMM tile rows
 constexpr int kMfmaBN1 = 128;          // gate/up tile: intermediate columns (x2 for gate and up)
 constexpr int kMfmaBN2 = 256;          // down tile: hidden columns

@@ -13,6 +13,8 @@
 //                   then an exclusive scan over experts gives expert_offsets.
 //   permute_scatter slot = chunk base of the expert + rank; writes slot_of and
 //                   sorted_token.
+// A token's expert indices must be distinct (top-k output is). Pairs whose index
+// lies outside [0, E) are skipped: slot_of = -1.
 // All integer work; results are deterministic.
 #include "moe_internal.h"
 
@@ -48,7 +50,7 @@ permute_count_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int
         for (int w2 = 0; w2 < w; ++w2) r += __popcll(mask[w2 * E + e]);
         r += __popcll(mask[w * E + e] & below);
       }
-      rank[t * k + j] = r;
+      rank[t * k + j] = (unsigned)e < (unsigned)E ? r : -1;
     }
   }
   for (int e = tid; e < E; e += kPermuteChunk) {
@@ -113,7 +115,7 @@ permute_scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, i
   if (t >= T) return;
   for (int j = 0; j < k; ++j) {
     const int e = topk_idx[t * k + j];
-    if ((unsigned)e >= (unsigned)E) continue;
+    if ((unsigned)e >= (unsigned)E) continue;  // slot_of stays -1
     const int slot = chunk_counts[(int64_t)blockIdx.x * E + e] + slot_of[t * k + j];  // slot_of holds the rank
     slot_of[t * k + j] = slot;
     sorted_token[slot] = (int32_t)t;

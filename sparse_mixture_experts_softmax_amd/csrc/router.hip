@@ -210,8 +210,30 @@ router_logits_kernel(const XT* __restrict__ x, const float* __restrict__ wr, flo
   }
 }
 
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// Maximum over the 64 lanes of a wavefront, uniform result. Within each row of 16 lanes the
+// maximum spreads by DPP lane moves (swap neighbours, swap pairs, rotate by 4, rotate by 8);
+// the four row maxima are then read as scalars.
+__device__ __forceinline__ float dpp_max(float x, int ctrl) {
+  // ctrl is one of the four row-local moves below; every lane's source lane exists
+  int y = 0;
+  switch (ctrl) {
+    case 0xB1: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false); break;  // quad [1,0,3,2]
+    case 0x4E: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false); break;  // quad [2,3,0,1]
+    case 0x124: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false); break; // row_ror:4
+    default: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false); break;    // row_ror:8
+  }
+  return fmaxf(x, __int_as_float(y));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = dpp_max(x, 0xB1);
+  x = dpp_max(x, 0x4E);
+  x = dpp_max(x, 0x124);
+  x = dpp_max(x, 0x128);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // One wavefront per token, 4 tokens per 256-thread workgroup.
@@ -225,26 +247,30 @@ router_topk_kernel(const float* __restrict__ part, int splits, const float* __re
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together; no block-wide barrier below
 
+  // partial sums added in split order. The loads of 8 splits for every logit of the lane are all
+  // issued before the first add, so a token costs ceil(splits / 8) memory round trips.
   float v[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) v[j] = 0.f;
+  for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+    float q[NJ][8];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        q[j][u] = (e < E && sp0 + u < splits) ? part[((int64_t)(sp0 + u) * T + t) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (sp0 + u < splits) v[j] += q[j][u];
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
-    if (e < E) {
-      // partial sums added in split order; loads issued 8 at a time
-      float s = 0.f;
-      for (int sp0 = 0; sp0 < splits; sp0 += 8) {
-        float q[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) q[u] = sp0 + u < splits ? part[((int64_t)(sp0 + u) * T + t) * E + e] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (sp0 + u < splits) s += q[u];
-      }
-      if (bias) s += bias[e];
-      v[j] = s;
-    } else {
-      v[j] = -INFINITY;
-    }
+    v[j] = e < E ? (bias ? v[j] + bias[e] : v[j]) : -INFINITY;
   }
 
   const int rounds = k < E ? k + 1 : k;
@@ -256,30 +282,24 @@ router_topk_kernel(const float* __restrict__ part, int splits, const float* __re
     sel_v[r] = -INFINITY;
     sel_i[r] = 0x7fffffff;
   }
+  // Round r takes the largest logit not yet taken, ties to the lower expert index: the wave
+  // maximum of the lanes' untaken logits, then the lowest index holding it (ballots in index order).
 #pragma unroll
   for (int r = 0; r < 17; ++r) {
     if (r < rounds) {
-      float bv = -INFINITY;
+      float lv = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (lane + 64 * j < E && !((taken >> j) & 1u)) lv = fmaxf(lv, v[j]);
+      const float mv = wave_max(lv);
       int bi = 0x7fffffff;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int e = lane + 64 * j;
-        if (e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) {
-          bv = v[j];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
+        const unsigned long long b = __ballot(lane + 64 * j < E && !((taken >> j) & 1u) && v[j] == mv);
+        if (bi == 0x7fffffff && b != 0ull) bi = 64 * j + (__ffsll(b) - 1);
       }
       if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      sel_v[r] = bv;
+      sel_v[r] = mv;
       sel_i[r] = bi;
     }
   }

@@ -106,6 +106,40 @@ def test_zero_tokens_is_a_no_op(torch):
 
 
 # --------------------------------------------------------------------------------------------
+# dispatch alone, on skewed indices with out-of-range entries; several 256-token chunks and a
+# ragged tail
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("E", [300, 700])
+def test_permute_skewed_with_invalid_indices(torch, E):
+    import sparse_mixture_experts_softmax_amd as moe
+    T, k = 2500, 5
+    rng = np.random.default_rng(E)
+    # k distinct experts per token (as top-k selection gives), drawn with Zipf(1.2) weights
+    p = 1.0 / np.arange(1, E + 1) ** 1.2
+    p /= p.sum()
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    bad = rng.random((T, k))
+    idx[bad < 0.01] = -1
+    idx[(bad >= 0.01) & (bad < 0.02)] = E
+    dims = moe.MoeDims(T, 64, E, k, 64, 0, syn.BF16, 1)
+    d_idx = torch.from_numpy(idx).to("cuda")
+    offs, sorted_token, slot_of = moe.moe_permute(dims, d_idx)
+    torch.cuda.synchronize()
+
+    flat_e = idx.reshape(-1).astype(np.int64)
+    flat_t = np.repeat(np.arange(T), k)
+    valid = (flat_e >= 0) & (flat_e < E)
+    order = np.lexsort((flat_t[valid], flat_e[valid]))  # expert major, token ascending
+    counts = np.bincount(flat_e[valid], minlength=E)
+    n = int(valid.sum())
+    exp_slot = np.full(T * k, -1, np.int64)
+    exp_slot[np.flatnonzero(valid)[order]] = np.arange(n)
+    assert np.array_equal(to_host(offs), np.concatenate([[0], np.cumsum(counts)]))
+    assert np.array_equal(to_host(sorted_token)[:n], flat_t[valid][order])
+    assert np.array_equal(to_host(slot_of), exp_slot)
+
+
+# --------------------------------------------------------------------------------------------
 # the four step entry points compose to moe_forward, bit for bit; permute is a stable sort
 # --------------------------------------------------------------------------------------------
 def test_steps_compose_and_permute_is_stable_sort(torch):
