@@ -145,17 +145,75 @@ def calibrate():
     print(json.dumps(out), flush=True)
 
 
+SWEEP_T = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]
+
+
+def sweep(steps, warmup):
+    """Token-count sweep at the large layer shape (d=8192, E=512, k=10, I=I_shared=2048, bf16):
+    one JSON line per T with the layer's tokens/s and its fraction of HBM peak over the bytes the
+    routing of that input requires (touched experts, shared expert, router weight, x and out)."""
+    import torch
+
+    import sparse_mixture_experts_softmax_amd as moe
+    import synthetic as syn
+    from sparse_mixture_experts_softmax_amd import workload as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.load_library()
+    big = syn.CONFIGS["decode"].with_(name="sweep", T=max(SWEEP_T))
+    print("bench: sweep %s at T in %s" % (big, SWEEP_T), file=sys.stderr, flush=True)
+    inp = syn.device_inputs(big, device=dev)  # token t's row does not depend on T
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    hip = HipEvents()
+    for T in SWEEP_T:
+        cfg = big.with_(T=T)
+        x = inp["x"][:T]
+        dims = moe.dims_for(x, inp["w_router"], inp["wg"], inp["wg_s"], cfg.k, bool(cfg.renorm))
+        ws = moe.workspace(dims, dev)
+        out = torch.empty_like(x)
+
+        def step():
+            moe.moe_forward(x, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"], inp["wu_s"],
+                            inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm), router_bias=None, ws=ws, out=out,
+                            dims=dims)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        a, b = hip.create(), hip.create()
+        hip.record(a, stream)
+        for _ in range(steps):
+            step()
+        hip.record(b, stream)
+        ms = hip.ms(a, b) / steps
+        hip.destroy(a)
+        hip.destroy(b)
+        _, idx, _, _ = moe.moe_forward(x, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"], inp["wu_s"],
+                                       inp["wd_s"], cfg.k, renormalize=True, return_routing=True, ws=ws, dims=dims)
+        torch.cuda.synchronize()
+        touched = wl.touched_experts(idx.cpu().numpy(), cfg.E)
+        nbytes = wl.algorithmic_bytes(T, cfg.d, cfg.E, cfg.I, cfg.Is, cfg.dtype, touched)
+        print(json.dumps({"T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "touched_experts": touched,
+                          "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / wl.HBM_PEAK_BPS,
+                          "config": {"workload": "sweep", "d": cfg.d, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                                     "I_shared": cfg.Is, "dtype": "bf16"}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mid", choices=["tiny", "mid", "decode", "prefill", "skew"])
+    ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count T")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy, the reference kernel for HBM byte counters")
     ap.add_argument("--calibrate", action="store_true",
                     help="only measure reference points (vendor bf16 GEMM, device copy) and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the token-count sweep T = 1 .. 512 at the large layer shape, one line per T")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -167,6 +225,9 @@ def main():
     if args.calibrate:
         calibrate()
         return
+    if args.sweep:
+        sweep(args.steps, args.warmup)
+        return
 
     import torch
 
@@ -175,6 +236,8 @@ def main():
     from sparse_mixture_experts_softmax_amd import workload as wl
 
     cfg = syn.CONFIGS[args.workload]
+    if args.tokens is not None:
+        cfg = cfg.with_(T=args.tokens)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = moe.load_library()
@@ -244,7 +307,7 @@ def main():
                 "peak": peak_flops / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_for(cfg.name)
-    roof["kernel"] = "ffn_mfma_stream_kernel<true, 1> (gate/up)" if cfg.dtype == syn.BF16 else "ffn_f32_kernel<true>"
+    roof["kernel"] = "ffn_mfma_stream_kernel<true, ...> (gate/up)" if cfg.dtype == syn.BF16 else "ffn_f32_kernel<true>"
     roof["kernel_ms"] = kern_avg_ms
     roof["algorithmic_bytes"] = kb
     roof["algorithmic_flops"] = kf

@@ -61,10 +61,12 @@ __device__ __forceinline__ Group group_info(int g, const int32_t* offsets, int64
 // ------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024)
 build_tiles_kernel(const int32_t* __restrict__ offsets, int64_t T, int E, int has_shared, int BM,
-                   int32_t* __restrict__ tile_group, int32_t* __restrict__ tile_m0, int32_t* __restrict__ tile_count) {
+                   int32_t* __restrict__ tile_group, int32_t* __restrict__ tile_m0, int32_t* __restrict__ tile_count,
+                   int32_t* __restrict__ split_cnt, int64_t n_cnt) {
   __shared__ int s_val[2048];
   __shared__ int s_tmp[1024];
   const int tid = threadIdx.x;
+  for (int64_t i = tid; i < n_cnt; i += 1024) split_cnt[i] = 0;  // split-K arrival counters
   const int G = E + has_shared;
   for (int g = tid; g < G; g += 1024) {
     const int64_t n = g < E ? (int64_t)(offsets[g + 1] - offsets[g]) : T;
@@ -121,6 +123,12 @@ struct MfmaArgs {
   int64_t T;
   int d, E, k, I, Is, ldh;
   int n_ntiles;
+  // split-K (streaming kernel): splits > 1 -> fp32 partial rows part[split][row][part_ld] and
+  // one arrival counter per tile
+  int splits;
+  float* part;
+  int64_t part_ld, part_sstride;
+  int32_t* cnt;
 };
 
 // Transpose a 4(K) x 8(N) block of bf16 (rows r[0..3], each 8 N-consecutive
@@ -331,9 +339,12 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
   const int wm = wave / WN;
   const int wn = wave % WN;
 
-  // logical tile -> (group, column tile, row tile)
-  const int L = xcd_remap(blockIdx.x, *p.tile_count * p.n_ntiles);
-  if (L < 0) return;
+  // logical work item -> (tile, K split); tile -> (group, column tile, row tile)
+  const int nsp = p.splits;
+  const int LS = xcd_remap(blockIdx.x, *p.tile_count * p.n_ntiles * nsp);
+  if (LS < 0) return;
+  const int L = LS / nsp;
+  const int split = LS - L * nsp;
   const int probe = L / p.n_ntiles;
   const int g = p.tile_group[probe];
   const int first = probe - p.tile_m0[probe] / SBM;  // the group's first row tile
@@ -371,7 +382,12 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
       src_row = G.row0 + m0 + r;
     a_off[i] = (uint32_t)(src_row * a_pitch) + a_dma_chunk_bytes(lane);
   }
-  const char* a_src = uniform_ptr((const char*)p.a_src);
+  // this split's K steps
+  const int nk_all = K / SBK;
+  const int chunk = (nk_all + nsp - 1) / nsp;
+  const int kt0 = split * chunk;
+  const int nk = min(chunk, nk_all - kt0);  // <= 0: an empty split, partial sums of zero
+  const char* a_src = uniform_ptr((const char*)p.a_src + (int64_t)kt0 * (SBK * 2));
   auto a_base = [=](int kt) { return a_src + kt * (SBK * 2); };
 
   // B: this wave's DMAs fill one 128-column block of the tile; for gate/up, blocks 0 .. WN/2-1
@@ -383,8 +399,8 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
     b_mat = (const char*)(blk < WN / 2 ? W0 : W1) + (int64_t)(n0 + 128 * (blk % (WN / 2))) * 2;
   else
     b_mat = (const char*)W0 + (int64_t)(n0 + 128 * blk) * 2;
-  const char* b0 = uniform_ptr(b_mat + (int64_t)b_dma_row0<WN>(wave, 0) * b_pitch);
   const int64_t b_kstep = (int64_t)SBK * b_pitch;
+  const char* b0 = uniform_ptr(b_mat + (int64_t)b_dma_row0<WN>(wave, 0) * b_pitch + (int64_t)kt0 * b_kstep);
   // the wave's B instructions load consecutive 4-row groups of one block
   auto b_base = [=](int kt, int i) { return b0 + kt * b_kstep + i * 4 * b_pitch; };
   const uint32_t b_off = b_dma_lane_offset(lane, (uint32_t)b_pitch);
@@ -396,12 +412,62 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
 
   f32x16_t acc[2][4];
   zero(acc);
-  mainloop<WN, S>(K / SBK, nl, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+  if (nk > 0) mainloop<WN, S>(nk, nl, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
 
-  // epilogue: 32x32 accumulator -- lane holds column (lane & 31); register r holds row
+  // 32x32 accumulator layout -- lane holds column (lane & 31); register r holds row
   // 8*(r/4) + 4*(lane/32) + (r%4)
   const int col_in = lane & 31;
   const int row_hi = (lane >> 5) * 4;
+
+  if (nsp > 1) {
+    // Split K: every split stores its partial rows; the last to arrive (arrival counter per tile)
+    // adds all partials in split order -- the same order whichever split arrives last -- and runs
+    // the epilogue. The partials are written and read with device-scope (relaxed atomic) accesses,
+    // which stay coherent across the XCDs' L2s; a store wait orders them before the counter.
+    // (A device-scope fence instead would write back and invalidate the whole L2 of the XCD,
+    // throwing away the weight tiles other workgroups are streaming through it.)
+    auto pcol = [&](int j) {
+      return GATED ? (j >> 1) * p.ldh + n0 + wn * 64 + (j & 1) * 32 + col_in : n0 + wn * 128 + j * 32 + col_in;
+    };
+    float* mine = p.part + (int64_t)split * p.part_sstride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          if (m0 + row < G.rows)
+            __hip_atomic_store(&mine[(G.row0 + m0 + row) * p.part_ld + pcol(j)], acc[i][j][r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
+    __syncthreads();  // ... and every wave's; every wave is past its mainloop: the LDS stages are free
+    int* last = (int*)smem;
+    if (tid == 0)
+      *last = __hip_atomic_fetch_add(&p.cnt[L], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsp - 1;
+    __syncthreads();
+    if (!*last) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          if (m0 + row < G.rows) {
+            const int64_t at = (G.row0 + m0 + row) * p.part_ld + pcol(j);
+            float v = 0.f;
+            for (int sp = 0; sp < nsp; ++sp)
+              v += sp == split ? acc[i][j][r]
+                               : __hip_atomic_load(&p.part[sp * p.part_sstride + at], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            acc[i][j][r] = v;
+          }
+        }
+  }
+
+  // epilogue
   if (GATED) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -429,6 +495,14 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
         }
       }
   }
+}
+
+// K splits for a product whose row x column tiles are expected to number `tiles`: double while
+// the grid would not cover two workgroups per CU and every split keeps >= 16 K steps.
+int pick_splits(int64_t tiles, int nk_min) {
+  int s = 1;
+  while (s < 8 && tiles * s < 512 && nk_min / (2 * s) >= 16) s *= 2;
+  return s;
 }
 
 // wn: wave columns of the streaming tile (2: 128 x 256, 4: 128 x 512)
@@ -559,6 +633,41 @@ ffn_f32_kernel(F32Args p) {
 
 }  // namespace
 
+FfnPlan ffn_plan(const moe_dims& dm) {
+  FfnPlan P;
+  const int has_shared = dm.I_shared > 0 ? 1 : 0;
+  const int64_t Tk = dm.T * dm.k;
+  const int64_t rows_total = Tk + (has_shared ? dm.T : 0);
+  const int ldh = dm.I > dm.I_shared ? dm.I : dm.I_shared;
+  // the streaming kernel needs whole tiles along N and whole 32-wide K steps
+  // (and 32-bit byte offsets for the gathered rows of x and of H)
+  P.stream = dm.dtype == MOE_BF16 && dm.d % 256 == 0 && dm.I % 128 == 0 && dm.I_shared % 128 == 0 &&
+             (uint64_t)dm.T * dm.d * 2 < (1ull << 32) && (uint64_t)rows_total * ldh * 2 < (1ull << 32);
+  // 128 x 512 streaming tiles (one workgroup per CU) for long K loops, where the shape divides
+  // them: the gate/up product at d >= 4096, the down product at I >= 2048 with at least 64 rows per
+  // expert on average. Short K loops (and the near-empty row tiles of decode) run faster on
+  // 128 x 256 tiles, two workgroups per CU, whose prologues and epilogues overlap.
+  const double rows_per_expert = (double)Tk / dm.E;
+  P.wn1 = P.stream && dm.I % 256 == 0 && dm.I_shared % 256 == 0 && dm.d >= 4096 ? 4 : 2;
+  P.wn2 = P.stream && dm.d % 512 == 0 && dm.I >= 2048 && rows_per_expert >= 64.0 ? 4 : 2;
+  const int tn1 = P.stream ? 64 * P.wn1 : kMfmaBN1;
+  const int tn2 = P.stream ? 128 * P.wn2 : kMfmaBN2;
+  P.nt1 = (ldh + tn1 - 1) / tn1;
+  P.nt2 = (dm.d + tn2 - 1) / tn2;
+  // Split the gate/up product's K when its tiles alone would leave CUs idle (few tokens: each
+  // touched expert is one row tile). Expected row tiles: one per group that can be touched, plus
+  // the full ones. The down product has 4x the column tiles and measured no faster split.
+  P.s1 = P.s2 = 1;
+  if (P.stream) {
+    const int64_t groups = (Tk < dm.E ? Tk : dm.E) + has_shared;
+    const int64_t mt = groups + rows_total / kMfmaBM;
+    P.s1 = pick_splits(mt * P.nt1, dm.d / 32);
+  }
+  P.part_cols1 = 2 * (int64_t)ldh;
+  P.part_cols2 = dm.d;
+  return P;
+}
+
 hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
                               const int32_t* sorted_token, const void* wg, const void* wu, const void* wd,
                               const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
@@ -569,25 +678,19 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
   int32_t* tm = (int32_t*)(ws + L.tile_m0);
   int32_t* tc = (int32_t*)(ws + L.tile_count);
   const int has_shared = dm.I_shared > 0 ? 1 : 0;
-  // the streaming kernel needs whole tiles along N and whole 32-wide K steps
-  // (and 32-bit byte offsets for the gathered rows of x and of H)
-  const bool stream_ok = dm.dtype == MOE_BF16 && dm.d % 256 == 0 && dm.I % 128 == 0 && dm.I_shared % 128 == 0 &&
-                         (uint64_t)dm.T * dm.d * 2 < (1ull << 32) &&
-                         (uint64_t)L.rows_total * L.ldh * 2 < (1ull << 32);
-  // 128 x 512 streaming tiles (one workgroup per CU) for long K loops, where the shape divides
-  // them: the gate/up product at d >= 4096, the down product at I >= 2048 with at least 64 rows per
-  // expert on average. Short K loops (and the near-empty row tiles of decode) run faster on
-  // 128 x 256 tiles, two workgroups per CU, whose prologues and epilogues overlap.
-  const double rows_per_expert = (double)dm.T * dm.k / dm.E;
-  const int wn1 = stream_ok && dm.I % 256 == 0 && dm.I_shared % 256 == 0 && dm.d >= 4096 ? 4 : 2;
-  const int wn2 = stream_ok && dm.d % 512 == 0 && dm.I >= 2048 && rows_per_expert >= 64.0 ? 4 : 2;
+  const FfnPlan P = ffn_plan(dm);
+  const bool stream_ok = P.stream;
   const int bm = dm.dtype == MOE_F32 ? kF32BM : kMfmaBM;
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, dm.T, dm.E, has_shared, bm, tg, tm, tc);
+  int32_t* cnt = (int32_t*)(ws + L.ffn_cnt);
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, dm.T, dm.E, has_shared, bm, tg, tm, tc,
+                     cnt, 2 * L.ffn_cnt_each);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // upper bound on row tiles: sum over groups of ceil(n_g / bm) <= (T*k)/bm + E + T/bm + 1
-  const int64_t max_mt = (dm.T * dm.k) / bm + dm.E + (has_shared ? dm.T / bm + 1 : 0);
+  // upper bound on row tiles: sum over non-empty groups of ceil(n_g / bm) <= (T*k)/bm + (routed
+  // groups with rows, at most min(E, T*k)) + T/bm + 1 for the shared expert
+  const int64_t Tk = dm.T * dm.k;
+  const int64_t max_mt = Tk / bm + (Tk < dm.E ? Tk : dm.E) + (has_shared ? dm.T / bm + 1 : 0);
   const int nmax = dm.I > dm.I_shared ? dm.I : dm.I_shared;
   char* H = ws + L.H;
 
@@ -605,6 +708,8 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.I = dm.I;
     a.Is = dm.I_shared;
     a.ldh = L.ldh;
+    a.part = (float*)(ws + L.ffn_part);
+    a.part_sstride = 0;
     // ffn1: gate/up
     a.a_src = (const bf16_t*)x;
     a.w0 = (const bf16_t*)wg;
@@ -612,11 +717,14 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.w0_s = (const bf16_t*)wg_s;
     a.w1_s = (const bf16_t*)wu_s;
     a.out = (bf16_t*)H;
-    const int tn1 = stream_ok ? 64 * wn1 : kMfmaBN1;
-    a.n_ntiles = (nmax + tn1 - 1) / tn1;
+    a.n_ntiles = P.nt1;
+    a.splits = P.s1;
+    a.part_ld = P.part_cols1;
+    a.part_sstride = L.rows_total * P.part_cols1;
+    a.cnt = cnt;
     if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
     if (stream_ok)
-      launch_stream<true>(wn1, (unsigned)(max_mt * a.n_ntiles), s, a);
+      launch_stream<true>(P.wn1, (unsigned)(max_mt * a.n_ntiles * a.splits), s, a);
     else
       hipLaunchKernelGGL(ffn_mfma_kernel<true>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -628,11 +736,14 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.w0_s = (const bf16_t*)wd_s;
     a.w1_s = nullptr;
     a.out = (bf16_t*)y;
-    const int tn2 = stream_ok ? 128 * wn2 : kMfmaBN2;
-    a.n_ntiles = (dm.d + tn2 - 1) / tn2;
+    a.n_ntiles = P.nt2;
+    a.splits = P.s2;
+    a.part_ld = P.part_cols2;
+    a.part_sstride = L.rows_total * P.part_cols2;
+    a.cnt = cnt + L.ffn_cnt_each;
     if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
     if (stream_ok)
-      launch_stream<false>(wn2, (unsigned)(max_mt * a.n_ntiles), s, a);
+      launch_stream<false>(P.wn2, (unsigned)(max_mt * a.n_ntiles * a.splits), s, a);
     else
       hipLaunchKernelGGL(ffn_mfma_kernel<false>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -7,6 +7,8 @@
 
 #include <string>
 
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -135,6 +137,13 @@ Layout make_layout(const moe_dims& dm) {
   L.tile_count = take(4);
   L.H = take((size_t)L.rows_total * L.ldh * esz);
   L.Y = take((size_t)L.rows_total * dm.d * esz);
+  const FfnPlan P = ffn_plan(dm);
+  size_t part = 0;
+  if (P.s1 > 1) part = (size_t)P.s1 * L.rows_total * P.part_cols1 * 4;
+  if (P.s2 > 1) part = std::max(part, (size_t)P.s2 * L.rows_total * P.part_cols2 * 4);
+  L.ffn_part = take(part);
+  L.ffn_cnt_each = (P.s1 > 1 || P.s2 > 1) ? L.max_tiles * std::max(P.nt1, P.nt2) : 0;
+  L.ffn_cnt = take((size_t)2 * L.ffn_cnt_each * 4);
   L.total = off;
   return L;
 }

@@ -58,10 +58,24 @@ struct Layout {
   int64_t rows_total;   // T*k + (I_shared ? T : 0)
   size_t router_planes, logits, topk_idx, topk_w, topk_gap, chunk_counts, offsets, sorted_token, slot_of;
   size_t tile_group, tile_m0, tile_count, H, Y;
+  size_t ffn_part;      // split-K partial sums of the grouped GEMMs (small T only)
+  size_t ffn_cnt;       // split-K arrival counters: gate/up tiles, then down tiles
+  int64_t ffn_cnt_each; // counters per product
   size_t total;
 };
 
 Layout make_layout(const moe_dims& dm);
+
+// How the bf16 grouped GEMMs run for these dims: streaming kernel or not, tile widths (wave
+// columns), column tiles and K splits of the gate/up and of the down product.
+struct FfnPlan {
+  bool stream;
+  int wn1, wn2;
+  int nt1, nt2;
+  int s1, s2;
+  int64_t part_cols1, part_cols2;  // columns of the fp32 partial rows (gate | up, or d)
+};
+FfnPlan ffn_plan(const moe_dims& dm);
 
 // ------------------------------------------------------------------------------------------
 // optional event pair around one kernel (moe_profile_next_forward)

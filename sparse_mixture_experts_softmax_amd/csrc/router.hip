@@ -210,6 +210,86 @@ router_logits_kernel(const XT* __restrict__ x, const float* __restrict__ wr, flo
   }
 }
 
+// Few tokens (T <= 64): one workgroup per (64 experts, K split) streams its weight rows with all
+// of a pass's loads (64 per thread) in flight before the first multiply, the pass's x rows staged
+// in LDS. Wavefront q takes rows 16i + 4q .. +4 of each 256-row pass; the four wavefronts' sums
+// are added in order q = 0..3 at the end. Writes the same per-split partial logits as
+// router_logits_kernel.
+constexpr int kSmallRows = 256;
+
+template <typename XT, int TT>
+__global__ void __launch_bounds__(256)
+router_small_kernel(const XT* __restrict__ x, const float* __restrict__ wr, float* __restrict__ part, int64_t T,
+                    int d, int E, int kchunk) {
+  __shared__ __attribute__((aligned(16))) float xs[TT * kSmallRows];  // [token][row of the pass]
+  const int tid = threadIdx.x;
+  const int el = tid & 63;
+  const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e = blockIdx.x * 64 + el;
+  const int split = blockIdx.y;
+  const int kbeg = split * kchunk;
+  const int kend = min(d, kbeg + kchunk);
+  float acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+
+  for (int k0 = kbeg; k0 < kend; k0 += kSmallRows) {
+    const int kn = min(kSmallRows, kend - k0);  // a multiple of 8
+    float w[64];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = 16 * i + 4 * q + c;
+        w[4 * i + c] = (r < kn && e < E) ? wr[(int64_t)(k0 + r) * E + e] : 0.f;
+      }
+    __syncthreads();  // the previous pass is done with xs
+    for (int i = tid; i < TT * kSmallRows / 4; i += 256) {
+      const int t = i / (kSmallRows / 4);
+      const int r4 = (i % (kSmallRows / 4)) * 4;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (t < T && r4 < kn) load_x4<XT>(x + (int64_t)t * d + k0 + r4, v);
+      *(float4*)&xs[t * kSmallRows + r4] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * i + 4 * q;
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        const float4 xv = *(const float4*)&xs[t * kSmallRows + r];
+        acc[t] = fmaf(xv.x, w[4 * i], acc[t]);
+        acc[t] = fmaf(xv.y, w[4 * i + 1], acc[t]);
+        acc[t] = fmaf(xv.z, w[4 * i + 2], acc[t]);
+        acc[t] = fmaf(xv.w, w[4 * i + 3], acc[t]);
+      }
+    }
+  }
+
+  __syncthreads();
+  float* red = xs;  // [3][TT][64]
+  if (q > 0)
+#pragma unroll
+    for (int t = 0; t < TT; ++t) red[((q - 1) * TT + t) * 64 + el] = acc[t];
+  __syncthreads();
+  if (q == 0 && e < E)
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+      if (t < T)
+        part[((int64_t)split * T + t) * E + e] =
+            ((acc[t] + red[t * 64 + el]) + red[(TT + t) * 64 + el]) + red[(2 * TT + t) * 64 + el];
+}
+
+template <typename XT>
+void launch_router_small(const XT* x, const float* wr, float* part, int64_t T, int d, int E, int splits, int kchunk,
+                         hipStream_t s) {
+  const dim3 grid((unsigned)((E + 63) / 64), (unsigned)splits);
+  if (T <= 8) hipLaunchKernelGGL((router_small_kernel<XT, 8>), grid, dim3(256), 0, s, x, wr, part, T, d, E, kchunk);
+  else if (T <= 16) hipLaunchKernelGGL((router_small_kernel<XT, 16>), grid, dim3(256), 0, s, x, wr, part, T, d, E, kchunk);
+  else if (T <= 32) hipLaunchKernelGGL((router_small_kernel<XT, 32>), grid, dim3(256), 0, s, x, wr, part, T, d, E, kchunk);
+  else hipLaunchKernelGGL((router_small_kernel<XT, 64>), grid, dim3(256), 0, s, x, wr, part, T, d, E, kchunk);
+}
+
 // Maximum over the 64 lanes of a wavefront, uniform result. Within each row of 16 lanes the
 // maximum spreads by DPP lane moves (swap neighbours, swap pairs, rotate by 4, rotate by 8);
 // the four row maxima are then read as scalars.
@@ -273,67 +353,58 @@ router_topk_kernel(const float* __restrict__ part, int splits, const float* __re
     v[j] = e < E ? (bias ? v[j] + bias[e] : v[j]) : -INFINITY;
   }
 
+  // Round r takes the largest logit not yet taken, ties to the lower expert index: the wave
+  // maximum of the lanes' untaken logits, then the lowest index holding it (ballots in index
+  // order). Lane r keeps round r's pick. The round loop stays rolled: for a handful of tokens
+  // one wavefront walks this code alone, and its length, not its arithmetic, sets the time.
   const int rounds = k < E ? k + 1 : k;
   uint32_t taken = 0;
-  float sel_v[17];
-  int sel_i[17];
+  float my_v = -INFINITY;
+  int my_i = 0x7fffffff;
+#pragma unroll 1
+  for (int r = 0; r < rounds; ++r) {
+    float lv = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 17; ++r) {
-    sel_v[r] = -INFINITY;
-    sel_i[r] = 0x7fffffff;
-  }
-  // Round r takes the largest logit not yet taken, ties to the lower expert index: the wave
-  // maximum of the lanes' untaken logits, then the lowest index holding it (ballots in index order).
+    for (int j = 0; j < NJ; ++j)
+      if (lane + 64 * j < E && !((taken >> j) & 1u)) lv = fmaxf(lv, v[j]);
+    const float mv = wave_max(lv);
+    int bi = 0x7fffffff;
 #pragma unroll
-  for (int r = 0; r < 17; ++r) {
-    if (r < rounds) {
-      float lv = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        if (lane + 64 * j < E && !((taken >> j) & 1u)) lv = fmaxf(lv, v[j]);
-      const float mv = wave_max(lv);
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const unsigned long long b = __ballot(lane + 64 * j < E && !((taken >> j) & 1u) && v[j] == mv);
-        if (bi == 0x7fffffff && b != 0ull) bi = 64 * j + (__ffsll(b) - 1);
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      sel_v[r] = mv;
-      sel_i[r] = bi;
+    for (int j = 0; j < NJ; ++j) {
+      const unsigned long long b = __ballot(lane + 64 * j < E && !((taken >> j) & 1u) && v[j] == mv);
+      if (bi == 0x7fffffff && b != 0ull) bi = 64 * j + (__ffsll(b) - 1);
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == r) {
+      my_v = mv;
+      my_i = bi;
     }
   }
 
-  const float m = sel_v[0];
+  // softmax over all E logits; lanes r < k hold the kept ones
+  const float m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(my_v)));
   float z = 0.f;
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
     if (lane + 64 * j < E) z += expf(v[j] - m);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
-
+  const float p_mine = lane < k ? expf(my_v - m) : 0.f;
   float denom = z;
   if (renorm) {
-    denom = 0.f;
+    denom = p_mine;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (r < k) denom += expf(sel_v[r] - m);
+    for (int off = 32; off >= 1; off >>= 1) denom += __shfl_xor(denom, off, 64);
   }
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r < k) {
-        topk_idx[t * k + r] = sel_i[r];
-        topk_w[t * k + r] = expf(sel_v[r] - m) / denom;
-      }
-    }
-    if (topk_gap) {
-      float g = INFINITY;
-#pragma unroll
-      for (int r = 1; r < 17; ++r)
-        if (r == k && k < E) g = sel_v[r - 1] - sel_v[r];
-      topk_gap[t] = g;
-    }
+  if (lane < k) {
+    topk_idx[t * k + lane] = my_i;
+    topk_w[t * k + lane] = p_mine / denom;
+  }
+  if (topk_gap) {
+    const float g = k < E ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), k - 1)) -
+                                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), k))
+                          : INFINITY;
+    if (lane == 0) topk_gap[t] = g;
   }
 }
 
@@ -363,6 +434,15 @@ hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, con
     hipLaunchKernelGGL(router_mfma_kernel, dim3((unsigned)(tiles * L.router_splits)), dim3(256), 0, s,
                        (const bf16_t*)x, planes, part, dm.T, dm.d, dm.E, L.router_kchunk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else if (dm.T <= 64) {
+    if (dm.dtype == MOE_F32)
+      launch_router_small<float>((const float*)x, w_router, part, dm.T, dm.d, dm.E, L.router_splits,
+                                 L.router_kchunk, s);
+    else
+      launch_router_small<bf16_t>((const bf16_t*)x, w_router, part, dm.T, dm.d, dm.E, L.router_splits,
+                                  L.router_kchunk, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   } else {
   const dim3 grid((unsigned)((dm.E + kRouterTileE - 1) / kRouterTileE),
                   (unsigned)((dm.T + kRouterTileT - 1) / kRouterTileT), (unsigned)L.router_splits);

@@ -83,6 +83,10 @@ SMALL_CASES = [
     # down at I >= 2048 with >= 64 rows per expert
     ("wide_gate_up", 200, 4096, 8, 2, 256, 512, syn.BF16, 1, 0.0),
     ("wide_down", 300, 512, 8, 2, 2048, 0, syn.BF16, 1, 0.0),
+    # few tokens: the gate/up product's K split over workgroups (4 ways; then 8 ways on 128 x 512
+    # tiles with a shared expert narrower than the routed ones)
+    ("split_k_T1", 1, 2048, 64, 4, 1024, 1024, syn.BF16, 1, 0.0),
+    ("split_k_T3", 3, 4096, 32, 6, 512, 256, syn.BF16, 1, 0.0),
 ]
 
 
