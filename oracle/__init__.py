@@ -31,6 +31,8 @@ def _load():
         lib.moe_oracle_forward.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32, p, p, p,
                                            p, p, p, p, p, p, p, p, p, p]
         lib.moe_oracle_forward.restype = ctypes.c_int
+        lib.moe_oracle_rmsnorm.argtypes = [i64, i32, i32, p, p, ctypes.c_double, p]
+        lib.moe_oracle_rmsnorm.restype = ctypes.c_int
         lib.moe_oracle_threads.argtypes = []
         lib.moe_oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -122,6 +124,44 @@ def forward(x, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renorm=True, bias=None
     if rc != 0:
         raise RuntimeError("moe_oracle_forward failed: %d" % rc)
     return out, idx, w, gap
+
+
+RMS_NORM_EPS = 1e-6
+
+
+def rmsnorm(x, gamma, eps=RMS_NORM_EPS):
+    """Zero-centred RMSNorm of each row: x / sqrt(mean(x^2) + eps) * (1 + gamma), in double,
+    rounded once to the element type of x (float32, or bf16 bits by round-to-nearest-even)."""
+    dt = _dtype_of(x)
+    npdt = np.float32 if dt == F32 else np.uint16
+    x = _c(x, npdt)
+    gamma = _c(gamma, npdt)
+    T, d = x.shape
+    assert gamma.shape == (d,)
+    h = np.empty((T, d), npdt)
+    rc = _load().moe_oracle_rmsnorm(T, d, dt, x.ctypes.data, gamma.ctypes.data, float(eps), h.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("moe_oracle_rmsnorm failed: %d" % rc)
+    return h
+
+
+def widen(a):
+    """float32 or bf16-bit array as float64."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def block_forward(x, gamma, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renorm=True, bias=None,
+                  eps=RMS_NORM_EPS):
+    """The MoE block between its neighbours: out = x + MoE(rmsnorm(x)); the router and the
+    experts both see the normalised rows, stored in the element type of x.
+
+    Returns (out float64 [T,d], topk_idx, topk_w, gap, h)."""
+    h = rmsnorm(x, gamma, eps)
+    moe_out, idx, w, gap = forward(h, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renorm=renorm, bias=bias)
+    return widen(x) + moe_out, idx, w, gap, h
 
 
 def threads():

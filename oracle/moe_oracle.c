@@ -8,9 +8,8 @@
  * It is the plain definition, written out token by token, with every sum
  * accumulated in double:
  *
- *   router  ("a small linear network that takes the token's embedding and
- *            produces one score per expert" -- Qwen3.6 MoE explorer page,
- *            section on the MoE router):
+ *   router  (the router maps the token's embedding to one score per expert --
+ *            Qwen3.6 MoE explorer page, section on the MoE router):
  *              l_e = fp32( sum_i x_i * W_r[i, e]  (+ b_e) )
  *   top-k   (same section: a probability for each expert, the K most
  *            probable kept): S = the k largest l_e, ties to the lower index,
@@ -30,6 +29,16 @@
  * Readings where the pages are silent: softmax over all E then top-k (equal
  * to a softmax over the k kept logits when renormalising); selection on the
  * fp32 logits; lower index wins ties; the shared expert is unweighted.
+ *
+ * Around the block (moe_oracle_rmsnorm; the residual add is done by the
+ * caller): zero-centred RMSNorm in front of it -- the Qwen3-Next article names
+ * Zero-Centered RMSNorm, whose parameters start at zero, so the scale is
+ * 1 + gamma; the configuration listing on the Qwen3.8-Max architecture page
+ * gives rms_norm_eps = 1e-6:
+ *              h = x / sqrt(mean_i x_i^2 + eps) * (1 + gamma)
+ * and the layer's output is x + MoE(h). The parameter table of the overview
+ * page counts two norms per layer plus a final one, which places a norm in
+ * front of every MoE block.
  *
  * Element types: x and the expert weights are fp32 (dtype 0) or bf16 bit
  * patterns (dtype 1, widened exactly); the router weight and bias are fp32.
@@ -236,4 +245,43 @@ int moe_oracle_forward(int64_t T, int32_t d, int32_t E, int32_t k, int32_t I, in
 }
 
 /* Threads the parallel regions above use (OpenMP's current maximum). */
+/* v rounded to bf16, round to nearest with ties to even, from the exact double
+ * (not through fp32): significand scaled to [128, 256), rounded by rint in the
+ * default rounding mode, scaled back. Normal range only (|v| >= 2^-126 or 0). */
+static uint16_t round_bf16(double v) {
+  if (v == 0.0) return signbit(v) ? 0x8000u : 0u;
+  int e;
+  const double m = frexp(v, &e); /* v = m 2^e, 0.5 <= |m| < 1 */
+  const double r = ldexp(rint(ldexp(m, 8)), e - 8);
+  const float f = (float)r; /* exact: 8 significant bits */
+  uint32_t bits;
+  memcpy(&bits, &f, sizeof bits);
+  return (uint16_t)(bits >> 16);
+}
+
+/* Zero-centred RMSNorm of each of the T rows of x [T, d] (see the header):
+ *   h = x / sqrt(mean(x^2) + eps) * (1 + gamma), in double,
+ * stored in the element type of x (rounded once: bf16 by round_bf16, fp32 by
+ * the conversion). gamma [d] has the element type of x. */
+int moe_oracle_rmsnorm(int64_t T, int32_t d, int32_t dtype, const void* x, const void* gamma, double eps, void* h) {
+  if (T < 0 || d < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16) || !(eps >= 0.0)) return ORACLE_ERR_ARG;
+  if (T > 0 && (!x || !gamma || !h)) return ORACLE_ERR_ARG;
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int32_t i = 0; i < d; ++i) {
+      const double v = elem(x, dtype, (size_t)t * d + i);
+      ss += v * v;
+    }
+    const double inv = 1.0 / sqrt(ss / d + eps);
+    for (int32_t i = 0; i < d; ++i) {
+      const double v = elem(x, dtype, (size_t)t * d + i) * inv * (1.0 + elem(gamma, dtype, (size_t)i));
+      if (dtype == ORACLE_F32)
+        ((float*)h)[(size_t)t * d + i] = (float)v;
+      else
+        ((uint16_t*)h)[(size_t)t * d + i] = round_bf16(v);
+    }
+  }
+  return ORACLE_OK;
+}
+
 int moe_oracle_threads(void) { return omp_get_max_threads(); }

@@ -301,3 +301,90 @@ def test_per_expert_pointers_allow_missing_unselected_experts():
     missing[0] = wg[0]
     with pytest.raises(RuntimeError):
         oracle.forward(x, wr, missing, missing, missing, wgs, wus, wds, k=cfg.k)
+
+
+# --------------------------------------------------------------------------------------------
+# zero-centred RMSNorm in front of the block, and the residual add around it
+# --------------------------------------------------------------------------------------------
+def bf16_bits_of(v):
+    """bf16 bit pattern of a value that bf16 holds exactly."""
+    b = np.float32(v).view(np.uint32)
+    assert b & 0xFFFF == 0, v
+    return np.uint16(b >> 16)
+
+
+def test_rmsnorm_constant_row_closed_form():
+    # a row of d equal values c: mean(x^2) = c^2, so h = c / sqrt(c^2 + eps) * (1 + gamma). A sum
+    # in place of the mean gives 1/sqrt(d); eps outside the root, or dropped, moves h at small c.
+    d = 64
+    for c, eps in ((0.5, 1e-6), (1e-3, 1e-6), (-2.0, 0.0), (3e-4, 1e-6)):
+        x = np.full((1, d), c, np.float32)
+        h = oracle.rmsnorm(x, np.zeros(d, np.float32), eps)
+        cf = float(np.float32(c))
+        expect = cf / math.sqrt(cf * cf + eps)  # in double; the oracle rounds once to fp32
+        assert np.allclose(h.astype(np.float64), expect, rtol=2 ** -23, atol=0), (c, eps, h[0, 0], expect)
+    # c = 1e-3, eps = 1e-6: h = 1/sqrt(2) exactly in the definition
+    h = oracle.rmsnorm(np.full((1, d), 1e-3, np.float64).astype(np.float32), np.zeros(d, np.float32), 1e-6)
+    assert abs(float(h[0, 0]) - 1 / math.sqrt(2)) < 1e-6
+
+
+def test_rmsnorm_scale_is_one_plus_gamma():
+    # gamma = 0 is the identity scale (zero-centred); gamma = -1 zeroes the element; gamma = 1
+    # doubles it. A plain-gamma scale would zero everything at gamma = 0.
+    rng = np.random.default_rng(5)
+    d = 48
+    x = rng.standard_normal((3, d)).astype(np.float32)
+    base = oracle.rmsnorm(x, np.zeros(d, np.float32), 1e-6).astype(np.float64)
+    gamma = np.zeros(d, np.float32)
+    gamma[::3] = -1.0
+    gamma[1::3] = 1.0
+    h = oracle.rmsnorm(x, gamma, 1e-6).astype(np.float64)
+    assert np.all(h[:, ::3] == 0.0)
+    assert np.allclose(h[:, 1::3], 2 * base[:, 1::3], rtol=2 ** -23, atol=0)
+    assert np.array_equal(h[:, 2::3], base[:, 2::3])
+    # rows have unit mean square before the scale (eps small against it)
+    assert np.allclose((base ** 2).mean(axis=1), 1.0, rtol=1e-5)
+
+
+def test_rmsnorm_scale_invariance_without_eps():
+    # with eps = 0 the norm is invariant to scaling a row by a power of two (exact in fp32)
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((4, 40)).astype(np.float32)
+    g = (rng.standard_normal(40) * 0.1).astype(np.float32)
+    assert np.array_equal(oracle.rmsnorm(x, g, 0.0), oracle.rmsnorm(x * np.float32(8.0), g, 0.0))
+
+
+def test_rmsnorm_bf16_rounds_to_nearest_even():
+    # rows of ones (h = 1 + gamma exactly with eps = 0): gamma = 2^-8 puts h halfway between bf16
+    # 1.0 and 1.0078125 (ties to the even 1.0); 3 * 2^-8 is halfway between 1.0078125 and
+    # 1.015625 (ties to the even 1.015625); 2^-8 + 2^-12 is above halfway (rounds up).
+    # Truncation or round-half-up fails one of them.
+    gam = [2 ** -8, 3 * 2 ** -8, 2 ** -8 + 2 ** -12, -(2 ** -9)]
+    want = [1.0, 1.015625, 1.0078125, 1.0]  # 1 - 2^-9 is halfway below 1.0 (bf16 step 2^-8 there)
+    d = len(gam)
+    x = np.full((1, d), bf16_bits_of(1.0), np.uint16)
+    g = np.array([bf16_bits_of(v) for v in gam], np.uint16)
+    h = oracle.rmsnorm(x, g, 0.0)
+    assert [int(b) for b in h[0]] == [int(bf16_bits_of(v)) for v in want]
+
+
+def test_block_forward_zero_experts_is_the_residual_and_composes():
+    # with every expert (and the shared one) zero, the block passes x through unchanged; in
+    # general it is x plus the block applied to the normalised rows
+    rng = np.random.default_rng(8)
+    T, d, E, k, I, Is = 5, 32, 6, 2, 16, 8
+    x, wr, wg, wu, wd, wgs, wus, wds = rand_layer(rng, T, d, E, I, Is)
+    gamma = (rng.standard_normal(d) * 0.1).astype(np.float32)
+    z = np.zeros_like
+    out, idx, _, _, h = oracle.block_forward(x, gamma, wr, z(wg), z(wu), z(wd), z(wgs), z(wus), z(wds), k)
+    assert np.array_equal(out, x.astype(np.float64))
+    out, idx, w, gap, h = oracle.block_forward(x, gamma, wr, wg, wu, wd, wgs, wus, wds, k)
+    ref = x.astype(np.float64)
+    hh = h.astype(np.float64)
+    for t in range(T):
+        acc = dense_swiglu(hh[t:t + 1], wgs, wus, wds)[0]
+        for j in range(k):
+            e = idx[t, j]
+            acc = acc + w[t, j] * dense_swiglu(hh[t:t + 1], wg[e], wu[e], wd[e])[0]
+        ref[t] += acc
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-12)
