@@ -207,6 +207,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mid", choices=["tiny", "mid", "decode", "prefill", "skew"])
     ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count T")
+    ap.add_argument("--block", action="store_true",
+                    help="time the block between its neighbours: zero-centred RMSNorm in front, residual add after")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy, the reference kernel for HBM byte counters")
@@ -248,9 +250,17 @@ def main():
     ws = moe.workspace(dims, dev)
     out = torch.empty_like(x)
 
+    gamma = syn.device_gamma(cfg, device=dev) if args.block else None
+
     def step():
-        moe.moe_forward(x, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"], inp["wu_s"], inp["wd_s"],
-                        cfg.k, renormalize=bool(cfg.renorm), router_bias=inp["bias"], ws=ws, out=out, dims=dims)
+        if args.block:
+            moe.moe_forward_block(x, gamma, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"],
+                                  inp["wu_s"], inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm),
+                                  router_bias=inp["bias"], ws=ws, out=out, dims=dims)
+        else:
+            moe.moe_forward(x, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"], inp["wu_s"],
+                            inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm), router_bias=inp["bias"], ws=ws, out=out,
+                            dims=dims)
 
     stream = torch.cuda.current_stream(dev).cuda_stream
     hip = HipEvents()
@@ -280,9 +290,14 @@ def main():
         hip.destroy(b)
 
     # routing of this input, for the algorithmic work actually required
-    _, idx, _, _ = moe.moe_forward(x, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"], inp["wu_s"],
-                                   inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm), router_bias=inp["bias"],
-                                   return_routing=True, ws=ws, dims=dims)
+    if args.block:
+        _, idx, _, _ = moe.moe_forward_block(x, gamma, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"],
+                                             inp["wu_s"], inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm),
+                                             router_bias=inp["bias"], return_routing=True, ws=ws, dims=dims)
+    else:
+        _, idx, _, _ = moe.moe_forward(x, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"],
+                                       inp["wu_s"], inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm),
+                                       router_bias=inp["bias"], return_routing=True, ws=ws, dims=dims)
     torch.cuda.synchronize()
     touched = wl.touched_experts(idx.cpu().numpy(), cfg.E)
 
@@ -328,9 +343,10 @@ def main():
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if cfg.dtype == syn.BF16 else "f32", "data": "synthetic",
-        "config": {"workload": "%s MoE layer: T=%d, d=%d, E=%d, k=%d, I=%d, shared I=%d, %s, fp32 router%s"
+        "config": {"workload": "%s MoE layer: T=%d, d=%d, E=%d, k=%d, I=%d, shared I=%d, %s, fp32 router%s%s"
                    % (cfg.name, cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.Is, cfg.dtype_name,
-                      ", Zipf(%.1f) router bias" % cfg.zipf_alpha if cfg.zipf_alpha else ""),
+                      ", Zipf(%.1f) router bias" % cfg.zipf_alpha if cfg.zipf_alpha else "",
+                      ", RMSNorm in front and residual add" if args.block else ""),
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "I": cfg.I, "I_shared": cfg.Is,
                    "renormalize": cfg.renorm, "seed": cfg.seed},
         "roofline": roof, "layer": layer, "cpu_baseline": cpu, "wall_s_timed": wall,

@@ -136,6 +136,33 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_route
                        const void* wd_s, void* out, int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws,
                        size_t ws_bytes, hipStream_t stream);
 
+/* Steps either side of the block: zero-centred RMSNorm in front of it (the Qwen3-Next
+ * article: Zero-Centered RMSNorm, parameters starting at zero, so the scale is 1 + gamma;
+ * the Qwen3.8-Max architecture page's configuration listing: rms_norm_eps = 1e-6) and the
+ * residual add after it (the overview page's parameter table counts two norms per layer
+ * plus a final one, a norm in front of each MoE block).
+ *
+ * moe_rmsnorm:  h[t] = x[t] / sqrt(mean_i x[t,i]^2 + eps) * (1 + gamma)
+ *   x, h [T, d] dtype; gamma [d] dtype; eps finite and >= 0. Computed in fp64 and rounded
+ *   once to dtype (to nearest, ties to even). h may not alias x. */
+moe_status moe_rmsnorm(const moe_dims* dims, const void* x, const void* gamma, double eps, void* h,
+                       hipStream_t stream);
+
+/* moe_combine with the residual row added last:
+ *   out[t] = sum_j topk_w[t, j] y[slot_of[t*k + j]] + y[T*k + t] + residual[t]
+ * residual [T, d] dtype (the block's input). */
+moe_status moe_combine_residual(const moe_dims* dims, const void* y, const int32_t* slot_of, const float* topk_w,
+                                const void* residual, void* out, hipStream_t stream);
+
+/* The block between its neighbours: out = x + MoE(moe_rmsnorm(x)); the router and the experts
+ * see the normalised rows (kept in the workspace). Arguments as moe_forward, plus gamma [d] and
+ * eps as for moe_rmsnorm. out may not alias x. */
+moe_status moe_forward_block(const moe_dims* dims, const void* x, const void* gamma, double eps,
+                             const float* w_router, const float* router_bias, const void* wg, const void* wu,
+                             const void* wd, const void* wg_s, const void* wu_s, const void* wd_s, void* out,
+                             int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* Instrumentation for timing one kernel of the path while the whole path runs.
  * The next moe_forward call made by the calling thread records `start` on its
  * stream immediately before launching the selected kernel and `stop` right

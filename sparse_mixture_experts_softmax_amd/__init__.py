@@ -60,6 +60,13 @@ def load_library(path=None):
     lib.moe_combine.restype = st
     lib.moe_forward.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.moe_forward.restype = st
+    lib.moe_rmsnorm.argtypes = [D, _P, _P, ctypes.c_double, _P, _P]
+    lib.moe_rmsnorm.restype = st
+    lib.moe_combine_residual.argtypes = [D, _P, _P, _P, _P, _P, _P]
+    lib.moe_combine_residual.restype = st
+    lib.moe_forward_block.argtypes = [D, _P, _P, ctypes.c_double, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, ctypes.c_size_t, _P]
+    lib.moe_forward_block.restype = st
     lib.moe_profile_next_forward.argtypes = [ctypes.c_int32, _P, _P]
     lib.moe_profile_next_forward.restype = st
     lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -179,6 +186,50 @@ def moe_forward(x, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renormalize=True, 
     _check(lib.moe_forward(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(wg), _ptr(wu),
                            _ptr(wd), _ptr(wg_s), _ptr(wu_s), _ptr(wd_s), _ptr(out), _ptr(idx), _ptr(w), _ptr(gap),
                            _ptr(ws), ws.numel(), _stream(x)))
+    if return_routing:
+        return out, idx, w, gap
+    return out
+
+
+RMS_NORM_EPS = 1e-6
+
+
+def moe_rmsnorm(dims, x, gamma, eps=RMS_NORM_EPS, h=None):
+    """Zero-centred RMSNorm of the rows of x: returns h [T, d] in x's dtype."""
+    import torch
+    lib = load_library()
+    h = torch.empty_like(x) if h is None else h
+    _check(lib.moe_rmsnorm(ctypes.byref(dims), _ptr(x), _ptr(gamma), float(eps), _ptr(h), _stream(x)))
+    return h
+
+
+def moe_combine_residual(dims, y, slot_of, topk_w, residual, out=None):
+    """moe_combine plus the residual rows; returns out [T, d] in y's dtype."""
+    import torch
+    lib = load_library()
+    out = torch.empty(dims.T, dims.d, dtype=y.dtype, device=y.device) if out is None else out
+    _check(lib.moe_combine_residual(ctypes.byref(dims), _ptr(y), _ptr(slot_of), _ptr(topk_w), _ptr(residual),
+                                    _ptr(out), _stream(y)))
+    return out
+
+
+def moe_forward_block(x, gamma, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renormalize=True, router_bias=None,
+                      eps=RMS_NORM_EPS, return_routing=False, ws=None, out=None, dims=None):
+    """out = x + MoE(rmsnorm(x)). Returns out [T, d], or (out, topk_idx, topk_w, topk_gap) with
+    return_routing."""
+    import torch
+    lib = load_library()
+    dims = dims_for(x, w_router, wg, wg_s, k, renormalize) if dims is None else dims
+    ws = workspace(dims, x.device) if ws is None else ws
+    out = torch.empty_like(x) if out is None else out
+    idx = w = gap = None
+    if return_routing:
+        idx = torch.empty(dims.T, dims.k, dtype=torch.int32, device=x.device)
+        w = torch.empty(dims.T, dims.k, dtype=torch.float32, device=x.device)
+        gap = torch.empty(dims.T, dtype=torch.float32, device=x.device)
+    _check(lib.moe_forward_block(ctypes.byref(dims), _ptr(x), _ptr(gamma), float(eps), _ptr(w_router),
+                                 _ptr(router_bias), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(wg_s), _ptr(wu_s), _ptr(wd_s),
+                                 _ptr(out), _ptr(idx), _ptr(w), _ptr(gap), _ptr(ws), ws.numel(), _stream(x)))
     if return_routing:
         return out, idx, w, gap
     return out

@@ -3,12 +3,13 @@
 // highest weights process the token) and the always-active shared expert is
 // added with no weight (same section; Qwen3-Next article on hyper.ai).
 //
-//   out[t] = sum_{j<k} w[t,j] * y[slot_of[t*k+j]]  +  y[T*k + t]
+//   out[t] = sum_{j<k} w[t,j] * y[slot_of[t*k+j]]  +  y[T*k + t]  (+ residual[t])
 //
 // One 256-thread workgroup per token; each thread owns 8 consecutive hidden
 // elements (16-byte bf16 or 2x16-byte fp32 loads), issues the loads of all k+1
-// rows before the first add, accumulates in fp32 in the fixed order j = 0..k-1
-// then the shared row, and rounds once on store. Pairs with slot_of = -1 (an
+// rows before the first add, accumulates in fp32 in the fixed order j = 0..k-1,
+// the shared row, then the residual row (the block's input, when the caller
+// asks for the residual add), and rounds once on store. Pairs with slot_of = -1 (an
 // expert index outside [0, E) at dispatch) contribute nothing.
 #include "moe_internal.h"
 
@@ -53,7 +54,7 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
 template <typename ET>
 __global__ void __launch_bounds__(256)
 combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, const float* __restrict__ topk_w,
-               ET* __restrict__ out, int64_t T, int d, int k, int has_shared) {
+               const ET* __restrict__ residual, ET* __restrict__ out, int64_t T, int d, int k, int has_shared) {
   __shared__ int s_slot[kMaxK];
   __shared__ float s_w[kMaxK];
   const int64_t t = blockIdx.x;
@@ -66,11 +67,12 @@ combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, co
   typedef typename RawOf<ET>::type Raw;
   for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
     // every row's load is issued before the first add
-    Raw raw[kMaxK + 1];
+    Raw raw[kMaxK + 2];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
       if (j < k && s_slot[j] >= 0) load_raw(y + (int64_t)s_slot[j] * d + c, raw[j]);
     if (has_shared) load_raw(y + shared_row * d + c, raw[kMaxK]);
+    if (residual) load_raw(residual + t * d + c, raw[kMaxK + 1]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
@@ -88,6 +90,12 @@ combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, co
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }
+    if (residual) {
+      float v[8];
+      widen(raw[kMaxK + 1], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
     store8(out + t * d + c, acc);
   }
 }
@@ -95,14 +103,14 @@ combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, co
 }  // namespace
 
 hipError_t launch_combine(const moe_dims& dm, const void* y, const int32_t* slot_of, const float* topk_w,
-                          void* out, hipStream_t s) {
+                          const void* residual, void* out, hipStream_t s) {
   const int hs = dm.I_shared > 0 ? 1 : 0;
   if (dm.dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3((unsigned)dm.T), dim3(256), 0, s, (const bf16_t*)y, slot_of,
-                       topk_w, (bf16_t*)out, dm.T, dm.d, dm.k, hs);
+                       topk_w, (const bf16_t*)residual, (bf16_t*)out, dm.T, dm.d, dm.k, hs);
   else
     hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)dm.T), dim3(256), 0, s, (const float*)y, slot_of, topk_w,
-                       (float*)out, dm.T, dm.d, dm.k, hs);
+                       (const float*)residual, (float*)out, dm.T, dm.d, dm.k, hs);
   return hipGetLastError();
 }
 

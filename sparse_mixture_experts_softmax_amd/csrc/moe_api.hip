@@ -8,6 +8,7 @@
 #include <string>
 
 #include <algorithm>
+#include <cmath>
 
 #include "moe_internal.h"
 
@@ -258,18 +259,80 @@ moe_status moe_combine(const moe_dims* dims, const void* y, const int32_t* slot_
   MOE_TRY(check_ptr(slot_of, 4, "slot_of"));
   MOE_TRY(check_ptr(topk_w, 4, "topk_w"));
   MOE_TRY(check_ptr(out, 16, "out"));
-  hipError_t e = launch_combine(dm, y, slot_of, topk_w, out, stream);
+  hipError_t e = launch_combine(dm, y, slot_of, topk_w, nullptr, out, stream);
   if (e != hipSuccess) return hip_fail(e, "moe_combine");
   return MOE_OK;
 }
 
-moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
-                       const void* wg, const void* wu, const void* wd, const void* wg_s, const void* wu_s,
-                       const void* wd_s, void* out, int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+moe_status moe_combine_residual(const moe_dims* dims, const void* y, const int32_t* slot_of, const float* topk_w,
+                                const void* residual, void* out, hipStream_t stream) {
   MOE_TRY(check_dims(dims));
   const moe_dims& dm = *dims;
   if (dm.T == 0) return MOE_OK;
+  MOE_TRY(check_ptr(y, 16, "y"));
+  MOE_TRY(check_ptr(slot_of, 4, "slot_of"));
+  MOE_TRY(check_ptr(topk_w, 4, "topk_w"));
+  MOE_TRY(check_ptr(residual, 16, "residual"));
+  MOE_TRY(check_ptr(out, 16, "out"));
+  hipError_t e = launch_combine(dm, y, slot_of, topk_w, residual, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_combine_residual");
+  return MOE_OK;
+}
+
+moe_status moe_rmsnorm(const moe_dims* dims, const void* x, const void* gamma, double eps, void* h,
+                       hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& dm = *dims;
+  if (!(eps >= 0.0 && eps < INFINITY)) return fail(MOE_ERR_INVALID_ARG, "eps = %g is not a finite value >= 0", eps);
+  if (dm.T == 0) return MOE_OK;
+  MOE_TRY(check_ptr(x, 16, "x"));
+  MOE_TRY(check_ptr(gamma, 16, "gamma"));
+  MOE_TRY(check_ptr(h, 16, "h"));
+  hipError_t e = launch_rmsnorm(dm, x, gamma, eps, h, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_rmsnorm");
+  return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The block on rows xin (the router and the experts see them); residual, when given, is added in
+// the combine. Pointers validated by the caller.
+moe_status forward_rows(const moe_dims& dm, const Layout& L, const void* xin, const void* residual,
+                        const float* w_router, const float* router_bias, const void* wg, const void* wu,
+                        const void* wd, const void* wg_s, const void* wu_s, const void* wd_s, void* out,
+                        int32_t* topk_idx, float* topk_w, float* topk_gap, char* w, hipStream_t stream) {
+  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(w + L.topk_idx);
+  float* tw = topk_w ? topk_w : (float*)(w + L.topk_w);
+  int32_t* offsets = (int32_t*)(w + L.offsets);
+  int32_t* sorted = (int32_t*)(w + L.sorted_token);
+  int32_t* slot = (int32_t*)(w + L.slot_of);
+  void* y = w + L.Y;
+  const Prof prof = g_prof;
+  g_prof = Prof();
+  hipError_t e;
+  if ((e = prof.begin(MOE_KERNEL_ROUTER, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  e = launch_router(dm, L, xin, w_router, router_bias, idx, tw, topk_gap, w, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/router");
+  if ((e = prof.end(MOE_KERNEL_ROUTER, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  if ((e = prof.begin(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  e = launch_permute(dm, L, idx, offsets, sorted, slot, w, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/permute");
+  if ((e = prof.end(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  e = launch_grouped_ffn(dm, L, xin, offsets, sorted, wg, wu, wd, wg_s, wu_s, wd_s, y, w, stream, &prof);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/grouped_ffn");
+  if ((e = prof.begin(MOE_KERNEL_COMBINE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  e = launch_combine(dm, y, slot, tw, residual, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
+  if ((e = prof.end(MOE_KERNEL_COMBINE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  return MOE_OK;
+}
+
+moe_status check_block_ptrs(const moe_dims& dm, const void* x, const float* w_router, const float* router_bias,
+                            const void* wg, const void* wu, const void* wd, const void* wg_s, const void* wu_s,
+                            const void* wd_s, const void* out, const int32_t* topk_idx, const float* topk_w,
+                            const float* topk_gap) {
   MOE_TRY(check_ptr(x, 16, "x"));
   MOE_TRY(check_ptr(w_router, 4, "w_router"));
   MOE_TRY(check_ptr(router_bias, 4, "router_bias", false));
@@ -284,33 +347,50 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_route
   MOE_TRY(check_ptr(topk_idx, 4, "topk_idx", false));
   MOE_TRY(check_ptr(topk_w, 4, "topk_w", false));
   MOE_TRY(check_ptr(topk_gap, 4, "topk_gap", false));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
+                       const void* wg, const void* wu, const void* wd, const void* wg_s, const void* wu_s,
+                       const void* wd_s, void* out, int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& dm = *dims;
+  if (dm.T == 0) return MOE_OK;
+  MOE_TRY(check_block_ptrs(dm, x, w_router, router_bias, wg, wu, wd, wg_s, wu_s, wd_s, out, topk_idx, topk_w,
+                           topk_gap));
   const Layout L = make_layout(dm);
   MOE_TRY(check_ws(dm, L, ws, ws_bytes));
+  return forward_rows(dm, L, x, nullptr, w_router, router_bias, wg, wu, wd, wg_s, wu_s, wd_s, out, topk_idx, topk_w,
+                      topk_gap, (char*)ws, stream);
+}
+
+moe_status moe_forward_block(const moe_dims* dims, const void* x, const void* gamma, double eps,
+                             const float* w_router, const float* router_bias, const void* wg, const void* wu,
+                             const void* wd, const void* wg_s, const void* wu_s, const void* wd_s, void* out,
+                             int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& dm = *dims;
+  if (!(eps >= 0.0 && eps < INFINITY)) return fail(MOE_ERR_INVALID_ARG, "eps = %g is not a finite value >= 0", eps);
+  if (dm.T == 0) return MOE_OK;
+  MOE_TRY(check_block_ptrs(dm, x, w_router, router_bias, wg, wu, wd, wg_s, wu_s, wd_s, out, topk_idx, topk_w,
+                           topk_gap));
+  MOE_TRY(check_ptr(gamma, 16, "gamma"));
+  const Layout L = make_layout(dm);
+  MOE_TRY(check_ws(dm, L, ws, ws_bytes));
+  // the normalised rows live at the start of the Y buffer: the router and the gate/up product
+  // read them before the down product writes Y
   char* w = (char*)ws;
-  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(w + L.topk_idx);
-  float* tw = topk_w ? topk_w : (float*)(w + L.topk_w);
-  int32_t* offsets = (int32_t*)(w + L.offsets);
-  int32_t* sorted = (int32_t*)(w + L.sorted_token);
-  int32_t* slot = (int32_t*)(w + L.slot_of);
-  void* y = w + L.Y;
-  const Prof prof = g_prof;
-  g_prof = Prof();
-  hipError_t e;
-  if ((e = prof.begin(MOE_KERNEL_ROUTER, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
-  e = launch_router(dm, L, x, w_router, router_bias, idx, tw, topk_gap, w, stream);
-  if (e != hipSuccess) return hip_fail(e, "moe_forward/router");
-  if ((e = prof.end(MOE_KERNEL_ROUTER, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
-  if ((e = prof.begin(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
-  e = launch_permute(dm, L, idx, offsets, sorted, slot, w, stream);
-  if (e != hipSuccess) return hip_fail(e, "moe_forward/permute");
-  if ((e = prof.end(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
-  e = launch_grouped_ffn(dm, L, x, offsets, sorted, wg, wu, wd, wg_s, wu_s, wd_s, y, w, stream, &prof);
-  if (e != hipSuccess) return hip_fail(e, "moe_forward/grouped_ffn");
-  if ((e = prof.begin(MOE_KERNEL_COMBINE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
-  e = launch_combine(dm, y, slot, tw, out, stream);
-  if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
-  if ((e = prof.end(MOE_KERNEL_COMBINE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
-  return MOE_OK;
+  void* h = w + L.Y;
+  hipError_t e = launch_rmsnorm(dm, x, gamma, eps, h, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward_block/rmsnorm");
+  return forward_rows(dm, L, h, x, w_router, router_bias, wg, wu, wd, wg_s, wu_s, wd_s, out, topk_idx, topk_w,
+                      topk_gap, w, stream);
 }
 
 }  // extern "C"

@@ -107,7 +107,10 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
                               const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
                               hipStream_t s, const Prof* prof = nullptr);
 
+// residual: [T, d] added last (nullptr: none)
 hipError_t launch_combine(const moe_dims& dm, const void* y, const int32_t* slot_of, const float* topk_w,
-                          void* out, hipStream_t s);
+                          const void* residual, void* out, hipStream_t s);
+
+hipError_t launch_rmsnorm(const moe_dims& dm, const void* x, const void* gamma, double eps, void* h, hipStream_t s);
 
 }  // namespace moe

@@ -23,7 +23,7 @@ from . import build as _build
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
-TID_X, TID_WR, TID_WG, TID_WU, TID_WD, TID_WGS, TID_WUS, TID_WDS = range(8)
+TID_X, TID_WR, TID_WG, TID_WU, TID_WD, TID_WGS, TID_WUS, TID_WDS, TID_GAMMA = range(9)
 
 F32, BF16 = 0, 1
 
@@ -71,7 +71,24 @@ def sigma_of(cfg, tid):
         return 1.0 / math.sqrt(cfg.I)
     if tid == TID_WDS:
         return 1.0 / math.sqrt(cfg.Is)
+    if tid == TID_GAMMA:
+        return GAMMA_SIGMA
     raise ValueError(tid)
+
+
+# zero-centred norm scale gamma (the scale is 1 + gamma): small spread around its zero start
+GAMMA_SIGMA = 0.1
+
+
+def host_gamma(cfg):
+    """The norm scale parameter gamma [d] in the config's dtype."""
+    return host_fill(cfg.d, cfg.dtype, cfg.seed, TID_GAMMA, GAMMA_SIGMA)
+
+
+def device_gamma(cfg, device="cuda"):
+    import torch
+    tdt = torch.float32 if cfg.dtype == F32 else torch.bfloat16
+    return device_fill(torch.empty(cfg.d, dtype=tdt, device=device), cfg.seed, TID_GAMMA, GAMMA_SIGMA)
 
 
 # ----------------------------------------------------------------------------------------------

@@ -125,3 +125,23 @@ def test_python_binding_raises_with_detail():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_workspace_size(dims(k=0))
     assert "MOE_ERR_INVALID_ARG" in str(ei.value)
+
+
+@pytest.mark.parametrize("eps", [-1e-6, float("nan"), float("inf")])
+def test_rmsnorm_and_block_reject_bad_eps(eps):
+    import sparse_mixture_experts_softmax_amd as moe
+    lib = moe.load_library()
+    dims = moe.MoeDims(4, 64, 8, 2, 32, 0, moe.MOE_BF16, 1)
+    rc = lib.moe_rmsnorm(ctypes.byref(dims), None, None, eps, None, None)
+    assert rc == 1 and b"eps" in lib.moe_last_error()  # MOE_ERR_INVALID_ARG
+    rc = lib.moe_forward_block(ctypes.byref(dims), None, None, eps, None, None, None, None, None, None, None, None,
+                               None, None, None, None, None, 0, None)
+    assert rc == 1 and b"eps" in lib.moe_last_error()  # MOE_ERR_INVALID_ARG
+
+
+def test_rmsnorm_rejects_null_gamma():
+    import sparse_mixture_experts_softmax_amd as moe
+    lib = moe.load_library()
+    dims = moe.MoeDims(4, 64, 8, 2, 32, 0, moe.MOE_BF16, 1)
+    rc = lib.moe_rmsnorm(ctypes.byref(dims), ctypes.c_void_p(4096), None, 1e-6, ctypes.c_void_p(4096), None)
+    assert rc == 1 and b"gamma" in lib.moe_last_error()  # MOE_ERR_INVALID_ARG

@@ -262,3 +262,74 @@ def test_skew_config(torch):
     for a, b in [(0, 10), (10, 50), (50, 200), (200, cfg.E)]:
         assert abs(load[a:b].sum() / L[a:b].sum() - 1) < 0.05, (a, b)
     assert np.corrcoef(np.log(load + 1), np.log(L + 1))[0, 1] > 0.97
+
+
+# --------------------------------------------------------------------------------------------
+# steps either side of the block: zero-centred RMSNorm in front, the residual add after
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [syn.F32, syn.BF16])
+def test_rmsnorm_matches_oracle_bit_for_bit(torch, dtype):
+    # both sides compute in fp64 and round once; the rows the router ranks on must be identical
+    import sparse_mixture_experts_softmax_amd as moe
+    cfg = syn.MoEConfig("norm", T=777, d=2048 + 8 * 3, E=8, k=2, I=64, Is=0, dtype=dtype, seed=4)
+    x = syn.host_x(cfg)
+    g = syn.host_gamma(cfg)
+    ref = oracle.rmsnorm(x, g)
+    dims = moe.MoeDims(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, 0, dtype, 1)
+    dt = torch_dtype(cfg)
+    from moe_testlib import to_device
+    h = moe.moe_rmsnorm(dims, to_device(x, dt), to_device(g, dt))
+    torch.cuda.synchronize()
+    hb = h.view(torch.int32 if dtype == syn.F32 else torch.int16).cpu().numpy().view(ref.dtype)
+    assert np.array_equal(hb, ref)
+
+
+BLOCK_CASES = [
+    syn.CONFIGS["tiny"],
+    syn.MoEConfig("block_ragged", T=300, d=264, E=40, k=3, I=136, Is=72, dtype=syn.BF16, seed=12),
+    syn.MoEConfig("block_mid_shape", T=700, d=2048, E=256, k=8, I=512, Is=512, dtype=syn.BF16, seed=13),
+]
+
+
+@pytest.mark.parametrize("cfg", BLOCK_CASES, ids=[c.name for c in BLOCK_CASES])
+def test_block_forward_matches_oracle(torch, cfg):
+    import sparse_mixture_experts_softmax_amd as moe
+    from moe_testlib import to_device
+    _say("case", cfg)
+    h = host_inputs(cfg)
+    dev = device_from_host(h, cfg)
+    g = syn.host_gamma(cfg)
+    dg = to_device(g, torch_dtype(cfg))
+    out, idx, w, gap = moe.moe_forward_block(dev["x"], dg, dev["w_router"], dev["wg"], dev["wu"], dev["wd"],
+                                             dev["wg_s"], dev["wu_s"], dev["wd_s"], cfg.k,
+                                             renormalize=bool(cfg.renorm), router_bias=dev["bias"],
+                                             return_routing=True)
+    torch.cuda.synchronize()
+    ref_out, ref_idx, ref_w, ref_gap, _ = oracle.block_forward(h["x"], g, h["w_router"], h["wg"], h["wu"], h["wd"],
+                                                               h["wg_s"], h["wu_s"], h["wd_s"], cfg.k,
+                                                               renorm=bool(cfg.renorm), bias=h["bias"])
+    st = compare(cfg, to_host(out), to_host(idx), to_host(w), ref_out, ref_idx, ref_w, ref_gap, cfg.name,
+                 residual=oracle.widen(h["x"]))
+    _say(cfg.name, st)
+
+
+def test_block_steps_compose_bit_for_bit(torch):
+    # rmsnorm -> router -> dispatch -> experts -> combine with the residual == the one-call block
+    import sparse_mixture_experts_softmax_amd as moe
+    from moe_testlib import to_device
+    cfg = syn.MoEConfig("block_steps", T=333, d=512, E=24, k=4, I=256, Is=128, dtype=syn.BF16, seed=14)
+    h = host_inputs(cfg)
+    dev = device_from_host(h, cfg)
+    dg = to_device(syn.host_gamma(cfg), torch_dtype(cfg))
+    dims = moe.dims_for(dev["x"], dev["w_router"], dev["wg"], dev["wg_s"], cfg.k, True)
+    ws = moe.workspace(dims, "cuda")
+    hn = moe.moe_rmsnorm(dims, dev["x"], dg)
+    idx, w, _ = moe.moe_router_topk(dims, hn, dev["w_router"], None, ws)
+    offs, sorted_token, slot_of = moe.moe_permute(dims, idx, ws)
+    y = moe.moe_grouped_ffn(dims, hn, offs, sorted_token, dev["wg"], dev["wu"], dev["wd"], dev["wg_s"],
+                            dev["wu_s"], dev["wd_s"], ws)
+    out = moe.moe_combine_residual(dims, y, slot_of, w, dev["x"])
+    out2, idx2, w2, _ = moe.moe_forward_block(dev["x"], dg, dev["w_router"], dev["wg"], dev["wu"], dev["wd"],
+                                              dev["wg_s"], dev["wu_s"], dev["wd_s"], cfg.k, return_routing=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(idx, idx2) and torch.equal(w, w2)
