@@ -126,6 +126,25 @@ def forward(x, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renorm=True, bias=None
     return out, idx, w, gap
 
 
+def router_stats(logits, topk_idx, E):
+    """Router statistics for load balancing, per expert e (the configuration listing on the
+    Qwen3.8-Max architecture page sets router_aux_loss_coef; the loss itself is not on the
+    pages): the number of tokens that select e, and the mean over tokens of e's probability
+    under the softmax over all E fp32 logits (the explorer page's router section: one
+    probability per expert), in double.
+
+    logits float32 [T,E] (from router(), bias included); topk_idx int32 [T,k].
+    Returns (counts int64 [E], prob_mean float64 [E])."""
+    lg = np.asarray(logits, dtype=np.float64)
+    T = lg.shape[0]
+    counts = np.bincount(np.asarray(topk_idx, dtype=np.int64).reshape(-1), minlength=E)
+    if T == 0:
+        return counts, np.zeros(E)
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    return counts, p.sum(axis=0) / T
+
+
 RMS_NORM_EPS = 1e-6
 
 

@@ -388,3 +388,35 @@ def test_block_forward_zero_experts_is_the_residual_and_composes():
             acc = acc + w[t, j] * dense_swiglu(hh[t:t + 1], wg[e], wu[e], wd[e])[0]
         ref[t] += acc
     assert np.allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+# --------------------------------------------------------------------------------------------
+# router statistics (per-expert counts, mean probability)
+# --------------------------------------------------------------------------------------------
+def test_router_stats_invariants_and_closed_forms():
+    rng = np.random.default_rng(21)
+    T, d, E, k = 57, 24, 11, 3
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = (rng.standard_normal((d, E)) / math.sqrt(d)).astype(np.float32)
+    idx, w, gap, logits = oracle.router(x, wr, k)
+    counts, pm = oracle.router_stats(logits, idx, E)
+    # every token contributes k selections and a probability vector that sums to one
+    assert counts.sum() == T * k and np.all(counts >= 0)
+    assert abs(pm.sum() - 1.0) < 1e-12
+    # counts equal a brute-force tally of the selections
+    assert np.array_equal(counts, [sum(int(e in idx[t]) for t in range(T)) for e in range(E)])
+    # a zero router weight gives equal logits: every expert has mean probability 1/E
+    _, _, _, lz = oracle.router(x, np.zeros_like(wr), k)
+    _, pz = oracle.router_stats(lz, idx, E)
+    assert np.allclose(pz, 1.0 / E, rtol=1e-12, atol=0)
+    # one token repeated: the mean is that token's own softmax (scipy, independent)
+    xr = np.repeat(x[:1], 9, axis=0)
+    i1, _, _, l1 = oracle.router(xr, wr, k)
+    _, p1 = oracle.router_stats(l1, i1, E)
+    assert np.allclose(p1, softmax(l1[0].astype(np.float64)), rtol=1e-12, atol=1e-15)
+    # the mean is over tokens, not over selections: doubling every logit's spread of one token
+    # changes only its own contribution
+    l2 = logits.astype(np.float64).copy()
+    l2[0] *= 2
+    _, pm2 = oracle.router_stats(l2, idx, E)
+    assert np.allclose(pm2 - pm, (softmax(l2[0]) - softmax(logits[0].astype(np.float64))) / T, atol=1e-15)
