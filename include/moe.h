@@ -94,6 +94,17 @@ moe_status moe_router_topk(const moe_dims* dims, const void* x, const float* w_r
                            int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* moe_router_topk plus router statistics for load balancing (the configuration listing on
+ * the Qwen3.8-Max architecture page sets router_aux_loss_coef; the loss formula is not on the
+ * pages, so the statistics such a loss is built from are returned):
+ *   expert_counts [E] int32  tokens that select expert e
+ *   prob_mean     [E] float  mean over the T tokens of e's probability under the softmax over
+ *                            all E logits (0 when T = 0)
+ * Sums run in fp64 in a fixed order: the results do not depend on scheduling. */
+moe_status moe_router_topk_stats(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
+                                 int32_t* topk_idx, float* topk_w, float* topk_gap, int32_t* expert_counts,
+                                 float* prob_mean, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Dispatch: group the T*k (token, expert) pairs by expert.
  *   topk_idx        [T, k]  int32 (from moe_router_topk); a token's indices in
  *                           [0, E) must be distinct, as top-k selection makes them

@@ -60,6 +60,8 @@ def load_library(path=None):
     lib.moe_combine.restype = st
     lib.moe_forward.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.moe_forward.restype = st
+    lib.moe_router_topk_stats.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.moe_router_topk_stats.restype = st
     lib.moe_rmsnorm.argtypes = [D, _P, _P, ctypes.c_double, _P, _P]
     lib.moe_rmsnorm.restype = st
     lib.moe_combine_residual.argtypes = [D, _P, _P, _P, _P, _P, _P]
@@ -233,3 +235,19 @@ def moe_forward_block(x, gamma, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renor
     if return_routing:
         return out, idx, w, gap
     return out
+
+
+def moe_router_topk_stats(dims, x, w_router, router_bias=None, ws=None):
+    """Router and top-k plus statistics. Returns (topk_idx [T,k], topk_w [T,k], topk_gap [T],
+    expert_counts int32 [E], prob_mean float32 [E])."""
+    import torch
+    lib = load_library()
+    ws = workspace(dims, x.device) if ws is None else ws
+    idx = torch.empty(dims.T, dims.k, dtype=torch.int32, device=x.device)
+    w = torch.empty(dims.T, dims.k, dtype=torch.float32, device=x.device)
+    gap = torch.empty(dims.T, dtype=torch.float32, device=x.device)
+    counts = torch.empty(dims.E, dtype=torch.int32, device=x.device)
+    pm = torch.empty(dims.E, dtype=torch.float32, device=x.device)
+    _check(lib.moe_router_topk_stats(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(idx),
+                                     _ptr(w), _ptr(gap), _ptr(counts), _ptr(pm), _ptr(ws), ws.numel(), _stream(x)))
+    return idx, w, gap, counts, pm

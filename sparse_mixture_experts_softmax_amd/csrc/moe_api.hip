@@ -138,6 +138,10 @@ Layout make_layout(const moe_dims& dm) {
   L.tile_count = take(4);
   L.H = take((size_t)L.rows_total * L.ldh * esz);
   L.Y = take((size_t)L.rows_total * dm.d * esz);
+  const int64_t stat_chunks = (T + 255) / 256;
+  L.probs = take((size_t)T * dm.E * 4);
+  L.stat_p = take((size_t)stat_chunks * dm.E * 8);
+  L.stat_c = take((size_t)stat_chunks * dm.E * 4);
   const FfnPlan P = ffn_plan(dm);
   size_t part = 0;
   if (P.s1 > 1) part = (size_t)P.s1 * L.rows_total * P.part_cols1 * 4;
@@ -205,6 +209,32 @@ moe_status moe_router_topk(const moe_dims* dims, const void* x, const float* w_r
   MOE_TRY(check_ws(dm, L, ws, ws_bytes));
   hipError_t e = launch_router(dm, L, x, w_router, router_bias, topk_idx, topk_w, topk_gap, (char*)ws, stream);
   if (e != hipSuccess) return hip_fail(e, "moe_router_topk");
+  return MOE_OK;
+}
+
+moe_status moe_router_topk_stats(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
+                                 int32_t* topk_idx, float* topk_w, float* topk_gap, int32_t* expert_counts,
+                                 float* prob_mean, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& dm = *dims;
+  MOE_TRY(check_ptr(expert_counts, 4, "expert_counts"));
+  MOE_TRY(check_ptr(prob_mean, 4, "prob_mean"));
+  MOE_TRY(check_ptr(x, 16, "x", dm.T > 0));
+  MOE_TRY(check_ptr(w_router, 4, "w_router", dm.T > 0));
+  MOE_TRY(check_ptr(router_bias, 4, "router_bias", false));
+  MOE_TRY(check_ptr(topk_idx, 4, "topk_idx", dm.T > 0));
+  MOE_TRY(check_ptr(topk_w, 4, "topk_w", dm.T > 0));
+  MOE_TRY(check_ptr(topk_gap, 4, "topk_gap", false));
+  const Layout L = make_layout(dm);
+  MOE_TRY(check_ws(dm, L, ws, ws_bytes));
+  hipError_t e;
+  if (dm.T > 0) {
+    e = launch_router(dm, L, x, w_router, router_bias, topk_idx, topk_w, topk_gap, (char*)ws, stream,
+                      (float*)((char*)ws + L.probs));
+    if (e != hipSuccess) return hip_fail(e, "moe_router_topk_stats");
+  }
+  e = launch_router_stats(dm, L, topk_idx, (char*)ws, expert_counts, prob_mean, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_router_topk_stats");
   return MOE_OK;
 }
 

@@ -58,6 +58,7 @@ struct Layout {
   int64_t rows_total;   // T*k + (I_shared ? T : 0)
   size_t router_planes, logits, topk_idx, topk_w, topk_gap, chunk_counts, offsets, sorted_token, slot_of;
   size_t tile_group, tile_m0, tile_count, H, Y;
+  size_t probs, stat_p, stat_c;  // router statistics: probabilities [T, E], per-chunk sums and counts
   size_t ffn_part;      // split-K partial sums of the grouped GEMMs (small T only)
   size_t ffn_cnt;       // split-K arrival counters: gate/up tiles, then down tiles
   int64_t ffn_cnt_each; // counters per product
@@ -95,9 +96,14 @@ struct Prof {
 // ------------------------------------------------------------------------------------------
 // launchers (enqueue only; return hipSuccess or the launch error)
 // ------------------------------------------------------------------------------------------
+// probs: when non-null, every expert's softmax probability [T, E] (for the router statistics)
 hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, const float* w_router,
                          const float* bias, int32_t* topk_idx, float* topk_w, float* topk_gap, char* ws,
-                         hipStream_t s);
+                         hipStream_t s, float* probs = nullptr);
+
+// per-expert selection counts and mean probability from the router's probs (ws) and topk_idx
+hipError_t launch_router_stats(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, char* ws,
+                               int32_t* counts, float* prob_mean, hipStream_t s);
 
 hipError_t launch_permute(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, int32_t* offsets,
                           int32_t* sorted_token, int32_t* slot_of, char* ws, hipStream_t s);

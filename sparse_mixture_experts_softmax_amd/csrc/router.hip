@@ -322,7 +322,7 @@ template <int NJ>
 __global__ void __launch_bounds__(256)
 router_topk_kernel(const float* __restrict__ part, int splits, const float* __restrict__ bias, int64_t T, int E,
                    int k, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                   float* __restrict__ topk_gap) {
+                   float* __restrict__ topk_gap, float* __restrict__ probs) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together; no block-wide barrier below
@@ -400,6 +400,11 @@ router_topk_kernel(const float* __restrict__ part, int splits, const float* __re
     topk_idx[t * k + lane] = my_i;
     topk_w[t * k + lane] = p_mine / denom;
   }
+  if (probs) {  // every expert's softmax probability, for the router statistics
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (lane + 64 * j < E) probs[t * E + lane + 64 * j] = expf(v[j] - m) / z;
+  }
   if (topk_gap) {
     const float g = k < E ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), k - 1)) -
                                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), k))
@@ -410,18 +415,70 @@ router_topk_kernel(const float* __restrict__ part, int splits, const float* __re
 
 template <int NJ>
 hipError_t launch_topk(const float* part, int splits, const float* bias, int64_t T, int E, int k, int renorm,
-                       int32_t* idx, float* w, float* gap, hipStream_t s) {
+                       int32_t* idx, float* w, float* gap, float* probs, hipStream_t s) {
   const unsigned grid = (unsigned)((T + 3) / 4);
   hipLaunchKernelGGL(router_topk_kernel<NJ>, dim3(grid), dim3(256), 0, s, part, splits, bias, T, E, k, renorm, idx,
-                     w, gap);
+                     w, gap, probs);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// router statistics: per expert, the tokens that select it and the mean of its probability.
+// Pass 1: one workgroup per (64 experts, 256 tokens); wavefront q sums tokens 64q .. +64 of the
+// chunk (lane = expert) in fp64, and the four are added in order q = 0..3. Pass 2: one thread per
+// expert adds the chunks in order. Fixed orders: the results do not depend on scheduling.
+// ------------------------------------------------------------------------------------------
+constexpr int kStatChunk = 256;
+
+__global__ void __launch_bounds__(256)
+router_stats_partial_kernel(const float* __restrict__ probs, const int32_t* __restrict__ idx, int64_t T, int E,
+                            int k, double* __restrict__ part_p, int32_t* __restrict__ part_c) {
+  __shared__ double sp[4][64];
+  __shared__ int sc[4][64];
+  const int lane = threadIdx.x & 63;
+  const int q = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int64_t c = blockIdx.y;
+  const int64_t t0 = c * kStatChunk + q * 64;
+  double acc = 0.0;
+  int n = 0;
+#pragma unroll 8
+  for (int i = 0; i < 64; ++i) {
+    const int64_t t = t0 + i;
+    if (t < T) {
+      if (e < E) acc += (double)probs[t * E + e];
+      for (int j = 0; j < k; ++j) n += idx[t * k + j] == e;
+    }
+  }
+  sp[q][lane] = acc;
+  sc[q][lane] = n;
+  __syncthreads();
+  if (q == 0 && e < E) {
+    part_p[c * E + e] = ((sp[0][lane] + sp[1][lane]) + sp[2][lane]) + sp[3][lane];
+    part_c[c * E + e] = sc[0][lane] + sc[1][lane] + sc[2][lane] + sc[3][lane];
+  }
+}
+
+__global__ void __launch_bounds__(256)
+router_stats_final_kernel(const double* __restrict__ part_p, const int32_t* __restrict__ part_c, int64_t chunks,
+                          int64_t T, int E, int32_t* __restrict__ counts, float* __restrict__ prob_mean) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  double acc = 0.0;
+  int64_t n = 0;
+  for (int64_t c = 0; c < chunks; ++c) {
+    acc += part_p[c * E + e];
+    n += part_c[c * E + e];
+  }
+  counts[e] = (int32_t)n;
+  prob_mean[e] = T > 0 ? (float)(acc / (double)T) : 0.f;
 }
 
 }  // namespace
 
 hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, const float* w_router,
                          const float* bias, int32_t* topk_idx, float* topk_w, float* topk_gap, char* ws,
-                         hipStream_t s) {
+                         hipStream_t s, float* probs) {
   float* part = (float*)(ws + L.logits);
   if (L.router_mfma) {
     bf16_t* planes = (bf16_t*)(ws + L.router_planes);
@@ -457,11 +514,28 @@ hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, con
   }
   const int nj = (dm.E + 63) / 64;
   const int sp = L.router_splits;
-  if (nj <= 1) return launch_topk<1>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, s);
-  if (nj <= 2) return launch_topk<2>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, s);
-  if (nj <= 4) return launch_topk<4>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, s);
-  if (nj <= 8) return launch_topk<8>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, s);
-  return launch_topk<16>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, s);
+  if (nj <= 1) return launch_topk<1>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, probs, s);
+  if (nj <= 2) return launch_topk<2>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, probs, s);
+  if (nj <= 4) return launch_topk<4>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, probs, s);
+  if (nj <= 8) return launch_topk<8>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, probs, s);
+  return launch_topk<16>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, probs,
+                          s);
+}
+
+hipError_t launch_router_stats(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, char* ws,
+                               int32_t* counts, float* prob_mean, hipStream_t s) {
+  const int64_t chunks = (dm.T + kStatChunk - 1) / kStatChunk;
+  double* part_p = (double*)(ws + L.stat_p);
+  int32_t* part_c = (int32_t*)(ws + L.stat_c);
+  hipError_t e;
+  if (chunks > 0) {
+    hipLaunchKernelGGL(router_stats_partial_kernel, dim3((unsigned)((dm.E + 63) / 64), (unsigned)chunks), dim3(256),
+                       0, s, (const float*)(ws + L.probs), topk_idx, dm.T, dm.E, dm.k, part_p, part_c);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(router_stats_final_kernel, dim3((unsigned)((dm.E + 255) / 256)), dim3(256), 0, s, part_p, part_c,
+                     chunks, dm.T, dm.E, counts, prob_mean);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -333,3 +333,46 @@ def test_block_steps_compose_bit_for_bit(torch):
                                               dev["wg_s"], dev["wu_s"], dev["wd_s"], cfg.k, return_routing=True)
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(idx, idx2) and torch.equal(w, w2)
+
+
+# --------------------------------------------------------------------------------------------
+# router statistics for load balancing
+# --------------------------------------------------------------------------------------------
+STAT_CASES = [
+    syn.CONFIGS["tiny"],
+    syn.MoEConfig("stats_mid_shape", T=1500, d=2048, E=256, k=8, I=64, Is=0, dtype=syn.BF16, seed=31),
+    syn.MoEConfig("stats_E512_skew", T=700, d=512, E=512, k=10, I=64, Is=0, dtype=syn.BF16, seed=32,
+                  zipf_alpha=1.2),
+    syn.MoEConfig("stats_E1024_one", T=1, d=256, E=1024, k=16, I=64, Is=0, dtype=syn.BF16, seed=33),
+]
+
+
+@pytest.mark.parametrize("cfg", STAT_CASES, ids=[c.name for c in STAT_CASES])
+def test_router_stats_match_oracle(torch, cfg):
+    import sparse_mixture_experts_softmax_amd as moe
+    from moe_testlib import to_device
+    _say("case", cfg)
+    x = syn.host_x(cfg)
+    wr = syn.host_router(cfg)
+    bias = syn.router_bias(cfg)
+    dx = to_device(x, torch_dtype(cfg))
+    dwr = to_device(wr, torch.float32)
+    db = None if bias is None else to_device(bias, torch.float32)
+    dims = moe.MoeDims(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, 0, cfg.dtype, 1)
+    idx, w, gap, counts, pm = moe.moe_router_topk_stats(dims, dx, dwr, db)
+    torch.cuda.synchronize()
+    ridx, rw, rgap, logits = oracle.router(x, wr, cfg.k, bias=bias)
+    rcounts, rpm = oracle.router_stats(logits, ridx, cfg.E)
+    gi = to_host(idx)
+    # counts: exactly the GPU's own selections; those equal the oracle's off the tie band
+    assert np.array_equal(to_host(counts), np.bincount(gi.reshape(-1), minlength=cfg.E))
+    ok = ~oracle.flagged(rgap)
+    assert np.array_equal(np.sort(gi[ok], axis=1), np.sort(ridx[ok], axis=1))
+    if ok.all():
+        assert np.array_equal(to_host(counts), rcounts)
+    # mean probabilities: fp32 logits agree to ~1e-6, so do the probabilities
+    g = to_host(pm).astype(np.float64)
+    assert abs(g.sum() - 1.0) < 1e-5
+    err = np.max(np.abs(g - rpm))
+    assert err <= 1e-5 * rpm.max(), (err, rpm.max())
+    _say(cfg.name, "flagged", int((~ok).sum()), "prob_mean max err", err)
