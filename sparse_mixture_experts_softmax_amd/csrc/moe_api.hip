@@ -138,7 +138,7 @@ Layout make_layout(const moe_dims& dm) {
   L.tile_count = take(4);
   L.H = take((size_t)L.rows_total * L.ldh * esz);
   L.Y = take((size_t)L.rows_total * dm.d * esz);
-  const int64_t stat_chunks = (T + 255) / 256;
+  const int64_t stat_chunks = (T + 63) / 64;  // router statistics: 64-token chunks
   L.probs = take((size_t)T * dm.E * 4);
   L.stat_p = take((size_t)stat_chunks * dm.E * 8);
   L.stat_c = take((size_t)stat_chunks * dm.E * 4);

@@ -424,30 +424,41 @@ hipError_t launch_topk(const float* part, int splits, const float* bias, int64_t
 
 // ------------------------------------------------------------------------------------------
 // router statistics: per expert, the tokens that select it and the mean of its probability.
-// Pass 1: one workgroup per (64 experts, 256 tokens); wavefront q sums tokens 64q .. +64 of the
-// chunk (lane = expert) in fp64, and the four are added in order q = 0..3. Pass 2: one thread per
-// expert adds the chunks in order. Fixed orders: the results do not depend on scheduling.
+// Pass 1: one workgroup per (64 experts, 64 tokens); the chunk's selections are staged in LDS,
+// wavefront q sums tokens 16q .. +16 of the chunk (lane = expert, all 16 probability loads in
+// flight) in fp64, and the four are added in order q = 0..3. Pass 2: one thread per expert adds
+// the chunks in order. Fixed orders: the results do not depend on scheduling.
 // ------------------------------------------------------------------------------------------
-constexpr int kStatChunk = 256;
+constexpr int kStatChunk = 64;
 
 __global__ void __launch_bounds__(256)
 router_stats_partial_kernel(const float* __restrict__ probs, const int32_t* __restrict__ idx, int64_t T, int E,
                             int k, double* __restrict__ part_p, int32_t* __restrict__ part_c) {
+  __shared__ int sel[kStatChunk * kMaxK];
   __shared__ double sp[4][64];
   __shared__ int sc[4][64];
   const int lane = threadIdx.x & 63;
   const int q = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + lane;
   const int64_t c = blockIdx.y;
-  const int64_t t0 = c * kStatChunk + q * 64;
+  const int64_t base = c * kStatChunk;
+  const int nt = (int)min<int64_t>(kStatChunk, T - base);
+  for (int i = threadIdx.x; i < nt * k; i += 256) sel[i] = idx[base * k + i];
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tt = q * 16 + i;
+    p[i] = (tt < nt && e < E) ? probs[(base + tt) * E + e] : 0.f;
+  }
+  __syncthreads();
   double acc = 0.0;
   int n = 0;
-#pragma unroll 8
-  for (int i = 0; i < 64; ++i) {
-    const int64_t t = t0 + i;
-    if (t < T) {
-      if (e < E) acc += (double)probs[t * E + e];
-      for (int j = 0; j < k; ++j) n += idx[t * k + j] == e;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tt = q * 16 + i;
+    if (tt < nt) {
+      acc += (double)p[i];
+      for (int j = 0; j < k; ++j) n += sel[tt * k + j] == e;
     }
   }
   sp[q][lane] = acc;
