@@ -145,6 +145,71 @@ def router_stats(logits, topk_idx, E):
     return counts, p.sum(axis=0) / T
 
 
+# ----------------------------------------------------------------------------------------------
+# FP8 expert weights (the Fondations page names FP8 among the formats; no scheme is given, so the
+# chosen one is stated here): OCP e4m3 (4 exponent bits, bias 7, 3 mantissa bits, no infinities,
+# largest finite 448), one power-of-two scale per output column, round to nearest even.
+# ----------------------------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code):
+    """Value of an OCP e4m3 byte (float64; NaN for the two NaN codes)."""
+    c = np.asarray(code, dtype=np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    v = np.where((e == 15) & ((c & 7) == 7), np.nan, v)
+    return s * v
+
+
+def e4m3_round(v):
+    """Nearest e4m3 code of each value (|v| <= 448), ties to the even code, found by search over
+    the 127 non-negative finite values in double."""
+    v = np.asarray(v, dtype=np.float64)
+    assert np.all(np.abs(v) <= E4M3_MAX), "outside the e4m3 range"
+    pos = e4m3_value(np.arange(127))          # codes 0 .. 126, ascending values
+    a = np.abs(v)
+    hi = np.searchsorted(pos, a, side="left")  # first code with value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - pos[lo]
+    dhi = pos[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a == pos[hi], hi, pick)
+    return (pick | np.where((v < 0) & (pick != 0), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_fp8(w):
+    """Quantise weights w [..., K, N] (float32, or bf16 bits as uint16) stored N-contiguous.
+
+    Per output column n: scale s_n = 2^ceil(log2(max_k |w[k, n]| / 448)) (1 for an all-zero
+    column), q = e4m3_round(w / s_n) -- the division by a power of two is exact. Returns
+    (q uint8 [..., N, K] with K contiguous, s float32 [..., N])."""
+    wf = widen(w)
+    amax = np.abs(wf).max(axis=-2)                            # [..., N]
+    ex = np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / E4M3_MAX))
+    # exact guard: the smallest power of two with amax / s <= 448
+    ex = np.where(amax / np.exp2(ex) > E4M3_MAX, ex + 1, ex)
+    ex = np.where(amax / np.exp2(ex - 1) <= E4M3_MAX, ex - 1, ex)
+    scale = np.where(amax > 0, np.exp2(ex), 1.0)
+    q = e4m3_round(wf / scale[..., None, :])
+    return np.ascontiguousarray(np.swapaxes(q, -1, -2)), scale.astype(np.float32)
+
+
+def dequantize_fp8(q, s, dtype=np.uint16):
+    """The weights q, s stand for, back in the N-contiguous [..., K, N] layout: exact in bf16
+    (4 significant bits times a power of two), returned as bf16 bits (or float32)."""
+    v = e4m3_value(q) * np.asarray(s, dtype=np.float64)[..., :, None]   # [..., N, K]
+    v = np.ascontiguousarray(np.swapaxes(v, -1, -2)).astype(np.float32)
+    if dtype == np.float32:
+        return v
+    b = v.view(np.uint32)
+    assert np.all(b & 0xFFFF == 0), "dequantised weight not exact in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
 RMS_NORM_EPS = 1e-6
 
 

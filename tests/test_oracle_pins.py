@@ -420,3 +420,64 @@ def test_router_stats_invariants_and_closed_forms():
     l2[0] *= 2
     _, pm2 = oracle.router_stats(l2, idx, E)
     assert np.allclose(pm2 - pm, (softmax(l2[0]) - softmax(logits[0].astype(np.float64))) / T, atol=1e-15)
+
+
+# --------------------------------------------------------------------------------------------
+# FP8 expert weights: OCP e4m3 codes, round to nearest even, power-of-two column scales
+# --------------------------------------------------------------------------------------------
+def test_e4m3_code_table_closed_forms():
+    # values fixed by the format: bias 7, 3 mantissa bits, subnormals below 2^-6, 448 the largest
+    # finite value, S.1111.111 the NaN codes, sign-magnitude
+    v = oracle.e4m3_value(np.arange(256))
+    assert v[0x00] == 0.0 and v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9
+    assert v[0x08] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x39] == 1.125 and v[0x7E] == 448.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.sum(np.isnan(v)) == 2
+    assert np.array_equal(v[0x80:0xFF], -v[0x00:0x7F])
+    assert np.all(np.diff(v[:0x7F]) > 0)  # codes 0 .. 126 ascend
+
+
+def test_e4m3_round_to_nearest_even():
+    pos = oracle.e4m3_value(np.arange(127))
+    # every finite value rounds to its own code
+    assert np.array_equal(oracle.e4m3_round(pos), np.arange(127, dtype=np.uint8))
+    assert np.array_equal(oracle.e4m3_round(-pos[1:]), (np.arange(1, 127) | 0x80).astype(np.uint8))
+    # halfway points go to the even code; just off halfway goes to the nearer one
+    cases = [(1.0625, 0x38), (1.1875, 0x3A), (1.0625 + 2 ** -20, 0x39), (2.0 ** -10, 0x00),
+             (1.5 * 2.0 ** -9, 0x02), (2.5 * 2.0 ** -9, 0x02), (432.0, 0x7E), (416.0, 0x7D), (-1.0625, 0xB8)]
+    for val, code in cases:
+        assert int(oracle.e4m3_round(np.array([val]))[0]) == code, (val, hex(code))
+    # against brute force: the code whose value is nearest, ties to the even code
+    rng = np.random.default_rng(41)
+    x = rng.uniform(-448, 448, 4000) * rng.choice([1, 2.0 ** -6, 2.0 ** -9], 4000)
+    got = oracle.e4m3_round(x)
+    d = np.abs(np.abs(x)[:, None] - pos[None, :])
+    best = d.min(axis=1, keepdims=True)
+    near = d == best
+    want = np.where(near.sum(axis=1) == 2, np.argmax(near & (np.arange(127) % 2 == 0), axis=1), np.argmax(near, axis=1))
+    want = np.where((x < 0) & (want != 0), want | 0x80, want)
+    assert np.array_equal(got, want.astype(np.uint8))
+
+
+def test_fp8_quantisation_scales_layout_and_error():
+    rng = np.random.default_rng(42)
+    K, N = 96, 40
+    w = (rng.standard_normal((2, K, N)) * np.exp2(rng.integers(-12, 4, size=(2, 1, N)))).astype(np.float32)
+    w[1, :, 7] = 0.0
+    q, s = oracle.quantize_fp8(w)
+    assert q.shape == (2, N, K) and s.shape == (2, N)
+    amax = np.abs(w).max(axis=1)
+    # power-of-two scales, the smallest with amax / s <= 448
+    e = np.log2(s.astype(np.float64))
+    assert np.array_equal(e, np.round(e))
+    nz = amax > 0
+    assert np.all(amax[nz] / s[nz] <= 448) and np.all(amax[nz] / s[nz] > 224)
+    assert s[1, 7] == 1.0 and np.all(q[1, 7] == 0)
+    # q[n, k] encodes w[k, n] (the transposed, K-contiguous layout), each within half a step
+    d = oracle.dequantize_fp8(q, s, np.float32).astype(np.float64)
+    wf = w.astype(np.float64)
+    step = np.where(np.abs(wf) / s[:, None, :] < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(wf) / s[:, None, :], 2.0 ** -6))) - 3))
+    assert np.all(np.abs(d - wf) <= 0.5 * step * s[:, None, :] * (1 + 1e-12))
+    # values already on the grid come back exactly
+    g = oracle.dequantize_fp8(q, s, np.float32)
+    q2, s2 = oracle.quantize_fp8(g)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
