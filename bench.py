@@ -213,6 +213,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mid", choices=["tiny", "mid", "decode", "prefill", "skew"])
     ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count T")
+    ap.add_argument("--fp8", action="store_true",
+                    help="expert weights in FP8 (e4m3, power-of-two column scales), quantised before timing")
     ap.add_argument("--block", action="store_true",
                     help="time the block between its neighbours: zero-centred RMSNorm in front, residual add after")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -257,9 +259,21 @@ def main():
     out = torch.empty_like(x)
 
     gamma = syn.device_gamma(cfg, device=dev) if args.block else None
+    if args.fp8 and args.block:
+        print("bench.py: --fp8 and --block are separate entry points; pick one", file=sys.stderr)
+        sys.exit(2)
+    fp8 = None
+    if args.fp8:
+        fp8 = moe.Fp8Experts(inp["wg"], inp["wu"], inp["wd"], inp["wg_s"], inp["wu_s"], inp["wd_s"])
+        for key in ("wg", "wu", "wd", "wg_s", "wu_s", "wd_s"):  # the bf16 copies are not needed any more
+            inp[key] = None
+        torch.cuda.empty_cache()
 
     def step():
-        if args.block:
+        if fp8 is not None:
+            moe.moe_forward_fp8(x, inp["w_router"], fp8, cfg.k, renormalize=bool(cfg.renorm), router_bias=inp["bias"],
+                                ws=ws, out=out, dims=dims)
+        elif args.block:
             moe.moe_forward_block(x, gamma, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"],
                                   inp["wu_s"], inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm),
                                   router_bias=inp["bias"], ws=ws, out=out, dims=dims)
@@ -296,7 +310,10 @@ def main():
         hip.destroy(b)
 
     # routing of this input, for the algorithmic work actually required
-    if args.block:
+    if fp8 is not None:
+        _, idx, _, _ = moe.moe_forward_fp8(x, inp["w_router"], fp8, cfg.k, renormalize=bool(cfg.renorm),
+                                           router_bias=inp["bias"], return_routing=True, ws=ws, dims=dims)
+    elif args.block:
         _, idx, _, _ = moe.moe_forward_block(x, gamma, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"],
                                              inp["wu_s"], inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm),
                                              router_bias=inp["bias"], return_routing=True, ws=ws, dims=dims)
@@ -317,7 +334,10 @@ def main():
 
     ms_per_step = total_ms / K
     tokens_per_s = cfg.T / (ms_per_step * 1e-3)
-    kb = wl.ffn1_algorithmic_bytes(cfg.T, cfg.d, cfg.I, cfg.Is, cfg.dtype, touched, cfg.k)
+    if fp8 is not None:
+        kb = wl.ffn1_algorithmic_bytes_fp8(cfg.T, cfg.d, cfg.I, cfg.Is, touched, cfg.k)
+    else:
+        kb = wl.ffn1_algorithmic_bytes(cfg.T, cfg.d, cfg.I, cfg.Is, cfg.dtype, touched, cfg.k)
     kf = wl.ffn1_flops(cfg.T, cfg.d, cfg.k, cfg.I, cfg.Is)
     peak_flops = wl.BF16_MFMA_PEAK_FLOPS if cfg.dtype == syn.BF16 else wl.FP32_VECTOR_PEAK_FLOPS
     t_s = kern_avg_ms * 1e-3
@@ -327,13 +347,17 @@ def main():
         roof = {"bound": "mfma" if cfg.dtype == syn.BF16 else "alu", "achieved": kf / t_s / 1e12,
                 "peak": peak_flops / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_for(cfg.name)
-    roof["kernel"] = "ffn_mfma_stream_kernel<true, ...> (gate/up)" if cfg.dtype == syn.BF16 else "ffn_f32_kernel<true>"
+    roof["traffic"] = None if (fp8 is not None or args.block or args.tokens is not None) else traffic_for(cfg.name)
+    roof["kernel"] = ("ffn_fp8_stream_kernel<true, 4> (gate/up, e4m3 weights)" if fp8 is not None else
+                      "ffn_mfma_stream_kernel<true, ...> (gate/up)" if cfg.dtype == syn.BF16 else "ffn_f32_kernel<true>")
     roof["kernel_ms"] = kern_avg_ms
     roof["algorithmic_bytes"] = kb
     roof["algorithmic_flops"] = kf
 
-    lb = wl.algorithmic_bytes(cfg.T, cfg.d, cfg.E, cfg.I, cfg.Is, cfg.dtype, touched)
+    if fp8 is not None:
+        lb = wl.algorithmic_bytes_fp8(cfg.T, cfg.d, cfg.E, cfg.I, cfg.Is, touched)
+    else:
+        lb = wl.algorithmic_bytes(cfg.T, cfg.d, cfg.E, cfg.I, cfg.Is, cfg.dtype, touched)
     lf = wl.expert_flops(cfg.T, cfg.d, cfg.k, cfg.I, cfg.Is)
     layer = {"touched_experts": touched, "algorithmic_bytes": lb, "expert_flops": lf,
              "router_flops": wl.router_flops(cfg.T, cfg.d, cfg.E),
@@ -352,7 +376,8 @@ def main():
         "config": {"workload": "%s MoE layer: T=%d, d=%d, E=%d, k=%d, I=%d, shared I=%d, %s, fp32 router%s%s"
                    % (cfg.name, cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.Is, cfg.dtype_name,
                       ", Zipf(%.1f) router bias" % cfg.zipf_alpha if cfg.zipf_alpha else "",
-                      ", RMSNorm in front and residual add" if args.block else ""),
+                      ", RMSNorm in front and residual add" if args.block else
+                      ", FP8 e4m3 expert weights" if fp8 is not None else ""),
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "I": cfg.I, "I_shared": cfg.Is,
                    "renormalize": cfg.renorm, "seed": cfg.seed},
         "roofline": roof, "layer": layer, "cpu_baseline": cpu, "wall_s_timed": wall,

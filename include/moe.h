@@ -147,6 +147,29 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_route
                        const void* wd_s, void* out, int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws,
                        size_t ws_bytes, hipStream_t stream);
 
+/* FP8 expert weights (the Fondations page of the Qwen3.8-Max report names FP8 among the formats
+ * and gives no scheme; this is the one used): weight-only OCP e4m3 (bias 7, 3 mantissa bits,
+ * largest finite 448), one power-of-two fp32 scale per output column, codes by round to nearest
+ * with ties to even, stored K-contiguous:
+ *   W[k, n] = e4m3(Q[n, k]) * s[n]
+ *
+ * moe_quantize_fp8: w [batch, K, N] (dtype, N-contiguous as the bf16 expert weights are stored)
+ *   -> q [batch, N, K] uint8 codes, scale [batch, N] float; s[n] is the smallest power of two with
+ *   max_k |w[k, n]| / s[n] <= 448 (1 for an all-zero column). batch <= 65535. */
+moe_status moe_quantize_fp8(const void* w, int32_t dtype, int64_t batch, int32_t K, int32_t N, uint8_t* q,
+                            float* scale, hipStream_t stream);
+
+/* moe_forward with FP8 expert weights (moe_quantize_fp8 layout): wg, wu [E, I, d] codes with sg, su
+ * [E, I]; wd [E, d, I] with sd [E, d]; the shared expert wg_s, wu_s [I_shared, d], wd_s
+ * [d, I_shared] with sg_s, su_s [I_shared], sd_s [d]. x, out bf16 (dims.dtype = MOE_BF16);
+ * d % 256 == 0 and I, I_shared % 128 == 0, else MOE_ERR_UNSUPPORTED. The products run on the bf16
+ * MFMA with the codes widened exactly; the column scales are applied to the fp32 sums. */
+moe_status moe_forward_fp8(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
+                           const uint8_t* wg, const uint8_t* wu, const uint8_t* wd, const float* sg, const float* su,
+                           const float* sd, const uint8_t* wg_s, const uint8_t* wu_s, const uint8_t* wd_s,
+                           const float* sg_s, const float* su_s, const float* sd_s, void* out, int32_t* topk_idx,
+                           float* topk_w, float* topk_gap, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Steps either side of the block: zero-centred RMSNorm in front of it (the Qwen3-Next
  * article: Zero-Centered RMSNorm, parameters starting at zero, so the scale is 1 + gamma;
  * the Qwen3.8-Max architecture page's configuration listing: rms_norm_eps = 1e-6) and the

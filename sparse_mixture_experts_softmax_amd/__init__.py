@@ -62,6 +62,12 @@ def load_library(path=None):
     lib.moe_forward.restype = st
     lib.moe_router_topk_stats.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.moe_router_topk_stats.restype = st
+    lib.moe_quantize_fp8.argtypes = [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+    lib.moe_quantize_fp8.restype = st
+    # dims; x, w_router, router_bias, 6 code arrays and 6 scale arrays, out, topk_idx, topk_w, topk_gap, ws;
+    # ws_bytes; stream
+    lib.moe_forward_fp8.argtypes = [D] + [_P] * 20 + [ctypes.c_size_t, _P]
+    lib.moe_forward_fp8.restype = st
     lib.moe_rmsnorm.argtypes = [D, _P, _P, ctypes.c_double, _P, _P]
     lib.moe_rmsnorm.restype = st
     lib.moe_combine_residual.argtypes = [D, _P, _P, _P, _P, _P, _P]
@@ -251,3 +257,59 @@ def moe_router_topk_stats(dims, x, w_router, router_bias=None, ws=None):
     _check(lib.moe_router_topk_stats(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(idx),
                                      _ptr(w), _ptr(gap), _ptr(counts), _ptr(pm), _ptr(ws), ws.numel(), _stream(x)))
     return idx, w, gap, counts, pm
+
+
+def moe_quantize_fp8(w):
+    """FP8 (e4m3) codes and column scales of w [..., K, N] (float32 or bfloat16, N-contiguous).
+    Returns (q uint8 [..., N, K], scale float32 [..., N])."""
+    import torch
+    lib = load_library()
+    K, N = w.shape[-2], w.shape[-1]
+    batch = w.numel() // (K * N) if w.numel() else 0
+    q = torch.empty(w.shape[:-2] + (N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty(w.shape[:-2] + (N,), dtype=torch.float32, device=w.device)
+    _check(lib.moe_quantize_fp8(_ptr(w), _dtype_code(w), batch, K, N, _ptr(q), _ptr(s), _stream(w)))
+    return q, s
+
+
+class Fp8Experts:
+    """Expert weights in FP8 (moe_quantize_fp8 of the bf16 wg, wu, wd and the shared expert)."""
+
+    def __init__(self, wg, wu, wd, wg_s=None, wu_s=None, wd_s=None):
+        self.wg, self.sg = moe_quantize_fp8(wg)
+        self.wu, self.su = moe_quantize_fp8(wu)
+        self.wd, self.sd = moe_quantize_fp8(wd)
+        if wg_s is not None:
+            self.wg_s, self.sg_s = moe_quantize_fp8(wg_s)
+            self.wu_s, self.su_s = moe_quantize_fp8(wu_s)
+            self.wd_s, self.sd_s = moe_quantize_fp8(wd_s)
+        else:
+            self.wg_s = self.sg_s = self.wu_s = self.su_s = self.wd_s = self.sd_s = None
+        self.E, self.I, self.d = self.wg.shape
+        self.I_shared = 0 if wg_s is None else wg_s.shape[1]
+
+
+def moe_forward_fp8(x, w_router, experts, k, renormalize=True, router_bias=None, return_routing=False, ws=None,
+                    out=None, dims=None):
+    """The MoE block with FP8 expert weights (an Fp8Experts). Returns out [T, d], or
+    (out, topk_idx, topk_w, topk_gap) with return_routing."""
+    import torch
+    lib = load_library()
+    f = experts
+    if dims is None:
+        T, d = x.shape
+        dims = MoeDims(T, d, w_router.shape[1], k, f.I, f.I_shared, _dtype_code(x), int(bool(renormalize)))
+    ws = workspace(dims, x.device) if ws is None else ws
+    out = torch.empty_like(x) if out is None else out
+    idx = w = gap = None
+    if return_routing:
+        idx = torch.empty(dims.T, dims.k, dtype=torch.int32, device=x.device)
+        w = torch.empty(dims.T, dims.k, dtype=torch.float32, device=x.device)
+        gap = torch.empty(dims.T, dtype=torch.float32, device=x.device)
+    _check(lib.moe_forward_fp8(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(f.wg),
+                               _ptr(f.wu), _ptr(f.wd), _ptr(f.sg), _ptr(f.su), _ptr(f.sd), _ptr(f.wg_s), _ptr(f.wu_s),
+                               _ptr(f.wd_s), _ptr(f.sg_s), _ptr(f.su_s), _ptr(f.sd_s), _ptr(out), _ptr(idx), _ptr(w),
+                               _ptr(gap), _ptr(ws), ws.numel(), _stream(x)))
+    if return_routing:
+        return out, idx, w, gap
+    return out

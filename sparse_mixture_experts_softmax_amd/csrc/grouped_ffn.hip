@@ -33,29 +33,6 @@ namespace {
 using stream::bf16x8_t;
 using stream::f32x16_t;
 
-struct Group {
-  int64_t row0;  // first sorted slot of the group
-  int rows;      // rows in the group
-  int n_inter;   // intermediate size of the group (I or I_shared)
-  bool shared;
-};
-
-__device__ __forceinline__ Group group_info(int g, const int32_t* offsets, int64_t T, int k, int E, int I, int Is) {
-  Group G;
-  if (g < E) {
-    G.row0 = offsets[g];
-    G.rows = offsets[g + 1] - offsets[g];
-    G.n_inter = I;
-    G.shared = false;
-  } else {
-    G.row0 = T * (int64_t)k;
-    G.rows = (int)T;
-    G.n_inter = Is;
-    G.shared = true;
-  }
-  return G;
-}
-
 // ------------------------------------------------------------------------------------------
 // tile list: for each group with n rows, ceil(n / BM) tiles (group, first row)
 // ------------------------------------------------------------------------------------------
@@ -412,7 +389,8 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
 
   f32x16_t acc[2][4];
   zero(acc);
-  if (nk > 0) mainloop<WN, S>(nk, nl, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+  const int rows = G.rows - m0 < SBM ? G.rows - m0 : SBM;
+  if (nk > 0) mainloop<WN, S>(nk, nl, rows, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
 
   // 32x32 accumulator layout -- lane holds column (lane & 31); register r holds row
   // 8*(r/4) + 4*(lane/32) + (r%4)
@@ -633,6 +611,15 @@ ffn_f32_kernel(F32Args p) {
 
 }  // namespace
 
+int ffn_tile_rows(const moe_dims& dm) { return dm.dtype == MOE_F32 ? kF32BM : kMfmaBM; }
+
+hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s) {
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, dm.T, dm.E, dm.I_shared > 0 ? 1 : 0,
+                     ffn_tile_rows(dm), (int32_t*)(ws + L.tile_group), (int32_t*)(ws + L.tile_m0),
+                     (int32_t*)(ws + L.tile_count), (int32_t*)(ws + L.ffn_cnt), 2 * L.ffn_cnt_each);
+  return hipGetLastError();
+}
+
 FfnPlan ffn_plan(const moe_dims& dm) {
   FfnPlan P;
   const int has_shared = dm.I_shared > 0 ? 1 : 0;
@@ -680,11 +667,9 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
   const int has_shared = dm.I_shared > 0 ? 1 : 0;
   const FfnPlan P = ffn_plan(dm);
   const bool stream_ok = P.stream;
-  const int bm = dm.dtype == MOE_F32 ? kF32BM : kMfmaBM;
+  const int bm = ffn_tile_rows(dm);
   int32_t* cnt = (int32_t*)(ws + L.ffn_cnt);
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, dm.T, dm.E, has_shared, bm, tg, tm, tc,
-                     cnt, 2 * L.ffn_cnt_each);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_build_tiles(dm, L, offsets, ws, s);
   if (e != hipSuccess) return e;
 
   // upper bound on row tiles: sum over non-empty groups of ceil(n_g / bm) <= (T*k)/bm + (routed

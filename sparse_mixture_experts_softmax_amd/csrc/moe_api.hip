@@ -332,7 +332,8 @@ namespace {
 moe_status forward_rows(const moe_dims& dm, const Layout& L, const void* xin, const void* residual,
                         const float* w_router, const float* router_bias, const void* wg, const void* wu,
                         const void* wd, const void* wg_s, const void* wu_s, const void* wd_s, void* out,
-                        int32_t* topk_idx, float* topk_w, float* topk_gap, char* w, hipStream_t stream) {
+                        int32_t* topk_idx, float* topk_w, float* topk_gap, char* w, hipStream_t stream,
+                        const Fp8Weights* fp8 = nullptr) {
   int32_t* idx = topk_idx ? topk_idx : (int32_t*)(w + L.topk_idx);
   float* tw = topk_w ? topk_w : (float*)(w + L.topk_w);
   int32_t* offsets = (int32_t*)(w + L.offsets);
@@ -350,7 +351,10 @@ moe_status forward_rows(const moe_dims& dm, const Layout& L, const void* xin, co
   e = launch_permute(dm, L, idx, offsets, sorted, slot, w, stream);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/permute");
   if ((e = prof.end(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
-  e = launch_grouped_ffn(dm, L, xin, offsets, sorted, wg, wu, wd, wg_s, wu_s, wd_s, y, w, stream, &prof);
+  if (fp8)
+    e = launch_grouped_ffn_fp8(dm, L, xin, offsets, sorted, *fp8, y, w, stream, &prof);
+  else
+    e = launch_grouped_ffn(dm, L, xin, offsets, sorted, wg, wu, wd, wg_s, wu_s, wd_s, y, w, stream, &prof);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/grouped_ffn");
   if ((e = prof.begin(MOE_KERNEL_COMBINE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
   e = launch_combine(dm, y, slot, tw, residual, out, stream);
@@ -397,6 +401,49 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_route
   MOE_TRY(check_ws(dm, L, ws, ws_bytes));
   return forward_rows(dm, L, x, nullptr, w_router, router_bias, wg, wu, wd, wg_s, wu_s, wd_s, out, topk_idx, topk_w,
                       topk_gap, (char*)ws, stream);
+}
+
+moe_status moe_forward_fp8(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
+                           const uint8_t* wg, const uint8_t* wu, const uint8_t* wd, const float* sg, const float* su,
+                           const float* sd, const uint8_t* wg_s, const uint8_t* wu_s, const uint8_t* wd_s,
+                           const float* sg_s, const float* su_s, const float* sd_s, void* out, int32_t* topk_idx,
+                           float* topk_w, float* topk_gap, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& dm = *dims;
+  if (!fp8_shape_ok(dm))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "FP8 experts need bf16 activations, d %% 256 == 0, I and I_shared %% 128 == 0 (dtype %d, d %d, I %d, "
+                "I_shared %d)",
+                dm.dtype, dm.d, dm.I, dm.I_shared);
+  if (dm.T == 0) return MOE_OK;
+  const bool hs = dm.I_shared > 0;
+  MOE_TRY(check_block_ptrs(dm, x, w_router, router_bias, wg, wu, wd, wg_s, wu_s, wd_s, out, topk_idx, topk_w,
+                           topk_gap));
+  MOE_TRY(check_ptr(sg, 4, "sg"));
+  MOE_TRY(check_ptr(su, 4, "su"));
+  MOE_TRY(check_ptr(sd, 4, "sd"));
+  MOE_TRY(check_ptr(sg_s, 4, "sg_s", hs));
+  MOE_TRY(check_ptr(su_s, 4, "su_s", hs));
+  MOE_TRY(check_ptr(sd_s, 4, "sd_s", hs));
+  const Layout L = make_layout(dm);
+  MOE_TRY(check_ws(dm, L, ws, ws_bytes));
+  const Fp8Weights W{wg, wu, wd, sg, su, sd, wg_s, wu_s, wd_s, sg_s, su_s, sd_s};
+  return forward_rows(dm, L, x, nullptr, w_router, router_bias, wg, wu, wd, wg_s, wu_s, wd_s, out, topk_idx, topk_w,
+                      topk_gap, (char*)ws, stream, &W);
+}
+
+moe_status moe_quantize_fp8(const void* w, int32_t dtype, int64_t batch, int32_t K, int32_t N, uint8_t* q,
+                            float* scale, hipStream_t stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "dtype = %d", dtype);
+  if (batch < 0 || K < 1 || N < 1 || batch > 65535)
+    return fail(MOE_ERR_INVALID_ARG, "batch = %lld (0 .. 65535), K = %d, N = %d (>= 1)", (long long)batch, K, N);
+  if (batch == 0) return MOE_OK;
+  MOE_TRY(check_ptr(w, dtype == MOE_BF16 ? 2 : 4, "w"));
+  MOE_TRY(check_ptr(q, 1, "q"));
+  MOE_TRY(check_ptr(scale, 4, "scale"));
+  hipError_t e = launch_quantize_fp8(w, dtype, batch, K, N, q, scale, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_quantize_fp8");
+  return MOE_OK;
 }
 
 moe_status moe_forward_block(const moe_dims* dims, const void* x, const void* gamma, double eps,

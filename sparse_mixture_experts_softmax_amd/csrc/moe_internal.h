@@ -94,6 +94,33 @@ struct Prof {
 };
 
 // ------------------------------------------------------------------------------------------
+// grouped GEMM groups: routed expert g < E owns sorted slots [offsets[g], offsets[g+1]); group E
+// is the shared expert over all T tokens, whose rows follow the T*k routed ones
+// ------------------------------------------------------------------------------------------
+struct Group {
+  int64_t row0;  // first sorted slot of the group
+  int rows;      // rows in the group
+  int n_inter;   // intermediate size of the group (I or I_shared)
+  bool shared;
+};
+
+__device__ __forceinline__ Group group_info(int g, const int32_t* offsets, int64_t T, int k, int E, int I, int Is) {
+  Group G;
+  if (g < E) {
+    G.row0 = offsets[g];
+    G.rows = offsets[g + 1] - offsets[g];
+    G.n_inter = I;
+    G.shared = false;
+  } else {
+    G.row0 = T * (int64_t)k;
+    G.rows = (int)T;
+    G.n_inter = Is;
+    G.shared = true;
+  }
+  return G;
+}
+
+// ------------------------------------------------------------------------------------------
 // launchers (enqueue only; return hipSuccess or the launch error)
 // ------------------------------------------------------------------------------------------
 // probs: when non-null, every expert's softmax probability [T, E] (for the router statistics)
@@ -114,6 +141,25 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
                               hipStream_t s, const Prof* prof = nullptr);
 
 // residual: [T, d] added last (nullptr: none)
+// row-tile list of the grouped GEMMs (rows per tile ffn_tile_rows) and zeroed split-K counters
+int ffn_tile_rows(const moe_dims& dm);
+hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s);
+
+// FP8 (e4m3) expert weights: K-contiguous codes [.., N, K] with one fp32 scale per output column
+struct Fp8Weights {
+  const uint8_t *wg, *wu, *wd;      // [E, I, d], [E, I, d], [E, d, I]
+  const float *sg, *su, *sd;        // [E, I], [E, I], [E, d]
+  const uint8_t *wg_s, *wu_s, *wd_s;  // [I_s, d], [I_s, d], [d, I_s]
+  const float *sg_s, *su_s, *sd_s;    // [I_s], [I_s], [d]
+};
+bool fp8_shape_ok(const moe_dims& dm);
+hipError_t launch_grouped_ffn_fp8(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
+                                  const int32_t* sorted_token, const Fp8Weights& W, void* y, char* ws, hipStream_t s,
+                                  const Prof* prof = nullptr);
+// w [batch, K, N] (dtype) -> q [batch, N, K] e4m3, scale [batch, N]
+hipError_t launch_quantize_fp8(const void* w, int dtype, int64_t batch, int K, int N, uint8_t* q, float* scale,
+                               hipStream_t s);
+
 hipError_t launch_combine(const moe_dims& dm, const void* y, const int32_t* slot_of, const float* topk_w,
                           const void* residual, void* out, hipStream_t s);
 

@@ -100,7 +100,7 @@ router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ plan
 
   f32x16_t acc[2][4];
   zero(acc);
-  mainloop<2, 3>(nk, nl, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+  mainloop<2, 3>(nk, nl, (int)min<int64_t>(T - t0, 128), (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
 
   float* out = part + (int64_t)split * T * E;
   const int col_in = lane & 31;

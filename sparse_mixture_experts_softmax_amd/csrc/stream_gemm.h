@@ -145,14 +145,15 @@ __device__ __forceinline__ void wait_groups(int n) {
   else wait_vmcnt<0>();
 }
 
-template <int WN, int S, int NL, class ABase, class BBase>
+template <int WN, int S, int NL, int NAD, class ABase, class BBase>
 __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
                                            const uint32_t (&a_off)[Geo<WN>::A_DMA], BBase b_base, uint32_t b_off,
                                            const int (&bcol)[4], f32x16_t (&acc)[2][4]) {
   static_assert(S >= 3 && S <= 5, "stages");
+  static_assert(NAD >= 0 && NAD <= Geo<WN>::A_DMA, "A instructions");
   using GEO = Geo<WN>;
   constexpr int STG = GEO::STAGE;
-  constexpr int DMA = GEO::DMA;  // DMA instructions per wave per stage
+  constexpr int DMA = NAD + GEO::B_DMA;  // DMA instructions this wave issues per stage
   constexpr int NA = NL > 0 ? NL : 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -165,7 +166,7 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
     const uint32_t dst = lds_base + stage * STG;
     const char* ab = a_base(kt);
 #pragma unroll
-    for (int i = 0; i < GEO::A_DMA; ++i) dma16(ab, a_off[i], dst + (wave * GEO::A_DMA + i) * 1024);
+    for (int i = 0; i < NAD; ++i) dma16(ab, a_off[i], dst + (wave * GEO::A_DMA + i) * 1024);
 #pragma unroll
     for (int i = 0; i < GEO::B_DMA; ++i)
       dma16(b_base(kt, i), b_off, dst + GEO::A_BYTES + (wave * GEO::B_DMA + i) * 1024);
@@ -223,15 +224,39 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
   }
 }
 
-// Dispatch on this wave's live 32-row sub-tiles (0, 1 or 2) outside the K loop. Every wave
-// takes part in the DMAs and barriers, whatever its live rows.
+// Dispatch outside the K loop on this wave's live 32-row sub-tiles (0, 1 or 2) and on the A
+// instructions it must issue: only those whose 16 rows hold a valid row of the tile (rows of them).
+// A tile rows past `rows` are then never loaded; the LDS holds stale values there, which only
+// reach accumulator rows that are not stored. Every wave takes part in the barriers.
+template <int WN, int S, int NL, class ABase, class BBase>
+__device__ __forceinline__ void mainloop_a(int nad, int nk, lds_char* lds, ABase a_base,
+                                           const uint32_t (&a_off)[Geo<WN>::A_DMA], BBase b_base, uint32_t b_off,
+                                           const int (&bcol)[4], f32x16_t (&acc)[2][4]) {
+  if constexpr (Geo<WN>::A_DMA == 2) {
+    if (nad >= 2) mainloop_v<WN, S, NL, 2>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+    else if (nad == 1) mainloop_v<WN, S, NL, 1>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+    else mainloop_v<WN, S, NL, 0>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  } else {
+    if (nad >= 1) mainloop_v<WN, S, NL, 1>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+    else mainloop_v<WN, S, NL, 0>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  }
+}
+
+// A instructions this wave needs for a tile with `rows` valid rows (instruction q holds rows 16q ..)
+template <int WN>
+__device__ __forceinline__ int needed_a_dma(int rows, int wave) {
+  const int n = (rows + 15) / 16 - wave * Geo<WN>::A_DMA;
+  return n < 0 ? 0 : (n > Geo<WN>::A_DMA ? Geo<WN>::A_DMA : n);
+}
+
 template <int WN, int S, class ABase, class BBase>
-__device__ __forceinline__ void mainloop(int nk, int nl, lds_char* lds, ABase a_base,
+__device__ __forceinline__ void mainloop(int nk, int nl, int rows, lds_char* lds, ABase a_base,
                                          const uint32_t (&a_off)[Geo<WN>::A_DMA], BBase b_base, uint32_t b_off,
                                          const int (&bcol)[4], f32x16_t (&acc)[2][4]) {
-  if (nl >= 2) mainloop_v<WN, S, 2>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
-  else if (nl == 1) mainloop_v<WN, S, 1>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
-  else mainloop_v<WN, S, 0>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  const int nad = needed_a_dma<WN>(rows, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+  if (nl >= 2) mainloop_a<WN, S, 2>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else if (nl == 1) mainloop_a<WN, S, 1>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else mainloop_a<WN, S, 0>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
 }
 
 // this wave's live 32-row sub-tiles (rows 64*wm + {0, 32} of the tile) given the rows left

@@ -43,6 +43,19 @@ def ffn1_algorithmic_bytes(T, d, I, Is, dtype, touched, k):
     return (touched * 2 * d * I + (2 * d * Is if Is else 0)) * s + T * d * s + (T * k * I + T * Is) * s
 
 
+def algorithmic_bytes_fp8(T, d, E, I, Is, touched):
+    """As algorithmic_bytes with e4m3 expert weights (1 byte each) and their fp32 column scales
+    (I + I + d per expert); activations bf16."""
+    w = touched * (expert_params(d, I) + 4 * (2 * I + d)) + ((expert_params(d, Is) + 4 * (2 * Is + d)) if Is else 0)
+    return w + 4 * d * E + 2 * T * d * 2
+
+
+def ffn1_algorithmic_bytes_fp8(T, d, I, Is, touched, k):
+    """Gate/up step with e4m3 weights: codes and scales of W_g, W_u, x in, H out (bf16)."""
+    return (touched * 2 * (d * I + 4 * I) + ((2 * (d * Is + 4 * Is)) if Is else 0)) + T * d * 2 + \
+        (T * k * I + T * Is) * 2
+
+
 def expert_flops(T, d, k, I, Is):
     """Multiply-adds x2 of the routed and shared SwiGLU experts."""
     return 6 * d * (T * k * I + T * Is)

@@ -145,3 +145,38 @@ def test_rmsnorm_rejects_null_gamma():
     dims = moe.MoeDims(4, 64, 8, 2, 32, 0, moe.MOE_BF16, 1)
     rc = lib.moe_rmsnorm(ctypes.byref(dims), ctypes.c_void_p(4096), None, 1e-6, ctypes.c_void_p(4096), None)
     assert rc == 1 and b"gamma" in lib.moe_last_error()  # MOE_ERR_INVALID_ARG
+
+
+def test_fp8_forward_rejects_unsupported_shapes():
+    import sparse_mixture_experts_softmax_amd as moe
+    lib = moe.load_library()
+    args = [None] * 20 + [0, None]
+    for dims in (moe.MoeDims(4, 512, 8, 2, 256, 0, moe.MOE_F32, 1),    # fp32 activations
+                 moe.MoeDims(4, 264, 8, 2, 256, 0, moe.MOE_BF16, 1),   # d % 256 != 0
+                 moe.MoeDims(4, 512, 8, 2, 200, 0, moe.MOE_BF16, 1)):  # I % 128 != 0
+        rc = lib.moe_forward_fp8(ctypes.byref(dims), *args)
+        assert rc == 2 and b"FP8" in lib.moe_last_error()  # MOE_ERR_UNSUPPORTED
+
+
+def test_fp8_quantiser_rejects_bad_arguments():
+    import sparse_mixture_experts_softmax_amd as moe
+    lib = moe.load_library()
+    assert lib.moe_quantize_fp8(None, 7, 1, 16, 16, None, None, None) == 1
+    assert lib.moe_quantize_fp8(None, moe.MOE_BF16, 1, 0, 16, None, None, None) == 1
+    assert lib.moe_quantize_fp8(None, moe.MOE_BF16, 1, 16, 16, None, None, None) == 1  # null w
+    assert lib.moe_quantize_fp8(None, moe.MOE_BF16, 0, 16, 16, None, None, None) == 0  # empty batch
+
+
+def test_binding_argument_lists_match_the_header():
+    # every ctypes argument list has as many entries as the C declaration has parameters
+    import sparse_mixture_experts_softmax_amd as moe
+    lib = moe.load_library()
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    decls = re.findall(r"(?:moe_status|const char\s*\*)\s+(moe_\w+)\s*\(([^)]*)\)\s*;", src)
+    assert decls
+    for name, params in decls:
+        params = params.strip()
+        n = 0 if params in ("", "void") else len(params.split(","))
+        at = getattr(lib, name).argtypes
+        assert at is not None and len(at) == n, (name, n, at)

@@ -376,3 +376,69 @@ def test_router_stats_match_oracle(torch, cfg):
     err = np.max(np.abs(g - rpm))
     assert err <= 1e-5 * rpm.max(), (err, rpm.max())
     _say(cfg.name, "flagged", int((~ok).sum()), "prob_mean max err", err)
+
+
+# --------------------------------------------------------------------------------------------
+# FP8 expert weights: the quantiser bit for bit, the block on the codes against the oracle on
+# the weights they stand for (each side quantises its own copy)
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [syn.F32, syn.BF16])
+def test_fp8_quantiser_matches_oracle_bit_for_bit(torch, dtype):
+    import sparse_mixture_experts_softmax_amd as moe
+    from moe_testlib import to_device
+    rng = np.random.default_rng(51 + dtype)
+    B, K, N = 3, 320, 200
+    w = (rng.standard_normal((B, K, N)) * np.exp2(rng.integers(-14, 6, size=(B, 1, N)))).astype(np.float32)
+    w[1, :, 5] = 0.0
+    w[2, 7, 9] = 1e-30  # a column whose maximum is tiny
+    if dtype == syn.BF16:
+        w = (w.view(np.uint32) >> 16).astype(np.uint16)  # truncation: any bf16 values will do
+    q_ref, s_ref = oracle.quantize_fp8(w)
+    dw = to_device(w, torch.float32 if dtype == syn.F32 else torch.bfloat16)
+    q, s = moe.moe_quantize_fp8(dw)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def _fp8_host_experts(h, cfg):
+    """The oracle's view of FP8 experts: its own quantisation of the bf16 weights, dequantised
+    (exact in bf16)."""
+    def rt(w):
+        if w is None:
+            return None
+        q, s = oracle.quantize_fp8(w)
+        return oracle.dequantize_fp8(q, s)
+    return {key: rt(h[key]) for key in ("wg", "wu", "wd", "wg_s", "wu_s", "wd_s")}
+
+
+FP8_CASES = [
+    syn.MoEConfig("fp8_ragged", T=300, d=512, E=24, k=4, I=256, Is=128, dtype=syn.BF16, seed=61),
+    syn.MoEConfig("fp8_mid_width", T=400, d=2048, E=32, k=8, I=512, Is=512, dtype=syn.BF16, seed=62),
+    syn.MoEConfig("fp8_one_token", T=1, d=2048, E=64, k=4, I=512, Is=256, dtype=syn.BF16, seed=63),
+    syn.MoEConfig("fp8_no_shared", T=129, d=768, E=16, k=3, I=384, Is=0, dtype=syn.BF16, seed=64),
+]
+
+
+@pytest.mark.parametrize("cfg", FP8_CASES, ids=[c.name for c in FP8_CASES])
+def test_fp8_forward_matches_oracle(torch, cfg):
+    import sparse_mixture_experts_softmax_amd as moe
+    _say("case", cfg)
+    h = host_inputs(cfg)
+    dev = device_from_host(h, cfg)
+    experts = moe.Fp8Experts(dev["wg"], dev["wu"], dev["wd"], dev["wg_s"], dev["wu_s"], dev["wd_s"])
+    out, idx, w, gap = moe.moe_forward_fp8(dev["x"], dev["w_router"], experts, cfg.k,
+                                           renormalize=bool(cfg.renorm), router_bias=dev["bias"],
+                                           return_routing=True)
+    out16 = run_forward(dev, cfg)[0]
+    torch.cuda.synchronize()
+    hq = _fp8_host_experts(h, cfg)
+    ref_out, ref_idx, ref_w, ref_gap = oracle.forward(h["x"], h["w_router"], hq["wg"], hq["wu"], hq["wd"], hq["wg_s"],
+                                                      hq["wu_s"], hq["wd_s"], cfg.k, renorm=bool(cfg.renorm),
+                                                      bias=h["bias"])
+    st = compare(cfg, to_host(out), to_host(idx), to_host(w), ref_out, ref_idx, ref_w, ref_gap, cfg.name)
+    # what the format costs (reported, loosely bounded): the FP8 block against the bf16 one
+    o8, o16 = to_host(out).astype(np.float64), to_host(out16).astype(np.float64)
+    qerr = float(np.max(np.abs(o8 - o16)) / np.max(np.abs(o16)))
+    _say(cfg.name, st, "fp8 vs bf16 max rel", qerr)
+    assert qerr < 0.15
