@@ -414,7 +414,7 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          const int row = sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
           if (m0 + row < G.rows)
             __hip_atomic_store(&mine[(G.row0 + m0 + row) * p.part_ld + pcol(j)], acc[i][j][r], __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
@@ -432,7 +432,7 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          const int row = sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
           if (m0 + row < G.rows) {
             const int64_t at = (G.row0 + m0 + row) * p.part_ld + pcol(j);
             float v = 0.f;
@@ -454,7 +454,7 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
         const int col = n0 + wn * 64 + jj * 32 + col_in;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          const int row = sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
           if (m0 + row < G.rows)
             p.out[(G.row0 + m0 + row) * (int64_t)p.ldh + col] =
                 f32_to_bf16(silu_f32(acc[i][jj][r]) * acc[i][jj + 2][r]);
@@ -468,7 +468,7 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
         const int col = n0 + wn * 128 + j * 32 + col_in;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          const int row = sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
           if (m0 + row < G.rows) p.out[(G.row0 + m0 + row) * (int64_t)p.d + col] = f32_to_bf16(acc[i][j][r]);
         }
       }

@@ -11,8 +11,8 @@
 // scale is applied to the fp32 accumulator in the epilogue. Half the weight bytes of bf16: the
 // decode shapes, bound by streaming the touched experts' weights, move half as much.
 //
-// Tile: 128 x 256 (four wavefronts, wavefront w owning rows 64*(w/2) .. +64 and columns
-// 128*(w%2) .. +128), K step 32, S stages of 8 KB of A (bf16) + 8 KB of B (e4m3), two workgroups
+// Tile: 128 x 256 (four wavefronts, wavefront w owning the 32-row sub-tiles w/2 and 2 + w/2 and
+// columns 128*(w%2) .. +128), K step 32, S stages of 8 KB of A (bf16) + 8 KB of B (e4m3), two workgroups
 // per CU. Schedule, DMA and the A operand as in stream_gemm.h.
 //   B tile [256 columns][32 K] bytes, 32 B per column: the 16-byte chunk h of column r sits at
 //   slot h ^ ((r >> 3) & 1). B instruction q (0..7; wave w issues 2w, 2w+1) loads columns 32q ..
@@ -83,7 +83,7 @@ __device__ __forceinline__ void mainloop_f8(int nk, lds_char* lds, ABase a_base,
   auto read = [&](const lds_char* st, int s, bf16x8_t (&a)[NA], bf16x8_t (&b)[4]) {
     if constexpr (NL > 0) {
 #pragma unroll
-      for (int u = 0; u < NL; ++u) a[u] = read_a(st, wm * 64 + u * 32 + (lane & 31), 2 * s + (lane >> 5));
+      for (int u = 0; u < NL; ++u) a[u] = read_a(st, sub_row(wm, u) + (lane & 31), 2 * s + (lane >> 5));
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = read_b_f8(st + F8_A_BYTES, bcol[j] + (lane & 31), s, lane >> 5);
     }
@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(256, 2) ffn_fp8_stream_kernel(Fp8Args p) {
         const float sg = S0[col], su = S1[col];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          const int row = sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
           if (m0 + row < G.rows)
             p.out[(G.row0 + m0 + row) * (int64_t)p.ldh + col] =
                 f32_to_bf16(silu_f32(acc[i][jj][r] * sg) * (acc[i][jj + 2][r] * su));
@@ -261,7 +261,7 @@ __global__ void __launch_bounds__(256, 2) ffn_fp8_stream_kernel(Fp8Args p) {
         const float sd = S0[col];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          const int row = sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
           if (m0 + row < G.rows) p.out[(G.row0 + m0 + row) * (int64_t)p.d + col] = f32_to_bf16(acc[i][j][r] * sd);
         }
       }

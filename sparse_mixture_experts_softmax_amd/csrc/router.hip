@@ -112,7 +112,7 @@ router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ plan
       const int e = e0 + wn * 128 + j * 32 + col_in;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t t = t0 + wm * 64 + i * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+        const int64_t t = t0 + sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
         if (t < T) out[t * E + e] = acc[i][j][r];
       }
     }

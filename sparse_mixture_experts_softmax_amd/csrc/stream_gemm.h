@@ -2,8 +2,9 @@
 // router GEMM.
 //
 // One workgroup of 2*WN wavefronts accumulates a 128 x (128*WN) fp32 tile
-// acc += A[128 x K] * B[K x 128*WN] with v_mfma_f32_32x32x16_bf16. Wavefront w owns rows
-// 64*(w / WN) .. +64 and columns 128*(w % WN) .. +128 (2 x 4 sub-tiles of 32 x 32). WN = 2 gives a
+// acc += A[128 x K] * B[K x 128*WN] with v_mfma_f32_32x32x16_bf16. Wavefront w, in wave row
+// wm = w / WN, owns the 32-row sub-tiles wm and 2 + wm (rows 32*wm .. +32 and 64 + 32*wm .. +32)
+// and columns 128*(w % WN) .. +128: 2 x 4 sub-tiles of 32 x 32. WN = 2 gives a
 // 128 x 256 tile of four wavefronts (two workgroups per CU); WN = 4 a 128 x 512 tile of eight (one
 // workgroup per CU, two wavefronts per SIMD, more of the CU's LDS in flight per FLOP).
 //
@@ -56,6 +57,16 @@ struct Geo {
   static constexpr int B_DMA = B_BYTES / 1024 / NW;  // B DMA instructions per wave per stage
   static constexpr int DMA = A_DMA + B_DMA;
 };
+
+// First row of sub-tile u (0 or 1) of wave row wm (0 or 1). The two wave rows take the tile's
+// 32-row sub-tiles in turn (wave row wm: sub-tiles wm and 2 + wm), so the live rows of a partly
+// filled tile spread over both and over the CU's SIMDs.
+__device__ __forceinline__ int sub_row(int wm, int u) { return (2 * u + wm) * 32; }
+
+// this wave row's live 32-row sub-tiles (0, 1 or 2; a prefix in u) given the rows left
+__device__ __forceinline__ int live_subtiles(int rows_left, int wm) {
+  return (sub_row(wm, 0) < rows_left) + (sub_row(wm, 1) < rows_left);
+}
 
 // A-tile row loaded by this lane's i-th A DMA instruction, and the lane's byte offset inside
 // that row (16-byte chunk, swizzled)
@@ -175,7 +186,7 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
   auto read = [&](const lds_char* st, int s, bf16x8_t (&a)[NA], bf16x8_t (&b)[4]) {
     if constexpr (NL > 0) {
 #pragma unroll
-      for (int u = 0; u < NL; ++u) a[u] = read_a(st, wm * 64 + u * 32 + (lane & 31), 2 * s + (lane >> 5));
+      for (int u = 0; u < NL; ++u) a[u] = read_a(st, sub_row(wm, u) + (lane & 31), 2 * s + (lane >> 5));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kb = 16 * s + 8 * (g16 >> 1) + (i16 >> 2);
@@ -259,10 +270,6 @@ __device__ __forceinline__ void mainloop(int nk, int nl, int rows, lds_char* lds
   else mainloop_a<WN, S, 0>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
 }
 
-// this wave's live 32-row sub-tiles (rows 64*wm + {0, 32} of the tile) given the rows left
-__device__ __forceinline__ int live_subtiles(int rows_left, int wm) {
-  return (wm * 64 < rows_left) + (wm * 64 + 32 < rows_left);
-}
 
 __device__ __forceinline__ void zero(f32x16_t (&acc)[2][4]) {
 #pragma unroll
