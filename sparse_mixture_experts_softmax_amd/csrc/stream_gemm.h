@@ -172,6 +172,11 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
   const int g16 = lane >> 4;
   const int i16 = lane & 15;
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  // With eight wavefronts (two per SIMD) the second wavefront of each SIMD issues its DMAs after
+  // its second sub-step's MFMAs rather than right after the barrier, so that the two do not both
+  // stall on DMA issue while the SIMD's matrix unit idles. The stage is free from the barrier on,
+  // and the DMAs still go out before the wave's next wait.
+  const bool late = GEO::NW == 8 && wave >= 4;
 
   auto issue = [&](int kt, int stage) {
     const uint32_t dst = lds_base + stage * STG;
@@ -226,11 +231,12 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
       // stage kt+1 complete once at most the DMAs of k-steps kt+2 .. kt+S-1 are outstanding
       wait_groups<DMA>(min(S - 2, nk - kt - 2));
       barrier_after_lds_reads();
-      if (kt + S < nk) issue(kt + S, stage);
+      if (!late && kt + S < nk) issue(kt + S, stage);
       read(lds + next * STG, 0, a0, b0);
     }
     mma(a1, b1);
     __builtin_amdgcn_sched_barrier(0);
+    if (late && kt + S < nk) issue(kt + S, stage);
     stage = next;
   }
 }

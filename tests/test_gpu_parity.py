@@ -417,6 +417,9 @@ FP8_CASES = [
     syn.MoEConfig("fp8_mid_width", T=400, d=2048, E=32, k=8, I=512, Is=512, dtype=syn.BF16, seed=62),
     syn.MoEConfig("fp8_one_token", T=1, d=2048, E=64, k=4, I=512, Is=256, dtype=syn.BF16, seed=63),
     syn.MoEConfig("fp8_no_shared", T=129, d=768, E=16, k=3, I=384, Is=0, dtype=syn.BF16, seed=64),
+    # few tokens: 32-row tiles (T <= 32; the shared expert fills one) and 64-row tiles (T <= 64)
+    syn.MoEConfig("fp8_T32", T=32, d=2048, E=64, k=6, I=512, Is=512, dtype=syn.BF16, seed=65),
+    syn.MoEConfig("fp8_T48", T=48, d=1024, E=32, k=4, I=256, Is=384, dtype=syn.BF16, seed=66),
 ]
 
 
