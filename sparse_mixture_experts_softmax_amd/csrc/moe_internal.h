@@ -71,6 +71,7 @@ Layout make_layout(const moe_dims& dm);
 // columns), column tiles and K splits of the gate/up and of the down product.
 struct FfnPlan {
   bool stream;
+  bool balance;  // equal row tiles per group
   int wn1, wn2;
   int nt1, nt2;
   int s1, s2;

@@ -87,6 +87,8 @@ SMALL_CASES = [
     # tiles with a shared expert narrower than the routed ones)
     ("split_k_T1", 1, 2048, 64, 4, 1024, 1024, syn.BF16, 1, 0.0),
     ("split_k_T3", 3, 4096, 32, 6, 512, 256, syn.BF16, 1, 0.0),
+    # equal row tiles (<= 192 rows per expert on average) under Zipf-skewed loads of ~50 .. ~650 rows
+    ("balanced_tiles_skewed", 700, 512, 16, 4, 256, 128, syn.BF16, 1, 0.8),
 ]
 
 
