@@ -150,18 +150,23 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_route
 /* FP8 expert weights (the Fondations page of the Qwen3.8-Max report names FP8 among the formats
  * and gives no scheme; this is the one used): weight-only OCP e4m3 (bias 7, 3 mantissa bits,
  * largest finite 448), one power-of-two fp32 scale per output column, codes by round to nearest
- * with ties to even, stored K-contiguous:
+ * with ties to even:
  *   W[k, n] = e4m3(Q[n, k]) * s[n]
  *
  * moe_quantize_fp8: w [batch, K, N] (dtype, N-contiguous as the bf16 expert weights are stored)
- *   -> q [batch, N, K] uint8 codes, scale [batch, N] float; s[n] is the smallest power of two with
- *   max_k |w[k, n]| / s[n] <= 448 (1 for an all-zero column). batch <= 65535. */
+ *   -> q: batch x K*N uint8 codes in code tiles, scale [batch, N] float; s[n] is the smallest
+ *   power of two with max_k |w[k, n]| / s[n] <= 448 (1 for an all-zero column).
+ *   Code tiles: 128 columns x 32 K values, 4096 bytes, ordered by (column tile, K tile), i.e.
+ *   tile (n / 128) * (K / 32) + k / 32 of each matrix. In a tile, with r = n % 128,
+ *   j = k % 32, h = j / 16: Q[n, k] is byte 32 r + 16 (h ^ ((r / 8) % 2)) + j % 16.
+ *   K % 32 == 0 and N % 128 == 0, else MOE_ERR_UNSUPPORTED; q 16-byte aligned; batch <= 65535. */
 moe_status moe_quantize_fp8(const void* w, int32_t dtype, int64_t batch, int32_t K, int32_t N, uint8_t* q,
                             float* scale, hipStream_t stream);
 
-/* moe_forward with FP8 expert weights (moe_quantize_fp8 layout): wg, wu [E, I, d] codes with sg, su
- * [E, I]; wd [E, d, I] with sd [E, d]; the shared expert wg_s, wu_s [I_shared, d], wd_s
- * [d, I_shared] with sg_s, su_s [I_shared], sd_s [d]. x, out bf16 (dims.dtype = MOE_BF16);
+/* moe_forward with FP8 expert weights (moe_quantize_fp8 layout): wg, wu codes of [E] matrices
+ * with K = d, N = I and scales sg, su [E, I]; wd codes of [E] matrices with K = I, N = d and sd
+ * [E, d]; the shared expert likewise (wg_s, wu_s: K = d, N = I_shared; wd_s: K = I_shared,
+ * N = d) with sg_s, su_s [I_shared], sd_s [d]. x, out bf16 (dims.dtype = MOE_BF16);
  * d % 256 == 0 and I, I_shared % 128 == 0, else MOE_ERR_UNSUPPORTED. The products run on the bf16
  * MFMA with the codes widened exactly; the column scales are applied to the fp32 sums. */
 moe_status moe_forward_fp8(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,

@@ -260,13 +260,14 @@ def moe_router_topk_stats(dims, x, w_router, router_bias=None, ws=None):
 
 
 def moe_quantize_fp8(w):
-    """FP8 (e4m3) codes and column scales of w [..., K, N] (float32 or bfloat16, N-contiguous).
-    Returns (q uint8 [..., N, K], scale float32 [..., N])."""
+    """FP8 (e4m3) codes and column scales of w [..., K, N] (float32 or bfloat16, N-contiguous;
+    K % 32 == 0, N % 128 == 0). Returns (q uint8 [..., N // 128, K // 32, 4096]: the code tiles of
+    moe.h, scale float32 [..., N])."""
     import torch
     lib = load_library()
     K, N = w.shape[-2], w.shape[-1]
     batch = w.numel() // (K * N) if w.numel() else 0
-    q = torch.empty(w.shape[:-2] + (N, K), dtype=torch.uint8, device=w.device)
+    q = torch.empty(w.shape[:-2] + (N // 128, K // 32, 4096), dtype=torch.uint8, device=w.device)
     s = torch.empty(w.shape[:-2] + (N,), dtype=torch.float32, device=w.device)
     _check(lib.moe_quantize_fp8(_ptr(w), _dtype_code(w), batch, K, N, _ptr(q), _ptr(s), _stream(w)))
     return q, s
@@ -285,7 +286,7 @@ class Fp8Experts:
             self.wd_s, self.sd_s = moe_quantize_fp8(wd_s)
         else:
             self.wg_s = self.sg_s = self.wu_s = self.su_s = self.wd_s = self.sd_s = None
-        self.E, self.I, self.d = self.wg.shape
+        self.E, self.d, self.I = wg.shape
         self.I_shared = 0 if wg_s is None else wg_s.shape[1]
 
 

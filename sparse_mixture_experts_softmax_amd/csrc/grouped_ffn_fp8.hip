@@ -5,18 +5,23 @@
 //
 //   W[k, n] = e4m3(Q[n, k]) * s[n]      so   (A W)[m, n] = s[n] * sum_k A[m, k] e4m3(Q[n, k])
 //
-// The codes are stored K-contiguous ([N, K] per matrix), so the MFMA B operand (8 consecutive K
-// values of one column per lane) is a plain 8-byte LDS read; each e4m3 value is exact in bf16, so
-// the codes are widened to bf16 in registers and the product runs on the bf16 MFMA. The column
-// scale is applied to the fp32 accumulator in the epilogue. Half the weight bytes of bf16: the
-// decode shapes, bound by streaming the touched experts' weights, move half as much.
+// Code layout (per matrix of N columns and K rows; N % 128 == 0, K % 32 == 0): tiles of 128
+// columns x 32 K values, 4 KB each, ordered (column tile, K tile), so the codes of one 128-column
+// panel are one contiguous stream of K / 32 tiles. Inside a tile, column r holds its 32 K values
+// at bytes 32 r .. 32 r + 31, K-contiguous, as two 16-byte halves; half h (K 16h .. 16h+15) sits
+// at slot h ^ ((r >> 3) & 1). A tile is thus byte for byte the LDS image the kernel reads, and
+// the DMA copies 1 KB runs of it. The MFMA B operand (8 consecutive K values of one column per
+// lane) is a plain 8-byte LDS read; each e4m3 value is exact in bf16, so the codes are widened to
+// bf16 in registers and the product runs on the bf16 MFMA. The column scale is applied to the
+// fp32 accumulator in the epilogue. Half the weight bytes of bf16: the decode shapes, bound by
+// streaming the touched experts' weights, move half as much. (Stored plainly K-contiguous, one
+// 32-byte run per column and K step, the same kernel ran 12 % slower at decode.)
 //
 // Tile: 128 x 256 (four wavefronts, wavefront w owning the 32-row sub-tiles w/2 and 2 + w/2 and
-// columns 128*(w%2) .. +128), K step 32, S stages of 8 KB of A (bf16) + 8 KB of B (e4m3), two workgroups
-// per CU. Schedule, DMA and the A operand as in stream_gemm.h.
-//   B tile [256 columns][32 K] bytes, 32 B per column: the 16-byte chunk h of column r sits at
-//   slot h ^ ((r >> 3) & 1). B instruction q (0..7; wave w issues 2w, 2w+1) loads columns 32q ..
-//   32q+31: lane l takes column 32q + l/2, chunk (l & 1) ^ (((32q + l/2) >> 3) & 1).
+// columns 128*(w%2) .. +128), K step 32, S stages of 8 KB of A (bf16) + 8 KB of B (e4m3), two
+// workgroups per CU. Schedule, DMA and the A operand as in stream_gemm.h. The B stage holds two
+// code tiles (gate and up at the same columns, or two adjacent column tiles of W_d); B instruction
+// q (0..7; wave w issues 2w, 2w+1) copies bytes 1024 (q % 4) .. +1023 of tile q / 4, 16 per lane.
 #include "moe_internal.h"
 #include "stream_gemm.h"
 
@@ -200,20 +205,16 @@ __global__ void __launch_bounds__(256, 2) ffn_fp8_stream_kernel(Fp8Args p) {
   const char* a_src = uniform_ptr((const char*)p.a_src);
   auto a_base = [=](int kt) { return a_src + kt * (SBK * 2); };
 
-  // B: instruction q = 2*wave + i loads tile columns 32q .. +31 (K-contiguous code rows of K bytes);
-  // for gate/up, tile columns [0, 128) are W_g rows n0 .., [128, 256) W_u rows n0 ..
+  // B: waves 0-1 stream the 128-column code panel of tile columns [0, 128), waves 2-3 that of
+  // [128, 256): for gate/up the W_g and the W_u panel at columns n0 .., for the down product the
+  // panels at n0 and n0 + 128. A panel is K / 32 tiles of 4 KB, one per K step.
   const uint8_t* bmat = (GATED && wave >= 2) ? W1 : W0;
-  const int col0 = GATED ? 32 * (2 * wave) - (wave >= 2 ? 128 : 0) : 32 * (2 * wave);  // first column, this wave
-  const char* b0 = uniform_ptr((const char*)bmat + ((int64_t)n0 + col0) * K);
+  const int panel = n0 / 128 + (!GATED && wave >= 2 ? 1 : 0);
+  const char* b0 = uniform_ptr((const char*)bmat + (int64_t)panel * K * 128 + ((2 * wave) & 3) * 1024);
   uint32_t b_off[F8_B_DMA];
 #pragma unroll
-  for (int i = 0; i < F8_B_DMA; ++i) {
-    const int r = 32 * i + (lane >> 1);          // column within this wave's 64
-    const int tile_col = 32 * (2 * wave + i) + (lane >> 1);
-    const int chunk = (lane & 1) ^ ((tile_col >> 3) & 1);
-    b_off[i] = (uint32_t)(r * K + 16 * chunk);
-  }
-  auto b_base = [=](int kt, int) { return b0 + kt * SBK; };
+  for (int i = 0; i < F8_B_DMA; ++i) b_off[i] = (uint32_t)(i * 1024 + 16 * lane);
+  auto b_base = [=](int kt, int) { return b0 + (int64_t)kt * 4096; };
 
   int bcol[4];
 #pragma unroll
@@ -269,7 +270,7 @@ __global__ void __launch_bounds__(256, 2) ffn_fp8_stream_kernel(Fp8Args p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// quantiser: w [batch, K, N] -> codes [batch, N, K], scales [batch, N]
+// quantiser: w [batch, K, N] -> codes [batch] x (N / 128 x K / 32 tiles of 4 KB), scales [batch, N]
 // ------------------------------------------------------------------------------------------
 // nearest e4m3 code of v (|v| <= 448), ties to even, by rounding exactly scaled values to integers
 __device__ __forceinline__ uint8_t e4m3_rne(float v) {
@@ -308,8 +309,10 @@ __device__ __forceinline__ float wval<float>(const float* p, int64_t i) { return
 template <>
 __device__ __forceinline__ float wval<bf16_t>(const bf16_t* p, int64_t i) { return bf16lo_to_f32(p[i]); }
 
-// grid (ceil(N / 64), batch); 256 threads. Pass 1: column maxima (thread: column tid % 64, rows
-// tid / 64 + 4i). Pass 2: 64 x 64 blocks through LDS, written K-contiguous.
+// grid (N / 64, batch); 256 threads; N % 128 == 0, K % 32 == 0. Pass 1: column maxima (thread:
+// column tid % 64, rows tid / 64 + 4i). Pass 2: 64 x 64 blocks through LDS; each thread rounds 16
+// K-consecutive values of one column and stores them as one 16-byte half of the column's run in
+// its code tile.
 template <typename WT>
 __global__ void __launch_bounds__(256)
 quantize_fp8_kernel(const WT* __restrict__ w, int K, int N, uint8_t* __restrict__ q, float* __restrict__ scale) {
@@ -323,15 +326,14 @@ quantize_fp8_kernel(const WT* __restrict__ w, int K, int N, uint8_t* __restrict_
   const int64_t b = blockIdx.y;
   const WT* wb = w + b * (int64_t)K * N;
   float amax = 0.f;
-  if (n < N)
-    for (int k = r0; k < K; k += 4) amax = fmaxf(amax, fabsf(wval(wb, (int64_t)k * N + n)));
+  for (int k = r0; k < K; k += 4) amax = fmaxf(amax, fabsf(wval(wb, (int64_t)k * N + n)));
   red[r0][c] = amax;
   __syncthreads();
   if (r0 == 0) {
     const float m = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
     const int e = scale_exp(m);
     sexp[c] = e;
-    if (n < N) scale[b * N + n] = ldexpf(1.0f, e);
+    scale[b * N + n] = ldexpf(1.0f, e);
   }
   __syncthreads();
   uint8_t* qb = q + b * (int64_t)N * K;
@@ -339,17 +341,23 @@ quantize_fp8_kernel(const WT* __restrict__ w, int K, int N, uint8_t* __restrict_
     for (int i = tid; i < 64 * 64; i += 256) {
       const int kk = i / 64, cc = i % 64;
       const int nn = blockIdx.x * 64 + cc;
-      tile[kk][cc] = (k0 + kk < K && nn < N) ? wval(wb, (int64_t)(k0 + kk) * N + nn) : 0.f;
+      tile[kk][cc] = k0 + kk < K ? wval(wb, (int64_t)(k0 + kk) * N + nn) : 0.f;
     }
     __syncthreads();
     // thread: column tid / 4, K values 16 * (tid % 4) .. +16 of the block
     const int cc = tid >> 2;
-    const int kq = (tid & 3) * 16;
-    const int nn = blockIdx.x * 64 + cc;
-    if (nn < N) {
+    const int kk = k0 + (tid & 3) * 16;
+    if (kk < K) {
+      const int nn = blockIdx.x * 64 + cc;
       const int e = sexp[cc];
+      uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (k0 + kq + i < K) qb[(int64_t)nn * K + k0 + kq + i] = e4m3_rne(ldexpf(tile[kq + i][cc], -e));
+        wd[i >> 2] |= (uint32_t)e4m3_rne(ldexpf(tile[kk - k0 + i][cc], -e)) << (8 * (i & 3));
+      const int r = nn & 127;
+      const int h = (kk >> 4) & 1;
+      const int64_t at = ((int64_t)(nn >> 7) * (K >> 5) + (kk >> 5)) * 4096 + r * 32 + 16 * (h ^ ((r >> 3) & 1));
+      *(uint4*)(qb + at) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
     __syncthreads();
   }
@@ -360,8 +368,7 @@ quantize_fp8_kernel(const WT* __restrict__ w, int K, int N, uint8_t* __restrict_
 bool fp8_shape_ok(const moe_dims& dm) {
   return dm.dtype == MOE_BF16 && dm.d % 256 == 0 && dm.I % 128 == 0 && dm.I_shared % 128 == 0 &&
          (uint64_t)dm.T * dm.d * 2 < (1ull << 32) &&
-         (uint64_t)(dm.T * dm.k + dm.T) * (dm.I > dm.I_shared ? dm.I : dm.I_shared) * 2 < (1ull << 32) &&
-         (uint64_t)dm.d * (dm.I > dm.I_shared ? dm.I : dm.I_shared) < (1ull << 32);
+         (uint64_t)(dm.T * dm.k + dm.T) * (dm.I > dm.I_shared ? dm.I : dm.I_shared) * 2 < (1ull << 32);
 }
 
 hipError_t launch_grouped_ffn_fp8(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
@@ -425,7 +432,7 @@ hipError_t launch_grouped_ffn_fp8(const moe_dims& dm, const Layout& L, const voi
 
 hipError_t launch_quantize_fp8(const void* w, int dtype, int64_t batch, int K, int N, uint8_t* q, float* scale,
                                hipStream_t s) {
-  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)batch);
+  const dim3 grid((unsigned)(N / 64), (unsigned)batch);
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(quantize_fp8_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)w, K, N, q, scale);
   else

@@ -439,8 +439,10 @@ moe_status moe_quantize_fp8(const void* w, int32_t dtype, int64_t batch, int32_t
     return fail(MOE_ERR_INVALID_ARG, "batch = %lld (0 .. 65535), K = %d, N = %d (>= 1)", (long long)batch, K, N);
   if (batch == 0) return MOE_OK;
   MOE_TRY(check_ptr(w, dtype == MOE_BF16 ? 2 : 4, "w"));
-  MOE_TRY(check_ptr(q, 1, "q"));
+  MOE_TRY(check_ptr(q, 16, "q"));
   MOE_TRY(check_ptr(scale, 4, "scale"));
+  if (K % 32 || N % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 code tiles need K %% 32 == 0 and N %% 128 == 0 (K = %d, N = %d)", K, N);
   hipError_t e = launch_quantize_fp8(w, dtype, batch, K, N, q, scale, stream);
   if (e != hipSuccess) return hip_fail(e, "moe_quantize_fp8");
   return MOE_OK;

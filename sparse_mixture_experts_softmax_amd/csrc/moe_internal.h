@@ -146,9 +146,10 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
 int ffn_tile_rows(const moe_dims& dm);
 hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s);
 
-// FP8 (e4m3) expert weights: K-contiguous codes [.., N, K] with one fp32 scale per output column
+// FP8 (e4m3) expert weights: codes in 4 KB tiles of 128 columns x 32 K values (moe_quantize_fp8
+// layout) with one fp32 scale per output column
 struct Fp8Weights {
-  const uint8_t *wg, *wu, *wd;      // [E, I, d], [E, I, d], [E, d, I]
+  const uint8_t *wg, *wu, *wd;      // per expert d*I bytes each: W_g, W_u (N = I, K = d), W_d (N = d, K = I)
   const float *sg, *su, *sd;        // [E, I], [E, I], [E, d]
   const uint8_t *wg_s, *wu_s, *wd_s;  // [I_s, d], [I_s, d], [d, I_s]
   const float *sg_s, *su_s, *sd_s;    // [I_s], [I_s], [d]

@@ -38,6 +38,18 @@ def to_host(t):
     return t.cpu().numpy()
 
 
+def fp8_untile(q, N, K):
+    """FP8 code tiles (moe.h layout: tile (n // 128) * (K // 32) + k // 32 of 4096 bytes; in a tile
+    Q[n, k] at byte 32 r + 16 (h ^ ((r // 8) % 2)) + k % 16 with r = n % 128, h = (k % 32) // 16)
+    back to plain codes [..., N, K]."""
+    q = np.asarray(q).reshape(q.shape[:-3] + (-1,)) if q.ndim >= 3 else np.asarray(q)
+    n = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    r, h = n % 128, (k % 32) // 16
+    at = ((n // 128) * (K // 32) + k // 32) * 4096 + 32 * r + 16 * (h ^ ((r // 8) % 2)) + k % 16
+    return q[..., at]
+
+
 def host_inputs(cfg):
     """All inputs on the host (small configs): dict of numpy arrays in the config's dtype."""
     wg, wu, wd = syn.host_all_experts(cfg)

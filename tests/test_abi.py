@@ -165,6 +165,22 @@ def test_fp8_quantiser_rejects_bad_arguments():
     assert lib.moe_quantize_fp8(None, moe.MOE_BF16, 1, 0, 16, None, None, None) == 1
     assert lib.moe_quantize_fp8(None, moe.MOE_BF16, 1, 16, 16, None, None, None) == 1  # null w
     assert lib.moe_quantize_fp8(None, moe.MOE_BF16, 0, 16, 16, None, None, None) == 0  # empty batch
+    p = ctypes.c_void_p(FAKE)  # never dereferenced: the shape check fails first
+    assert lib.moe_quantize_fp8(p, moe.MOE_BF16, 1, 48, 128, p, p, None) == UNSUPPORTED  # K % 32
+    assert lib.moe_quantize_fp8(p, moe.MOE_BF16, 1, 64, 192, p, p, None) == UNSUPPORTED  # N % 128
+    assert lib.moe_quantize_fp8(p, moe.MOE_BF16, 1, 64, 128, ctypes.c_void_p(FAKE + 8), p, None) == INVALID  # q align
+
+
+def test_fp8_untile_is_a_permutation():
+    from moe_testlib import fp8_untile
+    import numpy as np
+    N, K = 256, 96
+    flat = np.arange(N * K, dtype=np.int64)
+    u = fp8_untile(flat.reshape(N // 128, K // 32, 4096), N, K)
+    assert u.shape == (N, K) and np.array_equal(np.sort(u.ravel()), flat)
+    # each tile's column run is 32 contiguous bytes; within a tile, columns follow each other
+    assert np.array_equal(np.sort(u[5, :32]), np.arange(5 * 32, 6 * 32))
+    assert u[130, 40] // 4096 == 1 * (K // 32) + 1
 
 
 def test_binding_argument_lists_match_the_header():
