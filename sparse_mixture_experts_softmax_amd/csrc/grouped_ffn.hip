@@ -40,41 +40,12 @@ __global__ void __launch_bounds__(1024)
 build_tiles_kernel(const int32_t* __restrict__ offsets, int64_t T, int E, int has_shared, int BM,
                    int32_t* __restrict__ tile_group, int32_t* __restrict__ tile_m0, int32_t* __restrict__ tile_count,
                    int32_t* __restrict__ split_cnt, int64_t n_cnt) {
+  __shared__ int s_rows[kMaxGroups];
   __shared__ int s_val[2048];
   __shared__ int s_tmp[1024];
-  const int tid = threadIdx.x;
-  for (int64_t i = tid; i < n_cnt; i += 1024) split_cnt[i] = 0;  // split-K arrival counters
   const int G = E + has_shared;
-  for (int g = tid; g < G; g += 1024) {
-    const int64_t n = g < E ? (int64_t)(offsets[g + 1] - offsets[g]) : T;
-    s_val[g] = (int)((n + BM - 1) / BM);
-  }
-  __syncthreads();
-  // exclusive scan of G <= 1025 values, two per thread
-  const int a = 2 * tid < G ? s_val[2 * tid] : 0;
-  const int b = 2 * tid + 1 < G ? s_val[2 * tid + 1] : 0;
-  s_tmp[tid] = a + b;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? s_tmp[tid - off] : 0;
-    __syncthreads();
-    s_tmp[tid] += v;
-    __syncthreads();
-  }
-  const int excl = s_tmp[tid] - (a + b);
-  const int starts[2] = {excl, excl + a};
-  const int cnts[2] = {a, b};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int g = 2 * tid + h;
-    if (g < G) {
-      for (int i = 0; i < cnts[h]; ++i) {
-        tile_group[starts[h] + i] = g;
-        tile_m0[starts[h] + i] = i * BM;
-      }
-    }
-  }
-  if (tid == 1023) *tile_count = s_tmp[1023];
+  for (int g = threadIdx.x; g < G; g += 1024) s_rows[g] = g < E ? offsets[g + 1] - offsets[g] : (int)T;
+  build_tile_list(s_rows, G, BM, s_val, s_tmp, tile_group, tile_m0, tile_count, split_cnt, n_cnt);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -680,7 +651,7 @@ FfnPlan ffn_plan(const moe_dims& dm) {
 hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
                               const int32_t* sorted_token, const void* wg, const void* wu, const void* wd,
                               const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
-                              hipStream_t s, const Prof* prof) {
+                              hipStream_t s, const Prof* prof, bool tiles_ready) {
   const Prof none;
   if (!prof) prof = &none;
   int32_t* tg = (int32_t*)(ws + L.tile_group);
@@ -691,8 +662,8 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
   const bool stream_ok = P.stream;
   const int bm = ffn_tile_rows(dm);
   int32_t* cnt = (int32_t*)(ws + L.ffn_cnt);
-  hipError_t e = launch_build_tiles(dm, L, offsets, ws, s);
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (!tiles_ready && (e = launch_build_tiles(dm, L, offsets, ws, s)) != hipSuccess) return e;
 
   // upper bound on row tiles: sum over non-empty groups of ceil(n_g / bm) <= (T*k)/bm + (routed
   // groups with rows, at most min(E, T*k)) + T/bm + 1 for the shared expert

@@ -348,13 +348,13 @@ moe_status forward_rows(const moe_dims& dm, const Layout& L, const void* xin, co
   if (e != hipSuccess) return hip_fail(e, "moe_forward/router");
   if ((e = prof.end(MOE_KERNEL_ROUTER, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
   if ((e = prof.begin(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
-  e = launch_permute(dm, L, idx, offsets, sorted, slot, w, stream);
+  e = launch_permute(dm, L, idx, offsets, sorted, slot, w, stream, !fp8);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/permute");
   if ((e = prof.end(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
   if (fp8)
     e = launch_grouped_ffn_fp8(dm, L, xin, offsets, sorted, *fp8, y, w, stream, &prof);
   else
-    e = launch_grouped_ffn(dm, L, xin, offsets, sorted, wg, wu, wd, wg_s, wu_s, wd_s, y, w, stream, &prof);
+    e = launch_grouped_ffn(dm, L, xin, offsets, sorted, wg, wu, wd, wg_s, wu_s, wd_s, y, w, stream, &prof, true);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/grouped_ffn");
   if ((e = prof.begin(MOE_KERNEL_COMBINE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
   e = launch_combine(dm, y, slot, tw, residual, out, stream);

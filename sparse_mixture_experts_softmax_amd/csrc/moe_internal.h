@@ -39,6 +39,7 @@ constexpr int kRouterTileT = 64;       // router logits tile: tokens
 constexpr int kRouterTileE = 64;       // router logits tile: experts
 constexpr int kRouterKStep = 16;       // router K step
 constexpr int kMaxK = 16;              // largest k (experts per token) accepted
+constexpr int kMaxGroups = 1025;       // grouped GEMM groups: up to 1024 experts + the shared one
 constexpr int kMfmaBM = 128;           // bf16 grouped GEMM tile rows
 constexpr int kMfmaBN1 = 128;          // gate/up tile: intermediate columns (x2 for gate and up)
 constexpr int kMfmaBN2 = 256;          // down tile: hidden columns
@@ -121,6 +122,43 @@ __device__ __forceinline__ Group group_info(int g, const int32_t* offsets, int64
   return G;
 }
 
+// Row-tile list of the grouped GEMMs: group g with s_rows[g] rows gets ceil(rows / BM) tiles,
+// listed group after group as (group, first row). One workgroup of 1024 threads; s_rows,
+// s_val[2048] and s_tmp[1024] are LDS arrays (G <= 2048 groups). Also zeroes the split-K
+// arrival counters.
+__device__ inline void build_tile_list(const int* s_rows, int G, int BM, int* s_val, int* s_tmp,
+                                       int32_t* tile_group, int32_t* tile_m0, int32_t* tile_count,
+                                       int32_t* split_cnt, int64_t n_cnt) {
+  const int tid = threadIdx.x;
+  for (int64_t i = tid; i < n_cnt; i += 1024) split_cnt[i] = 0;
+  for (int g = tid; g < G; g += 1024) s_val[g] = (s_rows[g] + BM - 1) / BM;
+  __syncthreads();
+  // exclusive scan of the tile counts, two per thread
+  const int a = 2 * tid < G ? s_val[2 * tid] : 0;
+  const int b = 2 * tid + 1 < G ? s_val[2 * tid + 1] : 0;
+  s_tmp[tid] = a + b;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? s_tmp[tid - off] : 0;
+    __syncthreads();
+    s_tmp[tid] += v;
+    __syncthreads();
+  }
+  const int excl = s_tmp[tid] - (a + b);
+  const int starts[2] = {excl, excl + a};
+  const int cnts[2] = {a, b};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int g = 2 * tid + h;
+    if (g < G)
+      for (int i = 0; i < cnts[h]; ++i) {
+        tile_group[starts[h] + i] = g;
+        tile_m0[starts[h] + i] = i * BM;
+      }
+  }
+  if (tid == 1023) *tile_count = s_tmp[1023];
+}
+
 // ------------------------------------------------------------------------------------------
 // launchers (enqueue only; return hipSuccess or the launch error)
 // ------------------------------------------------------------------------------------------
@@ -133,13 +171,15 @@ hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, con
 hipError_t launch_router_stats(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, char* ws,
                                int32_t* counts, float* prob_mean, hipStream_t s);
 
+// with_tiles: the scan also writes the grouped GEMM's tile list (launch_grouped_ffn with
+// tiles_ready then skips building it)
 hipError_t launch_permute(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, int32_t* offsets,
-                          int32_t* sorted_token, int32_t* slot_of, char* ws, hipStream_t s);
+                          int32_t* sorted_token, int32_t* slot_of, char* ws, hipStream_t s, bool with_tiles = false);
 
 hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
                               const int32_t* sorted_token, const void* wg, const void* wu, const void* wd,
                               const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
-                              hipStream_t s, const Prof* prof = nullptr);
+                              hipStream_t s, const Prof* prof = nullptr, bool tiles_ready = false);
 
 // residual: [T, d] added last (nullptr: none)
 // row-tile list of the grouped GEMMs (rows per tile ffn_tile_rows) and zeroed split-K counters

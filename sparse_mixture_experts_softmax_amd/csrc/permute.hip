@@ -23,6 +23,18 @@ namespace {
 
 constexpr int kWaves = kPermuteChunk / 64;
 
+// where the scan also writes the grouped GEMM's tile list (tile_group null: it does not)
+struct TileListArgs {
+  int32_t* tile_group;
+  int32_t* tile_m0;
+  int32_t* tile_count;
+  int32_t* split_cnt;
+  int64_t n_cnt;
+  int64_t T;
+  int has_shared;
+  int BM;
+};
+
 __global__ void __launch_bounds__(kPermuteChunk)
 permute_count_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int k, int32_t* __restrict__ rank,
                      int32_t* __restrict__ chunk_counts) {
@@ -82,29 +94,55 @@ __device__ void block_exclusive_scan_1024(int* s_val, int n, int* s_tmp, int* to
   __syncthreads();
 }
 
+// Chunk counts are loaded 16 at a time before any is rewritten, so each thread has 16 loads in
+// flight instead of one dependent load per chunk.
 __global__ void __launch_bounds__(1024)
-permute_scan_kernel(int32_t* __restrict__ chunk_counts, int64_t nchunks, int E, int32_t* __restrict__ offsets) {
+permute_scan_kernel(int32_t* __restrict__ chunk_counts, int64_t nchunks, int E, int32_t* __restrict__ offsets,
+                    TileListArgs tl) {
   __shared__ int s_val[2048];
   __shared__ int s_tmp[1024];
+  __shared__ int s_rows[kMaxGroups];
   __shared__ int s_total;
   const int tid = threadIdx.x;
+  constexpr int B = 16;
   for (int e = tid; e < E; e += 1024) {
     int run = 0;
-    for (int64_t c = 0; c < nchunks; ++c) {
-      const int v = chunk_counts[c * E + e];
-      chunk_counts[c * E + e] = run;
-      run += v;
+    for (int64_t c0 = 0; c0 < nchunks; c0 += B) {
+      int v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) v[i] = c0 + i < nchunks ? chunk_counts[(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+        if (c0 + i < nchunks) {
+          chunk_counts[(c0 + i) * E + e] = run;
+          run += v[i];
+        }
     }
     s_val[e] = run;
+    s_rows[e] = run;
   }
   __syncthreads();
   block_exclusive_scan_1024(s_val, E, s_tmp, &s_total);
   for (int e = tid; e < E; e += 1024) {
     const int base = s_val[e];
     offsets[e] = base;
-    for (int64_t c = 0; c < nchunks; ++c) chunk_counts[c * E + e] += base;
+    for (int64_t c0 = 0; c0 < nchunks; c0 += B) {
+      int v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) v[i] = c0 + i < nchunks ? chunk_counts[(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+        if (c0 + i < nchunks) chunk_counts[(c0 + i) * E + e] = v[i] + base;
+    }
   }
   if (tid == 0) offsets[E] = s_total;
+  if (tl.tile_group) {
+    // the grouped GEMM's tile list from the same group sizes (the shared expert last)
+    if (tid == 0 && tl.has_shared) s_rows[E] = (int)tl.T;
+    __syncthreads();
+    build_tile_list(s_rows, E + tl.has_shared, tl.BM, s_val, s_tmp, tl.tile_group, tl.tile_m0, tl.tile_count,
+                    tl.split_cnt, tl.n_cnt);
+  }
 }
 
 __global__ void __launch_bounds__(kPermuteChunk)
@@ -125,14 +163,25 @@ permute_scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, i
 }  // namespace
 
 hipError_t launch_permute(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, int32_t* offsets,
-                          int32_t* sorted_token, int32_t* slot_of, char* ws, hipStream_t s) {
+                          int32_t* sorted_token, int32_t* slot_of, char* ws, hipStream_t s, bool with_tiles) {
+  TileListArgs tl{};
+  if (with_tiles) {
+    tl.tile_group = (int32_t*)(ws + L.tile_group);
+    tl.tile_m0 = (int32_t*)(ws + L.tile_m0);
+    tl.tile_count = (int32_t*)(ws + L.tile_count);
+    tl.split_cnt = (int32_t*)(ws + L.ffn_cnt);
+    tl.n_cnt = 2 * L.ffn_cnt_each;
+    tl.T = dm.T;
+    tl.has_shared = dm.I_shared > 0 ? 1 : 0;
+    tl.BM = ffn_tile_rows(dm);
+  }
   int32_t* cc = (int32_t*)(ws + L.chunk_counts);
   const size_t lds = sizeof(unsigned long long) * kWaves * (size_t)dm.E;
   hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)L.nchunks), dim3(kPermuteChunk), lds, s, topk_idx, dm.T,
                      dm.E, dm.k, slot_of, cc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, cc, L.nchunks, dm.E, offsets);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, cc, L.nchunks, dm.E, offsets, tl);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)L.nchunks), dim3(kPermuteChunk), 0, s, topk_idx, dm.T,
