@@ -172,11 +172,14 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
   const int g16 = lane >> 4;
   const int i16 = lane & 15;
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  // With eight wavefronts (two per SIMD) the second wavefront of each SIMD issues its DMAs after
-  // its second sub-step's MFMAs rather than right after the barrier, so that the two do not both
-  // stall on DMA issue while the SIMD's matrix unit idles. The stage is free from the barrier on,
-  // and the DMAs still go out before the wave's next wait.
-  const bool late = GEO::NW == 8 && wave >= 4;
+  // With eight wavefronts (two per SIMD, one workgroup per CU) a wave with two live sub-tiles
+  // issues its DMAs after its second sub-step's MFMAs rather than right after the barrier: DMA
+  // issue stalls while the memory pipe is full, and behind the queued MFMAs that stall no longer
+  // idles the matrix unit (prefill gate/up 14.9 -> 14.1 ms). Waves with less MFMA work (the
+  // near-empty tiles of decode, bound by streaming the weights) issue at once, keeping the most
+  // bytes in flight. The stage is free from the barrier on, and the DMAs still go out before the
+  // wave's next wait. (Four-wave tiles, two workgroups per CU, measured no better this way.)
+  constexpr bool late = GEO::NW == 8 && NL == 2;
 
   auto issue = [&](int kt, int stage) {
     const uint32_t dst = lds_base + stage * STG;
