@@ -448,3 +448,56 @@ def test_fp8_forward_matches_oracle(torch, cfg):
     qerr = float(np.max(np.abs(o8 - o16)) / np.max(np.abs(o16)))
     _say(cfg.name, st, "fp8 vs bf16 max rel", qerr)
     assert qerr < 0.15
+
+
+# --------------------------------------------------------------------------------------------
+# HIP graphs: the forward enqueues kernels only (no allocation, copy, memset or sync), so it can
+# be captured once and replayed; each replay must equal an eager call on the same input
+# --------------------------------------------------------------------------------------------
+GRAPH_CASES = [
+    ("bf16_split_k", syn.MoEConfig("graph_split_k", T=3, d=2048, E=32, k=6, I=512, Is=256, dtype=syn.BF16, seed=71)),
+    ("bf16_mid_width", syn.MoEConfig("graph_mid", T=300, d=2048, E=64, k=8, I=512, Is=512, dtype=syn.BF16, seed=72)),
+    ("fp8", syn.MoEConfig("graph_fp8", T=40, d=1024, E=32, k=4, I=256, Is=256, dtype=syn.BF16, seed=73)),
+    ("block", syn.MoEConfig("graph_block", T=200, d=512, E=24, k=4, I=256, Is=128, dtype=syn.BF16, seed=74)),
+]
+
+
+@pytest.mark.parametrize("kind,cfg", GRAPH_CASES, ids=[c[0] for c in GRAPH_CASES])
+def test_forward_replays_in_a_hip_graph(torch, kind, cfg):
+    import sparse_mixture_experts_softmax_amd as moe
+    from moe_testlib import to_device
+    _say("case", kind, cfg)
+    h = host_inputs(cfg)
+    dev = device_from_host(h, cfg)
+    dims = moe.dims_for(dev["x"], dev["w_router"], dev["wg"], dev["wg_s"], cfg.k, True)
+    gamma = to_device(syn.host_gamma(cfg), torch_dtype(cfg)) if kind == "block" else None
+    experts = moe.Fp8Experts(dev["wg"], dev["wu"], dev["wd"], dev["wg_s"], dev["wu_s"], dev["wd_s"]) \
+        if kind == "fp8" else None
+
+    def call(x, ws):
+        if kind == "fp8":
+            return moe.moe_forward_fp8(x, dev["w_router"], experts, cfg.k, router_bias=dev["bias"], ws=ws, dims=dims)
+        if kind == "block":
+            return moe.moe_forward_block(x, gamma, dev["w_router"], dev["wg"], dev["wu"], dev["wd"], dev["wg_s"],
+                                         dev["wu_s"], dev["wd_s"], cfg.k, ws=ws, dims=dims)
+        return moe.moe_forward(x, dev["w_router"], dev["wg"], dev["wu"], dev["wd"], dev["wg_s"], dev["wu_s"],
+                               dev["wd_s"], cfg.k, router_bias=dev["bias"], ws=ws, dims=dims)
+
+    ws_graph, ws_eager = moe.workspace(dims, "cuda"), moe.workspace(dims, "cuda")
+    x_static = dev["x"].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(x_static, ws_graph)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out_g = call(x_static, ws_graph)
+    inputs = [dev["x"], torch.flip(dev["x"], dims=[0]).contiguous(), (dev["x"] * 0.5).contiguous()]
+    for rep, xi in enumerate(inputs + inputs[:1]):
+        x_static.copy_(xi)
+        g.replay()
+        ref = call(xi, ws_eager)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref), (kind, rep)
