@@ -110,8 +110,20 @@ def cpu_baseline(cfg, sample_tokens):
         dt += time.perf_counter() - t0
         passes += 1
     return {"value": passes * len(tokens) / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": "%d of the %d tokens (seeded), the whole block per token, %d pass(es), %.1f s"
-                      % (len(tokens), cfg.T, passes, dt)}
+            "sample": "%d of the %d tokens (seeded), the whole block per token, %d pass(es), %.1f s, on %s"
+                      % (len(tokens), cfg.T, passes, dt, cpu_model())}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), for the baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 CPU_SAMPLE = {"tiny": 64, "mid": 4096, "decode": 32, "prefill": 16, "skew": 16}
