@@ -13,6 +13,8 @@
 //                   then an exclusive scan over experts gives expert_offsets.
 //   permute_scatter slot = chunk base of the expert + rank; writes slot_of and
 //                   sorted_token.
+// When the tokens fit one chunk (T <= 256, decode) one workgroup does all three
+// with the counts in LDS (permute_one_chunk_kernel): two launches fewer.
 // A token's expert indices must be distinct (top-k output is). Pairs whose index
 // lies outside [0, E) are skipped: slot_of = -1.
 // All integer work; results are deterministic.
@@ -160,6 +162,66 @@ permute_scatter_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, i
   }
 }
 
+// All of dispatch in one workgroup when the tokens fit one chunk (T <= 256, decode): the masks and
+// ranks of permute_count, the scans of permute_scan (and the tile list) and the scatter, with
+// the counts kept in LDS. Same ranks, offsets and slots as the three kernels. 1024 threads;
+// threads 0 .. 255 hold one token each.
+__global__ void __launch_bounds__(1024)
+permute_one_chunk_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int k, int32_t* __restrict__ offsets,
+                         int32_t* __restrict__ slot_of, int32_t* __restrict__ sorted_token, TileListArgs tl) {
+  extern __shared__ unsigned long long mask[];  // [kWaves][E]
+  __shared__ int s_val[2048];
+  __shared__ int s_tmp[1024];
+  __shared__ int s_rows[kMaxGroups];
+  __shared__ int s_total;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kWaves * E; i += 1024) mask[i] = 0ull;
+  __syncthreads();
+  const int t = tid;  // token (chunk 0)
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const bool mine = tid < kPermuteChunk && t < T;
+  int e_of[kMaxK];
+  if (mine)
+    for (int j = 0; j < k; ++j) {
+      e_of[j] = topk_idx[(int64_t)t * k + j];
+      if ((unsigned)e_of[j] < (unsigned)E) atomicOr(&mask[w * E + e_of[j]], 1ull << lane);
+    }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) {
+    int c = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) c += __popcll(mask[w2 * E + e]);
+    s_val[e] = c;
+    s_rows[e] = c;
+  }
+  __syncthreads();
+  block_exclusive_scan_1024(s_val, E, s_tmp, &s_total);
+  for (int e = tid; e < E; e += 1024) offsets[e] = s_val[e];
+  if (tid == 0) offsets[E] = s_total;
+  if (mine) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int j = 0; j < k; ++j) {
+      const int e = e_of[j];
+      if ((unsigned)e >= (unsigned)E) {
+        slot_of[(int64_t)t * k + j] = -1;
+        continue;
+      }
+      int r = __popcll(mask[w * E + e] & below);
+      for (int w2 = 0; w2 < w; ++w2) r += __popcll(mask[w2 * E + e]);
+      const int slot = s_val[e] + r;
+      slot_of[(int64_t)t * k + j] = slot;
+      sorted_token[slot] = t;
+    }
+  }
+  if (tl.tile_group) {
+    if (tid == 0 && tl.has_shared) s_rows[E] = (int)tl.T;
+    __syncthreads();
+    build_tile_list(s_rows, E + tl.has_shared, tl.BM, s_val, s_tmp, tl.tile_group, tl.tile_m0, tl.tile_count,
+                    tl.split_cnt, tl.n_cnt);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_permute(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, int32_t* offsets,
@@ -177,6 +239,11 @@ hipError_t launch_permute(const moe_dims& dm, const Layout& L, const int32_t* to
   }
   int32_t* cc = (int32_t*)(ws + L.chunk_counts);
   const size_t lds = sizeof(unsigned long long) * kWaves * (size_t)dm.E;
+  if (L.nchunks == 1) {
+    hipLaunchKernelGGL(permute_one_chunk_kernel, dim3(1), dim3(1024), lds, s, topk_idx, dm.T, dm.E, dm.k, offsets,
+                       slot_of, sorted_token, tl);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)L.nchunks), dim3(kPermuteChunk), lds, s, topk_idx, dm.T,
                      dm.E, dm.k, slot_of, cc);
   hipError_t e = hipGetLastError();

@@ -113,13 +113,13 @@ def test_zero_tokens_is_a_no_op(torch):
 
 # --------------------------------------------------------------------------------------------
 # dispatch alone, on skewed indices with out-of-range entries; several 256-token chunks and a
-# ragged tail
+# ragged tail, and single chunks (T <= 256: the one-workgroup dispatch)
 # --------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("E", [300, 700])
-def test_permute_skewed_with_invalid_indices(torch, E):
+@pytest.mark.parametrize("E,T", [(300, 2500), (700, 2500), (300, 200), (1024, 256), (64, 1)])
+def test_permute_skewed_with_invalid_indices(torch, E, T):
     import sparse_mixture_experts_softmax_amd as moe
-    T, k = 2500, 5
-    rng = np.random.default_rng(E)
+    k = 5
+    rng = np.random.default_rng(E + T)
     # k distinct experts per token (as top-k selection gives), drawn with Zipf(1.2) weights
     p = 1.0 / np.arange(1, E + 1) ** 1.2
     p /= p.sum()
