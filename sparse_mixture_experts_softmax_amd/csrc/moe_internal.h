@@ -39,6 +39,7 @@ constexpr int kRouterTileT = 64;       // router logits tile: tokens
 constexpr int kRouterTileE = 64;       // router logits tile: experts
 constexpr int kRouterKStep = 16;       // router K step
 constexpr int kMaxK = 16;              // largest k (experts per token) accepted
+constexpr int kTopkWideMaxT = 64;      // top-k with four wavefronts per token up to this many tokens
 constexpr int kMaxGroups = 1025;       // grouped GEMM groups: up to 1024 experts + the shared one
 constexpr int kMfmaBM = 128;           // bf16 grouped GEMM tile rows
 constexpr int kMfmaBN1 = 128;          // gate/up tile: intermediate columns (x2 for gate and up)

@@ -413,6 +413,173 @@ router_topk_kernel(const float* __restrict__ part, int splits, const float* __re
   }
 }
 
+// Top-k for few tokens, four wavefronts per token. With one wavefront per token (above) a lone
+// token's time is set by its serial rounds over E/64 values per lane and by its split loads. Here
+// wavefront w holds experts 256 j + 64 w + lane (j < NJ2, all split loads of a logit in flight
+// 16 at a time), picks its own best k+1 by the same rule (largest logit, lowest index among
+// equals), the four lists go to LDS, and wavefront 0 picks the token's k+1 from those candidates:
+// the same selection. The softmax normaliser is summed per wavefront, then over the four in order.
+__device__ __forceinline__ int wave_min_int(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = min(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+template <int NJ2>
+__global__ void __launch_bounds__(256)
+router_topk_wide_kernel(const float* __restrict__ part, int splits, const float* __restrict__ bias, int64_t T, int E,
+                        int k, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                        float* __restrict__ topk_gap, float* __restrict__ probs) {
+  constexpr int MC = 4 * (kMaxK + 1);
+  constexpr int NONE = 0x7fffffff;
+  __shared__ float c_v[MC];
+  __shared__ int c_i[MC];
+  __shared__ float s_z[4];
+  __shared__ float s_m;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = blockIdx.x;
+
+  float v[NJ2];
+#pragma unroll
+  for (int j = 0; j < NJ2; ++j) v[j] = 0.f;
+  for (int sp0 = 0; sp0 < splits; sp0 += 16) {
+    float q[NJ2][16];
+#pragma unroll
+    for (int j = 0; j < NJ2; ++j) {
+      const int e = 256 * j + 64 * wave + lane;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        q[j][u] = (e < E && sp0 + u < splits) ? part[((int64_t)(sp0 + u) * T + t) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < NJ2; ++j)
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (sp0 + u < splits) v[j] += q[j][u];
+  }
+#pragma unroll
+  for (int j = 0; j < NJ2; ++j) {
+    const int e = 256 * j + 64 * wave + lane;
+    v[j] = e < E ? (bias ? v[j] + bias[e] : v[j]) : -INFINITY;
+  }
+
+  // this wavefront's best `rounds` (index NONE once it has no valid expert left)
+  const int rounds = k < E ? k + 1 : k;
+  uint32_t taken = 0;
+  float my_v = -INFINITY;
+  int my_i = NONE;
+#pragma unroll 1
+  for (int r = 0; r < rounds; ++r) {
+    float lv = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ2; ++j)
+      if (256 * j + 64 * wave + lane < E && !((taken >> j) & 1u)) lv = fmaxf(lv, v[j]);
+    const float mv = wave_max(lv);
+    int bi = NONE;
+#pragma unroll
+    for (int j = 0; j < NJ2; ++j) {
+      const unsigned long long b =
+          __ballot(256 * j + 64 * wave + lane < E && !((taken >> j) & 1u) && v[j] == mv);
+      if (bi == NONE && b != 0ull) bi = 256 * j + 64 * wave + (__ffsll(b) - 1);
+    }
+    if (bi != NONE && (bi & 63) == lane) taken |= 1u << (bi >> 8);
+    if (lane == r) {
+      my_v = mv;
+      my_i = bi;
+    }
+  }
+  if (lane < rounds) {
+    c_v[wave * rounds + lane] = my_v;
+    c_i[wave * rounds + lane] = my_i;
+  }
+  __syncthreads();
+
+  // wavefront 0: the token's best `rounds` among the 4 * rounds candidates (two per lane)
+  float fv = -INFINITY;
+  int fi = NONE;
+  if (wave == 0) {
+    const int nc = 4 * rounds;
+    float cv[2];
+    int ci[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = lane + 64 * h;
+      cv[h] = c < nc ? c_v[c] : -INFINITY;
+      ci[h] = c < nc ? c_i[c] : NONE;
+    }
+    uint32_t tk = 0;
+#pragma unroll 1
+    for (int r = 0; r < rounds; ++r) {
+      float lv = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (ci[h] != NONE && !((tk >> h) & 1u)) lv = fmaxf(lv, cv[h]);
+      const float mv = wave_max(lv);
+      int li = NONE;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (ci[h] != NONE && !((tk >> h) & 1u) && cv[h] == mv) li = min(li, ci[h]);
+      const int bi = wave_min_int(li);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (ci[h] == bi) tk |= 1u << h;
+      if (lane == r) {
+        fv = mv;
+        fi = bi;
+      }
+    }
+    if (lane == 0) s_m = fv;
+  }
+  __syncthreads();
+
+  // softmax over all E logits: per-wavefront sums, then the four in order
+  const float m = s_m;
+  float z = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ2; ++j)
+    if (256 * j + 64 * wave + lane < E) z += expf(v[j] - m);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+  if (lane == 0) s_z[wave] = z;
+  __syncthreads();
+  z = ((s_z[0] + s_z[1]) + s_z[2]) + s_z[3];
+  if (wave == 0) {
+    const float p_mine = lane < k ? expf(fv - m) : 0.f;
+    float denom = z;
+    if (renorm) {
+      denom = p_mine;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) denom += __shfl_xor(denom, off, 64);
+    }
+    if (lane < k) {
+      topk_idx[t * k + lane] = fi;
+      topk_w[t * k + lane] = p_mine / denom;
+    }
+    if (topk_gap) {
+      const float g = k < E ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fv), k - 1)) -
+                                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fv), k))
+                            : INFINITY;
+      if (lane == 0) topk_gap[t] = g;
+    }
+  }
+  if (probs) {
+#pragma unroll
+    for (int j = 0; j < NJ2; ++j) {
+      const int e = 256 * j + 64 * wave + lane;
+      if (e < E) probs[t * E + e] = expf(v[j] - m) / z;
+    }
+  }
+}
+
+template <int NJ2>
+hipError_t launch_topk_wide(const float* part, int splits, const float* bias, int64_t T, int E, int k, int renorm,
+                            int32_t* idx, float* w, float* gap, float* probs, hipStream_t s) {
+  hipLaunchKernelGGL(router_topk_wide_kernel<NJ2>, dim3((unsigned)T), dim3(256), 0, s, part, splits, bias, T, E, k,
+                     renorm, idx, w, gap, probs);
+  return hipGetLastError();
+}
+
 template <int NJ>
 hipError_t launch_topk(const float* part, int splits, const float* bias, int64_t T, int E, int k, int renorm,
                        int32_t* idx, float* w, float* gap, float* probs, hipStream_t s) {
@@ -525,6 +692,12 @@ hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, con
   }
   const int nj = (dm.E + 63) / 64;
   const int sp = L.router_splits;
+  if (dm.T <= kTopkWideMaxT && dm.E > 64) {
+    const int nj2 = (dm.E + 255) / 256;
+    if (nj2 <= 1) return launch_topk_wide<1>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, probs, s);
+    if (nj2 <= 2) return launch_topk_wide<2>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, probs, s);
+    return launch_topk_wide<4>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, probs, s);
+  }
   if (nj <= 1) return launch_topk<1>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, probs, s);
   if (nj <= 2) return launch_topk<2>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, probs, s);
   if (nj <= 4) return launch_topk<4>(part, sp, bias, dm.T, dm.E, dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, probs, s);

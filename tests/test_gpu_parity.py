@@ -87,6 +87,11 @@ SMALL_CASES = [
     # tiles with a shared expert narrower than the routed ones)
     ("split_k_T1", 1, 2048, 64, 4, 1024, 1024, syn.BF16, 1, 0.0),
     ("split_k_T3", 3, 4096, 32, 6, 512, 256, syn.BF16, 1, 0.0),
+    # few tokens with E > 64: top-k on four wavefronts per token (E not a multiple of 256, k = 16
+    # with 68 merge candidates, no renormalisation, fp32)
+    ("topk_wide_no_renorm", 5, 256, 300, 7, 128, 0, syn.BF16, 0, 0.0),
+    ("topk_wide_k16", 60, 512, 1024, 16, 64, 64, syn.BF16, 1, 0.0),
+    ("topk_wide_f32", 20, 64, 130, 4, 32, 32, syn.F32, 1, 0.0),
     # equal row tiles (<= 192 rows per expert on average) under Zipf-skewed loads of ~50 .. ~650 rows
     ("balanced_tiles_skewed", 700, 512, 16, 4, 256, 128, syn.BF16, 1, 0.8),
 ]
