@@ -5,9 +5,9 @@
 //
 //   out[t] = sum_{j<k} w[t,j] * y[slot_of[t*k+j]]  +  y[T*k + t]  (+ residual[t])
 //
-// One 256-thread workgroup per token; each thread owns 8 consecutive hidden
-// elements (16-byte bf16 or 2x16-byte fp32 loads), issues the loads of all k+1
-// rows before the first add, accumulates in fp32 in the fixed order j = 0..k-1,
+// One workgroup per token (256 threads; up to 1024 for few tokens); each thread owns
+// 8 consecutive hidden elements at a time (16-byte bf16 or 2x16-byte fp32 loads),
+// issues the loads of all k+1 rows before the first add, accumulates in fp32 in the fixed order j = 0..k-1,
 // the shared row, then the residual row (the block's input, when the caller
 // asks for the residual add), and rounds once on store. Pairs with slot_of = -1 (an
 // expert index outside [0, E) at dispatch) contribute nothing.
@@ -51,8 +51,8 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
   *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-template <typename ET>
-__global__ void __launch_bounds__(256)
+template <typename ET, int MAXT>
+__global__ void __launch_bounds__(MAXT)
 combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, const float* __restrict__ topk_w,
                const ET* __restrict__ residual, ET* __restrict__ out, int64_t T, int d, int k, int has_shared) {
   __shared__ int s_slot[kMaxK];
@@ -65,7 +65,7 @@ combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, co
   __syncthreads();
   const int64_t shared_row = T * k + t;
   typedef typename RawOf<ET>::type Raw;
-  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
     // every row's load is issued before the first add
     Raw raw[kMaxK + 2];
 #pragma unroll
@@ -105,12 +105,21 @@ combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, co
 hipError_t launch_combine(const moe_dims& dm, const void* y, const int32_t* slot_of, const float* topk_w,
                           const void* residual, void* out, hipStream_t s) {
   const int hs = dm.I_shared > 0 ? 1 : 0;
-  if (dm.dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3((unsigned)dm.T), dim3(256), 0, s, (const bf16_t*)y, slot_of,
-                       topk_w, (const bf16_t*)residual, (bf16_t*)out, dm.T, dm.d, dm.k, hs);
+  // few tokens: up to d / 8 threads per token (1024 at most), so that all of a token's row loads
+  // are in flight at once; otherwise 256 threads, looping over the row
+  // (bf16: the eight-element loads fit 128 registers; fp32 stays at 256 threads)
+  int threads = 256;
+  if (dm.T <= 256 && dm.dtype == MOE_BF16)
+    while (threads < 1024 && threads * 8 < dm.d) threads *= 2;
+  if (dm.dtype == MOE_BF16 && threads > 256)
+    hipLaunchKernelGGL((combine_kernel<bf16_t, 1024>), dim3((unsigned)dm.T), dim3(threads), 0, s, (const bf16_t*)y,
+                       slot_of, topk_w, (const bf16_t*)residual, (bf16_t*)out, dm.T, dm.d, dm.k, hs);
+  else if (dm.dtype == MOE_BF16)
+    hipLaunchKernelGGL((combine_kernel<bf16_t, 256>), dim3((unsigned)dm.T), dim3(256), 0, s, (const bf16_t*)y,
+                       slot_of, topk_w, (const bf16_t*)residual, (bf16_t*)out, dm.T, dm.d, dm.k, hs);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)dm.T), dim3(256), 0, s, (const float*)y, slot_of, topk_w,
-                       (const float*)residual, (float*)out, dm.T, dm.d, dm.k, hs);
+    hipLaunchKernelGGL((combine_kernel<float, 256>), dim3((unsigned)dm.T), dim3(256), 0, s, (const float*)y, slot_of,
+                       topk_w, (const float*)residual, (float*)out, dm.T, dm.d, dm.k, hs);
   return hipGetLastError();
 }
 
