@@ -233,8 +233,19 @@ router_small_kernel(const XT* __restrict__ x, const float* __restrict__ wr, floa
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = 0.f;
 
+  constexpr int NX = TT * kSmallRows / 4 / 256;  // 4-value x chunks per thread and pass
   for (int k0 = kbeg; k0 < kend; k0 += kSmallRows) {
     const int kn = min(kSmallRows, kend - k0);  // a multiple of 8
+    // the pass's x values and weights are all requested before any is used: one memory round trip
+    float xv[NX][4];
+#pragma unroll
+    for (int u = 0; u < NX; ++u) {
+      const int i = tid + 256 * u;
+      const int t = i / (kSmallRows / 4);
+      const int r4 = (i % (kSmallRows / 4)) * 4;
+      xv[u][0] = xv[u][1] = xv[u][2] = xv[u][3] = 0.f;
+      if (t < T && r4 < kn) load_x4<XT>(x + (int64_t)t * d + k0 + r4, xv[u]);
+    }
     float w[64];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -244,12 +255,12 @@ router_small_kernel(const XT* __restrict__ x, const float* __restrict__ wr, floa
         w[4 * i + c] = (r < kn && e < E) ? wr[(int64_t)(k0 + r) * E + e] : 0.f;
       }
     __syncthreads();  // the previous pass is done with xs
-    for (int i = tid; i < TT * kSmallRows / 4; i += 256) {
+#pragma unroll
+    for (int u = 0; u < NX; ++u) {
+      const int i = tid + 256 * u;
       const int t = i / (kSmallRows / 4);
       const int r4 = (i % (kSmallRows / 4)) * 4;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      if (t < T && r4 < kn) load_x4<XT>(x + (int64_t)t * d + k0 + r4, v);
-      *(float4*)&xs[t * kSmallRows + r4] = make_float4(v[0], v[1], v[2], v[3]);
+      *(float4*)&xs[t * kSmallRows + r4] = make_float4(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
     }
     __syncthreads();
 #pragma unroll
