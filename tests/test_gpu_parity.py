@@ -87,6 +87,8 @@ SMALL_CASES = [
     # tiles with a shared expert narrower than the routed ones)
     ("split_k_T1", 1, 2048, 64, 4, 1024, 1024, syn.BF16, 1, 0.0),
     ("split_k_T3", 3, 4096, 32, 6, 512, 256, syn.BF16, 1, 0.0),
+    # the most experts and the largest k on the streaming GEMMs and the MFMA router (1025 groups)
+    ("stream_E1024_k16", 300, 512, 1024, 16, 128, 128, syn.BF16, 1, 0.0),
     # few tokens with E > 64: top-k on four wavefronts per token (E not a multiple of 256, k = 16
     # with 68 merge candidates, no renormalisation, fp32)
     ("topk_wide_no_renorm", 5, 256, 300, 7, 128, 0, syn.BF16, 0, 0.0),
