@@ -41,11 +41,11 @@ build_tiles_kernel(const int32_t* __restrict__ offsets, int64_t T, int E, int ha
                    int32_t* __restrict__ tile_group, int32_t* __restrict__ tile_m0, int32_t* __restrict__ tile_count,
                    int32_t* __restrict__ split_cnt, int64_t n_cnt) {
   __shared__ int s_rows[kMaxGroups];
-  __shared__ int s_val[2048];
-  __shared__ int s_tmp[1024];
+  __shared__ int s_w[17];
   const int G = E + has_shared;
   for (int g = threadIdx.x; g < G; g += 1024) s_rows[g] = g < E ? offsets[g + 1] - offsets[g] : (int)T;
-  build_tile_list(s_rows, G, BM, s_val, s_tmp, tile_group, tile_m0, tile_count, split_cnt, n_cnt);
+  __syncthreads();
+  build_tile_list(s_rows, G, BM, s_w, tile_group, tile_m0, tile_count, split_cnt, n_cnt);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -123,29 +123,39 @@ __device__ __forceinline__ Group group_info(int g, const int32_t* offsets, int64
   return G;
 }
 
+// Exclusive prefix sum over the 1024 threads of a workgroup: each wavefront scans its 64 values
+// with lane shuffles, the 16 wavefront totals go through LDS (s_w, 17 ints), and each thread adds
+// the totals of the wavefronts before it. Two barriers instead of one per doubling step.
+// Returns the thread's exclusive prefix; *total (LDS) receives the sum of all values.
+__device__ inline int block_exclusive_scan_1024t(int x, int* s_w, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) s_w[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wv; ++w) before += s_w[w];
+  if (threadIdx.x == 1023) *total = before + incl;
+  __syncthreads();  // s_w may be reused once every thread has read it
+  return before + incl - x;
+}
+
 // Row-tile list of the grouped GEMMs: group g with s_rows[g] rows gets ceil(rows / BM) tiles,
-// listed group after group as (group, first row). One workgroup of 1024 threads; s_rows,
-// s_val[2048] and s_tmp[1024] are LDS arrays (G <= 2048 groups). Also zeroes the split-K
-// arrival counters.
-__device__ inline void build_tile_list(const int* s_rows, int G, int BM, int* s_val, int* s_tmp,
-                                       int32_t* tile_group, int32_t* tile_m0, int32_t* tile_count,
-                                       int32_t* split_cnt, int64_t n_cnt) {
+// listed group after group as (group, first row). One workgroup of 1024 threads; s_rows and s_w
+// (17 ints) are LDS arrays (G <= 2048 groups). Also zeroes the split-K arrival counters.
+__device__ inline void build_tile_list(const int* s_rows, int G, int BM, int* s_w, int32_t* tile_group,
+                                       int32_t* tile_m0, int32_t* tile_count, int32_t* split_cnt, int64_t n_cnt) {
   const int tid = threadIdx.x;
   for (int64_t i = tid; i < n_cnt; i += 1024) split_cnt[i] = 0;
-  for (int g = tid; g < G; g += 1024) s_val[g] = (s_rows[g] + BM - 1) / BM;
-  __syncthreads();
-  // exclusive scan of the tile counts, two per thread
-  const int a = 2 * tid < G ? s_val[2 * tid] : 0;
-  const int b = 2 * tid + 1 < G ? s_val[2 * tid + 1] : 0;
-  s_tmp[tid] = a + b;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? s_tmp[tid - off] : 0;
-    __syncthreads();
-    s_tmp[tid] += v;
-    __syncthreads();
-  }
-  const int excl = s_tmp[tid] - (a + b);
+  // tile counts of groups 2 tid and 2 tid + 1, and their exclusive prefix
+  const int a = 2 * tid < G ? (s_rows[2 * tid] + BM - 1) / BM : 0;
+  const int b = 2 * tid + 1 < G ? (s_rows[2 * tid + 1] + BM - 1) / BM : 0;
+  const int excl = block_exclusive_scan_1024t(a + b, s_w, &s_w[16]);
   const int starts[2] = {excl, excl + a};
   const int cnts[2] = {a, b};
 #pragma unroll
@@ -157,7 +167,7 @@ __device__ inline void build_tile_list(const int* s_rows, int G, int BM, int* s_
         tile_m0[starts[h] + i] = i * BM;
       }
   }
-  if (tid == 1023) *tile_count = s_tmp[1023];
+  if (tid == 1023) *tile_count = excl + a + b;
 }
 
 // ------------------------------------------------------------------------------------------

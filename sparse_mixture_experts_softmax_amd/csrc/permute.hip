@@ -75,24 +75,15 @@ permute_count_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int
   }
 }
 
-// Exclusive scan of n (<= 2048) values held two per thread across 1024 threads.
-__device__ void block_exclusive_scan_1024(int* s_val, int n, int* s_tmp, int* total) {
+// Exclusive scan of n (<= 2048) values in s_val, two per thread across 1024 threads, in place;
+// *total receives their sum. s_w: 17 ints of LDS.
+__device__ void block_exclusive_scan_1024(int* s_val, int n, int* s_w, int* total) {
   const int tid = threadIdx.x;
   const int a = 2 * tid < n ? s_val[2 * tid] : 0;
   const int b = 2 * tid + 1 < n ? s_val[2 * tid + 1] : 0;
-  s_tmp[tid] = a + b;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? s_tmp[tid - off] : 0;
-    __syncthreads();
-    s_tmp[tid] += v;
-    __syncthreads();
-  }
-  const int incl = s_tmp[tid];
-  const int excl = incl - (a + b);
+  const int excl = block_exclusive_scan_1024t(a + b, s_w, total);
   if (2 * tid < n) s_val[2 * tid] = excl;
   if (2 * tid + 1 < n) s_val[2 * tid + 1] = excl + a;
-  if (tid == 1023) *total = incl;
   __syncthreads();
 }
 
@@ -102,7 +93,7 @@ __global__ void __launch_bounds__(1024)
 permute_scan_kernel(int32_t* __restrict__ chunk_counts, int64_t nchunks, int E, int32_t* __restrict__ offsets,
                     TileListArgs tl) {
   __shared__ int s_val[2048];
-  __shared__ int s_tmp[1024];
+  __shared__ int s_w[17];
   __shared__ int s_rows[kMaxGroups];
   __shared__ int s_total;
   const int tid = threadIdx.x;
@@ -124,7 +115,7 @@ permute_scan_kernel(int32_t* __restrict__ chunk_counts, int64_t nchunks, int E, 
     s_rows[e] = run;
   }
   __syncthreads();
-  block_exclusive_scan_1024(s_val, E, s_tmp, &s_total);
+  block_exclusive_scan_1024(s_val, E, s_w, &s_total);
   for (int e = tid; e < E; e += 1024) {
     const int base = s_val[e];
     offsets[e] = base;
@@ -142,8 +133,8 @@ permute_scan_kernel(int32_t* __restrict__ chunk_counts, int64_t nchunks, int E, 
     // the grouped GEMM's tile list from the same group sizes (the shared expert last)
     if (tid == 0 && tl.has_shared) s_rows[E] = (int)tl.T;
     __syncthreads();
-    build_tile_list(s_rows, E + tl.has_shared, tl.BM, s_val, s_tmp, tl.tile_group, tl.tile_m0, tl.tile_count,
-                    tl.split_cnt, tl.n_cnt);
+    build_tile_list(s_rows, E + tl.has_shared, tl.BM, s_w, tl.tile_group, tl.tile_m0, tl.tile_count, tl.split_cnt,
+                    tl.n_cnt);
   }
 }
 
@@ -171,7 +162,7 @@ permute_one_chunk_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E,
                          int32_t* __restrict__ slot_of, int32_t* __restrict__ sorted_token, TileListArgs tl) {
   extern __shared__ unsigned long long mask[];  // [kWaves][E]
   __shared__ int s_val[2048];
-  __shared__ int s_tmp[1024];
+  __shared__ int s_w[17];
   __shared__ int s_rows[kMaxGroups];
   __shared__ int s_total;
   const int tid = threadIdx.x;
@@ -196,7 +187,7 @@ permute_one_chunk_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E,
     s_rows[e] = c;
   }
   __syncthreads();
-  block_exclusive_scan_1024(s_val, E, s_tmp, &s_total);
+  block_exclusive_scan_1024(s_val, E, s_w, &s_total);
   for (int e = tid; e < E; e += 1024) offsets[e] = s_val[e];
   if (tid == 0) offsets[E] = s_total;
   if (mine) {
@@ -217,8 +208,8 @@ permute_one_chunk_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E,
   if (tl.tile_group) {
     if (tid == 0 && tl.has_shared) s_rows[E] = (int)tl.T;
     __syncthreads();
-    build_tile_list(s_rows, E + tl.has_shared, tl.BM, s_val, s_tmp, tl.tile_group, tl.tile_m0, tl.tile_count,
-                    tl.split_cnt, tl.n_cnt);
+    build_tile_list(s_rows, E + tl.has_shared, tl.BM, s_w, tl.tile_group, tl.tile_m0, tl.tile_count, tl.split_cnt,
+                    tl.n_cnt);
   }
 }
 
