@@ -110,22 +110,26 @@ __device__ __forceinline__ void mainloop_f8(int nk, lds_char* lds, ABase a_base,
 
   bf16x8_t a0[NA], b0[4], a1[NA], b1[4];
   read(lds, 0, a0, b0);
+  // last k-step peeled off, as in stream::mainloop_v: the loop body always crosses the barrier
   int stage = 0;
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt < nk - 1; ++kt) {
     const lds_char* cur = lds + stage * F8_STAGE;
     const int next = stage == S - 1 ? 0 : stage + 1;
     read(cur, 1, a1, b1);
     mma(a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      wait_groups<F8_DMA>(min(S - 2, nk - kt - 2));
-      barrier_after_lds_reads();
-      if (kt + S < nk) issue(kt + S, stage);
-      read(lds + next * F8_STAGE, 0, a0, b0);
-    }
+    wait_groups<F8_DMA>(min(S - 2, nk - kt - 2));
+    barrier_after_lds_reads();
+    if (kt + S < nk) issue(kt + S, stage);
+    read(lds + next * F8_STAGE, 0, a0, b0);
     mma(a1, b1);
     __builtin_amdgcn_sched_barrier(0);
     stage = next;
+  }
+  if (nk >= 1) {
+    read(lds + stage * F8_STAGE, 1, a1, b1);
+    mma(a0, b0);
+    mma(a1, b1);
   }
 }
 

@@ -223,24 +223,31 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
 
   bf16x8_t a0[NA], b0[4], a1[NA], b1[4];
   read(lds, 0, a0, b0);
+  // The last k-step is peeled off: inside the loop every path crosses the barrier, so the
+  // compiler's LDS wait before the second sub-step's MFMAs covers only their own fragments (read
+  // before the barrier). With the barrier under a branch its merged wait also covered the next
+  // stage's fresh reads, and their latency stalled the MFMAs it is meant to hide behind.
   int stage = 0;
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt < nk - 1; ++kt) {
     const lds_char* cur = lds + stage * STG;
     const int next = stage == S - 1 ? 0 : stage + 1;
     read(cur, 1, a1, b1);
     mma(a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      // stage kt+1 complete once at most the DMAs of k-steps kt+2 .. kt+S-1 are outstanding
-      wait_groups<DMA>(min(S - 2, nk - kt - 2));
-      barrier_after_lds_reads();
-      if (!late && kt + S < nk) issue(kt + S, stage);
-      read(lds + next * STG, 0, a0, b0);
-    }
+    // stage kt+1 complete once at most the DMAs of k-steps kt+2 .. kt+S-1 are outstanding
+    wait_groups<DMA>(min(S - 2, nk - kt - 2));
+    barrier_after_lds_reads();
+    if (!late && kt + S < nk) issue(kt + S, stage);
+    read(lds + next * STG, 0, a0, b0);
     mma(a1, b1);
     __builtin_amdgcn_sched_barrier(0);
     if (late && kt + S < nk) issue(kt + S, stage);
     stage = next;
+  }
+  if (nk >= 1) {  // k-step nk-1: all DMAs issued (nk-2+S >= nk), no barrier
+    read(lds + stage * STG, 1, a1, b1);
+    mma(a0, b0);
+    mma(a1, b1);
   }
 }
 
