@@ -94,7 +94,10 @@ Layout make_layout(const moe_dims& dm) {
   if (L.router_mfma) {
     const int64_t base_tiles = ((T + 127) / 128) * (dm.E / 256);
     const int64_t ksteps = 3 * (int64_t)dm.d / 32;
-    splits = (256 + base_tiles - 1) / base_tiles;
+    // one workgroup per CU for few tiles (more splits only add partial sums for the top-k to
+    // read); two per CU (a second split) once the tiles alone cover half the CUs
+    const int64_t target = base_tiles >= 128 ? 512 : 256;
+    splits = (target + base_tiles - 1) / base_tiles;
     if (splits > 8) splits = 8;
     if (splits > ksteps / 8) splits = ksteps / 8 > 0 ? ksteps / 8 : 1;
     if (splits < 1) splits = 1;
