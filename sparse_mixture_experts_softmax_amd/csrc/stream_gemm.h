@@ -29,8 +29,6 @@
 // 16 bytes per lane) on distinct banks of the 64 x 4-byte LDS banks.
 #pragma once
 
-#include <type_traits>
-
 #include "moe_internal.h"
 
 namespace moe {
