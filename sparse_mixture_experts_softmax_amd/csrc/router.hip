@@ -102,20 +102,36 @@ router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ plan
   zero(acc);
   mainloop<2, 3>(nk, nl, (int)min<int64_t>(T - t0, 128), (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
 
-  float* out = part + (int64_t)split * T * E;
+  // Partial logits through LDS, 64 tile rows at a time (sub-tile u of both wave rows: tile rows
+  // 64u .. 64u+63), so that each lane stores whole 16-byte runs of a row instead of single floats.
+  // Row pitch 1056 bytes: the rows r and r + 4 that the two lane halves write fall on disjoint
+  // banks.
+  constexpr int PITCH = 256 * 4 + 32;
+  static_assert(64 * PITCH <= 3 * Geo<2>::STAGE, "64 staged rows fit the LDS stages");
+  float* out = part + (int64_t)split * T * E + e0;
+  char* st = smem;
   const int col_in = lane & 31;
   const int row_hi = (lane >> 5) * 4;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int u = 0; u < 2; ++u) {
+    __syncthreads();  // every wave is past its mainloop (u = 0) or its stores of the last pass
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int e = e0 + wn * 128 + j * 32 + col_in;
+      const int c = wn * 128 + j * 32 + col_in;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t t = t0 + sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
-        if (t < T) out[t * E + e] = acc[i][j][r];
+        const int row = wm * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+        *(float*)(st + row * PITCH + c * 4) = acc[u][j][r];
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int q = tid; q < 64 * 64; q += 256) {  // 64 rows x 64 runs of 16 bytes
+      const int row = q >> 6, ch = q & 63;
+      const int64_t t = t0 + 64 * u + row;
+      if (t < T) *(float4*)(out + t * E + ch * 4) = *(const float4*)(st + row * PITCH + ch * 16);
+    }
+  }
 }
 
 template <typename XT>
