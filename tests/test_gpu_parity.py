@@ -106,6 +106,31 @@ def test_small_shapes(torch, case):
     _full_check(torch, cfg, name)
 
 
+# Every token routed to the same k experts: a router bias of +32 on them lies far above the
+# synthetic logits' spread (under 8), so k groups hold all T rows and every other group is empty --
+# the largest groups the grouped GEMMs meet, next to empty ones; one-workgroup and chunked dispatch,
+# 128 x 256 and 128 x 512 tiles. Bias +32 keeps the fp32 logits' rounding (ulp 3.8e-6) within the
+# routing-weight bound.
+@pytest.mark.parametrize("T,d,E,k,Is", [(200, 512, 64, 4, 128), (1100, 512, 64, 4, 128), (300, 4096, 16, 2, 512)])
+def test_all_tokens_to_the_same_experts(torch, T, d, E, k, Is):
+    cfg = syn.MoEConfig("same_experts", T=T, d=d, E=E, k=k, I=256, Is=Is, dtype=syn.BF16, renorm=1, seed=5)
+    label = "same_experts_T%d_d%d" % (T, d)
+    _say("case", label, cfg)
+    h = host_inputs(cfg)
+    chosen = [5, E - 1, 2, 11][:k]
+    bias = np.zeros(E, np.float32)
+    bias[chosen] = 32.0
+    h["bias"] = bias
+    dev = device_from_host(h, cfg)
+    out, idx, w, gap = run_forward(dev, cfg)
+    torch.cuda.synchronize()
+    ref_out, ref_idx, ref_w, ref_gap = oracle_full(h, cfg)
+    assert sorted(set(ref_idx.ravel().tolist())) == sorted(chosen)  # the bias does force the routing
+    st = compare(cfg, to_host(out), to_host(idx), to_host(w), ref_out, ref_idx, ref_w, ref_gap, label)
+    assert st["flagged"] == 0
+    _say(label, st)
+
+
 def test_zero_tokens_is_a_no_op(torch):
     import sparse_mixture_experts_softmax_amd as moe
     cfg = syn.CONFIGS["tiny"].with_(T=3)
