@@ -8,7 +8,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["moe_api.hip", "norm.hip", "router.hip", "permute.hip", "grouped_ffn.hip", "grouped_ffn_fp8.hip",
+SOURCES = ["moe_api.hip", "norm.hip", "router.hip", "permute.hip", "grouped_ffn.hip", "grouped_ffn_fp8.hip", "grouped_ffn_skinny.hip",
            "combine.hip"]
 
 HIPCC_FLAGS = [

@@ -65,7 +65,8 @@ __device__ __forceinline__ bf16x8_t read_b_f8(const lds_char* sb, int n, int s, 
 // a_base(kt) / b_base(kt, i): uniform bases of k-step kt (B: this wave's i-th instruction);
 // a_off / b_off[i]: per-lane byte offsets. Same schedule as stream::mainloop_v.
 // NAD: A instructions this wave issues (those whose 16 rows hold a valid row of the tile).
-template <int S, int NL, int NAD, class ABase, class BBase>
+// NT: code DMAs with the non-temporal hint (the group's only row tile reads them).
+template <int S, int NL, int NAD, bool NT, class ABase, class BBase>
 __device__ __forceinline__ void mainloop_f8(int nk, lds_char* lds, ABase a_base, const uint32_t (&a_off)[F8_A_DMA],
                                             BBase b_base, const uint32_t (&b_off)[F8_B_DMA], const int (&bcol)[4],
                                             f32x16_t (&acc)[2][4]) {
@@ -83,7 +84,8 @@ __device__ __forceinline__ void mainloop_f8(int nk, lds_char* lds, ABase a_base,
 #pragma unroll
     for (int i = 0; i < NAD; ++i) dma16(ab, a_off[i], dst + (wave * F8_A_DMA + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < F8_B_DMA; ++i) dma16(b_base(kt, i), b_off[i], dst + F8_A_BYTES + (wave * F8_B_DMA + i) * 1024);
+    for (int i = 0; i < F8_B_DMA; ++i)
+      dma16<NT>(b_base(kt, i), b_off[i], dst + F8_A_BYTES + (wave * F8_B_DMA + i) * 1024);
   };
   auto read = [&](const lds_char* st, int s, bf16x8_t (&a)[NA], bf16x8_t (&b)[4]) {
     if constexpr (NL > 0) {
@@ -229,15 +231,22 @@ __global__ void __launch_bounds__(256, 2) ffn_fp8_stream_kernel(Fp8Args p) {
   f32x16_t acc[2][4];
   zero(acc);
   const int nad = needed_a_dma<2>(G.rows - m0 < SBM ? G.rows - m0 : SBM, wave);
-  auto run = [&](auto nlc) {
+  // the group's only row tile streams its code panels with the non-temporal hint (as in the bf16
+  // kernel); row tiles of a larger group share them through L2
+  auto run = [&](auto nlc, auto ntc) {
     constexpr int NL = decltype(nlc)::value;
-    if (nad >= 2) mainloop_f8<S, NL, 2>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
-    else if (nad == 1) mainloop_f8<S, NL, 1>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
-    else mainloop_f8<S, NL, 0>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+    constexpr bool NT = decltype(ntc)::value;
+    if (nad >= 2) mainloop_f8<S, NL, 2, NT>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+    else if (nad == 1) mainloop_f8<S, NL, 1, NT>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+    else mainloop_f8<S, NL, 0, NT>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
   };
-  if (nl >= 2) run(std::integral_constant<int, 2>());
-  else if (nl == 1) run(std::integral_constant<int, 1>());
-  else run(std::integral_constant<int, 0>());
+  auto run_nt = [&](auto ntc) {
+    if (nl >= 2) run(std::integral_constant<int, 2>(), ntc);
+    else if (nl == 1) run(std::integral_constant<int, 1>(), ntc);
+    else run(std::integral_constant<int, 0>(), ntc);
+  };
+  if (cnt == 1) run_nt(std::true_type());
+  else run_nt(std::false_type());
 
   // epilogue: column scales, then as in the bf16 kernel
   const int col_in = lane & 31;

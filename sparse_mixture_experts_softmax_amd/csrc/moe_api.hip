@@ -149,8 +149,12 @@ Layout make_layout(const moe_dims& dm) {
   size_t part = 0;
   if (P.s1 > 1) part = (size_t)P.s1 * L.rows_total * P.part_cols1 * 4;
   if (P.s2 > 1) part = std::max(part, (size_t)P.s2 * L.rows_total * P.part_cols2 * 4);
+  if (P.skinny && P.ks1 > 1) part = std::max(part, (size_t)P.ks1 * L.rows_total * P.part_cols1 * 4);
+  if (P.skinny && P.ks2 > 1) part = std::max(part, (size_t)P.ks2 * L.rows_total * P.part_cols2 * 4);
   L.ffn_part = take(part);
-  L.ffn_cnt_each = (P.s1 > 1 || P.s2 > 1) ? L.max_tiles * std::max(P.nt1, P.nt2) : 0;
+  int64_t per_tile = (P.s1 > 1 || P.s2 > 1) ? std::max(P.nt1, P.nt2) : 0;
+  if (P.skinny) per_tile = std::max<int64_t>(per_tile, std::max(P.cb1, P.cb2));
+  L.ffn_cnt_each = L.max_tiles * per_tile;
   L.ffn_cnt = take((size_t)2 * L.ffn_cnt_each * 4);
   L.total = off;
   return L;

@@ -46,6 +46,8 @@ constexpr int kMfmaBN1 = 128;          // gate/up tile: intermediate columns (x2
 constexpr int kMfmaBN2 = 256;          // down tile: hidden columns
 constexpr int kF32BM = 64;             // fp32 grouped GEMM tile rows
 constexpr int kF32BN = 64;             // fp32 grouped GEMM tile columns
+constexpr int kSkinnyMaxT = 2;         // skinny grouped GEMMs up to this many tokens
+constexpr int kSkinnyMaxKC = 2048;     // skinny grouped GEMMs: most K rows per split
 
 // ------------------------------------------------------------------------------------------
 // workspace layout: a pure function of the dims
@@ -78,6 +80,12 @@ struct FfnPlan {
   int nt1, nt2;
   int s1, s2;
   int64_t part_cols1, part_cols2;  // columns of the fp32 partial rows (gate | up, or d)
+  // few tokens (every group <= kSkinnyMaxT rows): the skinny kernels, 256-column blocks, K in
+  // splits of kc1 / kc2 rows (multiples of 8, <= kSkinnyMaxKC)
+  bool skinny;
+  int skinny_rows;        // rows per group the kernel is built for (1 or 2)
+  int cb1, cb2;           // 256-column blocks of the widest group
+  int ks1, ks2, kc1, kc2;
 };
 FfnPlan ffn_plan(const moe_dims& dm);
 
@@ -192,7 +200,13 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
                               const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
                               hipStream_t s, const Prof* prof = nullptr, bool tiles_ready = false);
 
-// residual: [T, d] added last (nullptr: none)
+// few tokens (plan.skinny): both products on the vector ALUs with the weights streamed by plain
+// 16-byte loads; tile list and counters as for launch_grouped_ffn
+hipError_t launch_ffn_skinny(const moe_dims& dm, const Layout& L, const FfnPlan& P, const void* x,
+                             const int32_t* offsets, const int32_t* sorted_token, const void* wg, const void* wu,
+                             const void* wd, const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
+                             hipStream_t s, const Prof* prof);
+
 // row-tile list of the grouped GEMMs (rows per tile ffn_tile_rows) and zeroed split-K counters
 int ffn_tile_rows(const moe_dims& dm);
 hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s);

@@ -102,10 +102,16 @@ __device__ __forceinline__ void barrier_after_lds_reads() {
 }
 
 // 16 bytes per lane from base + voff (base wave-uniform, voff per lane) to LDS byte address
-// dst_base + 16 * lane (dst_base wave-uniform)
+// dst_base + 16 * lane (dst_base wave-uniform). NT: with the non-temporal hint, for weight panels
+// that no other workgroup reads (an expert with a single row tile).
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t dst_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(dst_base)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(dst_base)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(dst_base)
+                 : "memory", "m0");
 }
 
 __device__ __forceinline__ const char* uniform_ptr(const char* p) {
@@ -154,7 +160,7 @@ __device__ __forceinline__ void wait_groups(int n) {
   else wait_vmcnt<0>();
 }
 
-template <int WN, int S, int NL, int NAD, class ABase, class BBase>
+template <int WN, int S, int NL, int NAD, bool NT, class ABase, class BBase>
 __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
                                            const uint32_t (&a_off)[Geo<WN>::A_DMA], BBase b_base, uint32_t b_off,
                                            const int (&bcol)[4], f32x16_t (&acc)[2][4]) {
@@ -186,7 +192,7 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
     for (int i = 0; i < NAD; ++i) dma16(ab, a_off[i], dst + (wave * GEO::A_DMA + i) * 1024);
 #pragma unroll
     for (int i = 0; i < GEO::B_DMA; ++i)
-      dma16(b_base(kt, i), b_off, dst + GEO::A_BYTES + (wave * GEO::B_DMA + i) * 1024);
+      dma16<NT>(b_base(kt, i), b_off, dst + GEO::A_BYTES + (wave * GEO::B_DMA + i) * 1024);
   };
   // fragments of sub-step s (0 or 1) of the stage at st
   auto read = [&](const lds_char* st, int s, bf16x8_t (&a)[NA], bf16x8_t (&b)[4]) {
@@ -253,17 +259,17 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base,
 // instructions it must issue: only those whose 16 rows hold a valid row of the tile (rows of them).
 // A tile rows past `rows` are then never loaded; the LDS holds stale values there, which only
 // reach accumulator rows that are not stored. Every wave takes part in the barriers.
-template <int WN, int S, int NL, class ABase, class BBase>
+template <int WN, int S, int NL, bool NT, class ABase, class BBase>
 __device__ __forceinline__ void mainloop_a(int nad, int nk, lds_char* lds, ABase a_base,
                                            const uint32_t (&a_off)[Geo<WN>::A_DMA], BBase b_base, uint32_t b_off,
                                            const int (&bcol)[4], f32x16_t (&acc)[2][4]) {
   if constexpr (Geo<WN>::A_DMA == 2) {
-    if (nad >= 2) mainloop_v<WN, S, NL, 2>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
-    else if (nad == 1) mainloop_v<WN, S, NL, 1>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
-    else mainloop_v<WN, S, NL, 0>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+    if (nad >= 2) mainloop_v<WN, S, NL, 2, NT>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+    else if (nad == 1) mainloop_v<WN, S, NL, 1, NT>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+    else mainloop_v<WN, S, NL, 0, NT>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
   } else {
-    if (nad >= 1) mainloop_v<WN, S, NL, 1>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
-    else mainloop_v<WN, S, NL, 0>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+    if (nad >= 1) mainloop_v<WN, S, NL, 1, NT>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+    else mainloop_v<WN, S, NL, 0, NT>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
   }
 }
 
@@ -274,14 +280,23 @@ __device__ __forceinline__ int needed_a_dma(int rows, int wave) {
   return n < 0 ? 0 : (n > Geo<WN>::A_DMA ? Geo<WN>::A_DMA : n);
 }
 
+// nt: B (weight) DMAs with the non-temporal hint -- for panels no other workgroup reads
+template <int WN, int S, bool NT, class ABase, class BBase>
+__device__ __forceinline__ void mainloop_n(int nk, int nl, int nad, lds_char* lds, ABase a_base,
+                                           const uint32_t (&a_off)[Geo<WN>::A_DMA], BBase b_base, uint32_t b_off,
+                                           const int (&bcol)[4], f32x16_t (&acc)[2][4]) {
+  if (nl >= 2) mainloop_a<WN, S, 2, NT>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else if (nl == 1) mainloop_a<WN, S, 1, NT>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else mainloop_a<WN, S, 0, NT>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+}
+
 template <int WN, int S, class ABase, class BBase>
 __device__ __forceinline__ void mainloop(int nk, int nl, int rows, lds_char* lds, ABase a_base,
                                          const uint32_t (&a_off)[Geo<WN>::A_DMA], BBase b_base, uint32_t b_off,
-                                         const int (&bcol)[4], f32x16_t (&acc)[2][4]) {
+                                         const int (&bcol)[4], f32x16_t (&acc)[2][4], bool nt = false) {
   const int nad = needed_a_dma<WN>(rows, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
-  if (nl >= 2) mainloop_a<WN, S, 2>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
-  else if (nl == 1) mainloop_a<WN, S, 1>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
-  else mainloop_a<WN, S, 0>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  if (nt) mainloop_n<WN, S, true>(nk, nl, nad, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else mainloop_n<WN, S, false>(nk, nl, nad, lds, a_base, a_off, b_base, b_off, bcol, acc);
 }
 
 

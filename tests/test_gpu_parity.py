@@ -83,10 +83,20 @@ SMALL_CASES = [
     # down at I >= 2048 with >= 64 rows per expert
     ("wide_gate_up", 200, 4096, 8, 2, 256, 512, syn.BF16, 1, 0.0),
     ("wide_down", 300, 512, 8, 2, 2048, 0, syn.BF16, 1, 0.0),
-    # few tokens: the gate/up product's K split over workgroups (4 ways; then 8 ways on 128 x 512
-    # tiles with a shared expert narrower than the routed ones)
-    ("split_k_T1", 1, 2048, 64, 4, 1024, 1024, syn.BF16, 1, 0.0),
+    # T <= 2: the skinny kernels (one or two rows per group; K splits with the last-arriver sum,
+    # empty splits and unused column blocks; shared expert as wide as, wider than, narrower than
+    # the routed ones, or absent)
+    ("skinny_T1", 1, 2048, 64, 4, 1024, 1024, syn.BF16, 1, 0.0),
+    ("skinny_T1_narrow_shared", 1, 768, 6, 3, 512, 256, syn.BF16, 0, 0.0),
+    ("skinny_T2_wide_shared", 2, 512, 4, 2, 256, 512, syn.BF16, 1, 0.0),
+    ("skinny_T2_no_shared", 2, 1024, 8, 2, 256, 0, syn.BF16, 1, 0.0),
+    # a few more tokens: the MFMA gate/up product's K split over workgroups (2 ways on 128 x 256
+    # tiles; 4 or 8 ways on 128 x 512 tiles with a shared expert narrower than the routed ones)
     ("split_k_T3", 3, 4096, 32, 6, 512, 256, syn.BF16, 1, 0.0),
+    ("split_k_T4_narrow_shared", 4, 768, 6, 3, 512, 256, syn.BF16, 0, 0.0),
+    ("split_k_T4_no_shared", 4, 1024, 8, 2, 256, 0, syn.BF16, 1, 0.0),
+    ("split_k_T6", 6, 2048, 64, 4, 1024, 1024, syn.BF16, 1, 0.0),
+    ("split_k_T5", 5, 4096, 32, 6, 512, 256, syn.BF16, 1, 0.0),
     # the most experts and the largest k on the streaming GEMMs and the MFMA router (1025 groups)
     ("stream_E1024_k16", 300, 512, 1024, 16, 128, 128, syn.BF16, 1, 0.0),
     # few tokens with E > 64: top-k on four wavefronts per token (E not a multiple of 256, k = 16
@@ -246,8 +256,8 @@ def _device_inputs(cfg, cache={}):
     return dev
 
 
-def _full_size_check(torch, name, n_sample):
-    cfg = syn.CONFIGS[name]
+def _full_size_check(torch, name, n_sample, T=None):
+    cfg = syn.CONFIGS[name] if T is None else syn.CONFIGS[name].with_(T=T)
     _say("config", cfg)
     dev = _device_inputs(cfg)
     out, idx, w, gap = run_forward(dev, cfg)
@@ -282,6 +292,13 @@ def test_mid_config_router_all_tokens_and_sampled_outputs(torch):
 def test_decode_config(torch):
     cfg, idx_h, load = _full_size_check(torch, "decode", 8)
     assert (load > 0).sum() > 150
+
+
+@pytest.mark.parametrize("T", [1, 2, 3])
+def test_decode_shape_few_tokens(torch, T):
+    # the large shape at T <= 2 runs the skinny kernels, at T = 3 the MFMA kernels with K split;
+    # every token against the oracle
+    _full_size_check(torch, "decode", T, T=T)
 
 
 def test_prefill_config(torch):
