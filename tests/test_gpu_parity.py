@@ -190,9 +190,11 @@ def test_permute_skewed_with_invalid_indices(torch, E, T):
 # --------------------------------------------------------------------------------------------
 # the four step entry points compose to moe_forward, bit for bit; permute is a stable sort
 # --------------------------------------------------------------------------------------------
-def test_steps_compose_and_permute_is_stable_sort(torch):
+# the grouped GEMMs' three bf16 paths: MFMA tiles (T = 600), MFMA with K split (T = 5), skinny (T = 2)
+@pytest.mark.parametrize("T,d,I,Is", [(600, 256, 128, 64), (5, 2048, 512, 512), (2, 512, 256, 256)])
+def test_steps_compose_and_permute_is_stable_sort(torch, T, d, I, Is):
     import sparse_mixture_experts_softmax_amd as moe
-    cfg = syn.MoEConfig("steps", T=600, d=256, E=48, k=6, I=128, Is=64, dtype=syn.BF16, seed=3)
+    cfg = syn.MoEConfig("steps", T=T, d=d, E=48, k=6, I=I, Is=Is, dtype=syn.BF16, seed=3)
     h = host_inputs(cfg)
     dev = device_from_host(h, cfg)
     dims = moe.dims_for(dev["x"], dev["w_router"], dev["wg"], dev["wg_s"], cfg.k, True)
@@ -505,6 +507,7 @@ def test_fp8_forward_matches_oracle(torch, cfg):
 # --------------------------------------------------------------------------------------------
 GRAPH_CASES = [
     ("bf16_split_k", syn.MoEConfig("graph_split_k", T=3, d=2048, E=32, k=6, I=512, Is=256, dtype=syn.BF16, seed=71)),
+    ("bf16_skinny", syn.MoEConfig("graph_skinny", T=1, d=2048, E=32, k=6, I=512, Is=512, dtype=syn.BF16, seed=75)),
     ("bf16_mid_width", syn.MoEConfig("graph_mid", T=300, d=2048, E=64, k=8, I=512, Is=512, dtype=syn.BF16, seed=72)),
     ("fp8", syn.MoEConfig("graph_fp8", T=40, d=1024, E=32, k=4, I=256, Is=256, dtype=syn.BF16, seed=73)),
     ("block", syn.MoEConfig("graph_block", T=200, d=512, E=24, k=4, I=256, Is=128, dtype=syn.BF16, seed=74)),
