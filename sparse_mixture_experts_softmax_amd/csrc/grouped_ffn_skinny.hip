@@ -103,8 +103,9 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
   const int64_t col = n0 + 8 * cth;
   const bf16_t* w0p = W0 + col;
   const bf16_t* w1p = GATED ? W1 + col : nullptr;
-  // this thread's K rows k0 + kl + 8 i, i < steps, in batches of kU rows
-  const int steps = k1 - k0 - kl > 0 ? (k1 - k0 - kl + 7) / 8 : 0;
+  // this thread's K rows k0 + kl + 8 i, i < steps, in batches of kU rows. k1 - k0 is a multiple of
+  // 8 (K and kc are), so every thread of the workgroup has the same count.
+  const int steps = k1 > k0 ? (k1 - k0) / 8 : 0;
   auto load = [&](uint4 (&buf)[NM][kU], int b) {
     const int kb = k0 + kl + 8 * kU * b;
 #pragma unroll
@@ -176,7 +177,7 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
         for (int m = 0; m < NM; ++m) fma8(acc[m][r], a, buf[m][u]);
       }
   };
-  auto tail = [&](int from) {  // rows of the batches past nb, one at a time
+  auto tail = [&](int from) {  // rows past the whole batches, one at a time
     for (int i = from; i < steps; ++i) {
       const int kk = k0 + kl + 8 * i;
       uint4 wv[NM];
@@ -191,16 +192,13 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
     }
   };
 
-  // nb is the same for every thread of the workgroup but the odd-lane half's when the split's rows
-  // are not a multiple of 8 * kU; the branch is on the workgroup's smallest, the kl = 7 lane's
-  const int steps_min = k1 - k0 - 7 > 0 ? (k1 - k0 - 7 + 7) / 8 : 0;
-  if (steps_min / kU >= 1) {
+  if (steps >= kU) {
     // Straight-line streaming: every batch load is unconditional, so the compiler's waits before
     // a batch's FMAs count exactly that batch. The A loads go out before the first batch: waiting
     // for them (loads complete in order) leaves the batch in flight behind the staging. One batch
     // per thread at a time keeps the registers low enough for five workgroups per CU, whose loads
     // together keep the memory pipe full.
-    const int nbw = steps_min / kU;  // batches (the same for every thread)
+    const int nbw = steps / kU;  // whole batches
     uint4 buf[NM][kU];
     load_a();
     load(buf, 0);
