@@ -10,16 +10,19 @@
 //   ffn1:  H = silu(A Wg) * (A Wu),  A = x gathered through sorted_token
 //   ffn2:  Y = H Wd
 //
-// bf16 path (gfx950 MFMA): 256-thread workgroups (4 wavefronts in 2x2) compute a
-// 128-row tile with v_mfma_f32_32x32x16_bf16, fp32 accumulation, K step 32,
-// double-buffered LDS. The weights are stored N-contiguous ([K, N] row-major),
-// while MFMA wants 8 consecutive K values per lane for both operands, so each
-// thread loads a 4(K) x 8(N) block of B with 16-byte loads, transposes it in
-// registers and writes it K-contiguous into LDS. ffn1 keeps the gate and up
-// accumulators of the same (row, column) in the same lane, so silu(g)*u is
-// applied in registers and H is written once in bf16.
-//
-// fp32 path: 64x64 tiles on the vector ALUs, 4x4 outputs per thread.
+// Paths, chosen per call by ffn_plan:
+//   - bf16, aligned shapes: the streaming MFMA kernel (ffn_mfma_stream_kernel, mainloop in
+//     stream_gemm.h) on 128 x 256 or 128 x 512 tiles, global-to-LDS DMA, K split for few tokens;
+//   - bf16, one or two tokens: the skinny kernels (grouped_ffn_skinny.hip), weight streams on the
+//     vector ALUs;
+//   - bf16, other shapes: the generic MFMA kernel (ffn_mfma_kernel): 256-thread workgroups (4
+//     wavefronts in 2x2) on 128-row tiles with v_mfma_f32_32x32x16_bf16, K step 32,
+//     double-buffered LDS; the weights are stored N-contiguous ([K, N] row-major) while MFMA wants
+//     8 consecutive K values per lane, so each thread loads a 4(K) x 8(N) block of B with 16-byte
+//     loads, transposes it in registers and writes it K-contiguous into LDS;
+//   - fp32: 64x64 tiles on the vector ALUs, 4x4 outputs per thread (ffn_f32_kernel).
+// In every path ffn1 keeps the gate and up sums of the same (row, column) together, so silu(g)*u
+// is applied in registers and H is written once.
 //
 // Row tiles come from a device-built tile list (group, first row), so the host
 // launches an upper bound of tiles without knowing the routing; surplus
