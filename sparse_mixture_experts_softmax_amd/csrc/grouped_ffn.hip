@@ -379,10 +379,29 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
   const int col_in = lane & 31;
   const int row_hi = (lane >> 5) * 4;
 
+  if (GATED && nsp > 1) {
+    // Split K, gate/up: every split stores its fp32 partial rows with plain stores and ends; the
+    // next kernel on the stream (gate_up_finish_kernel) adds them in split order and applies
+    // silu * up. This spares each workgroup the acknowledge / counter / reload round trips of the
+    // last-arriver sum below.
+    float* mine = p.part + (int64_t)split * p.part_sstride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t pc = (j >> 1) * p.ldh + n0 + wn * 64 + (j & 1) * 32 + col_in;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
+          if (row < mrows) mine[(G.row0 + m0 + row) * p.part_ld + pc] = acc[i][j][r];
+        }
+      }
+    return;
+  }
   if (nsp > 1) {
-    // Split K: every split stores its partial rows; the last to arrive (arrival counter per tile)
-    // adds all partials in split order -- the same order whichever split arrives last -- and runs
-    // the epilogue. The partials are written and read with device-scope (relaxed atomic) accesses,
+    // Split K (down product): every split stores its partial rows; the last to arrive (arrival
+    // counter per tile) adds all partials in split order -- the same order whichever split
+    // arrives last -- and runs the epilogue. The partials are written and read with device-scope (relaxed atomic) accesses,
     // which stay coherent across the XCDs' L2s; a store wait orders them before the counter.
     // (A device-scope fence instead would write back and invalidate the whole L2 of the XCD,
     // throwing away the weight tiles other workgroups are streaming through it.)
@@ -468,6 +487,42 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
     const int row = c / CH, ch = c - row * CH;
     if (row < mrows) *(uint4*)(out + row * ld + ch * 8) = *(const uint4*)(st + row * PITCH + ch * 16);
   }
+}
+
+// H rows of a gate/up product with K split (streaming MFMA or skinny kernels): each split's fp32
+// gate and up sums (row pitch 2 ldh: gate at column c, up at ldh + c) added in split order, then
+// silu(gate) * up in bf16.
+// Row i < T*k is a routed slot (I columns), the rest shared rows (I_s columns). grid: (ldh / 1024
+// rounded up, rows_total); four columns per thread.
+__global__ void __launch_bounds__(256)
+gate_up_finish_kernel(const float* __restrict__ part, int64_t sstride, int64_t part_ld, int ks, int64_t Tk,
+                             int I, int Is, int ldh, bf16_t* __restrict__ H) {
+  const int64_t row = blockIdx.y;
+  const int c4 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int N = row < Tk ? I : Is;
+  if (c4 >= N) return;
+  const float* q = part + row * part_ld + c4;
+  float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int B = 8;  // splits loaded together
+  for (int s0 = 0; s0 < ks; s0 += B) {
+    float4 a[B], b[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      if (s0 + j < ks) {
+        a[j] = *(const float4*)(q + (int64_t)(s0 + j) * sstride);
+        b[j] = *(const float4*)(q + (int64_t)(s0 + j) * sstride + ldh);
+      }
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      if (s0 + j < ks) {
+        g[0] += a[j].x; g[1] += a[j].y; g[2] += a[j].z; g[3] += a[j].w;
+        u[0] += b[j].x; u[1] += b[j].y; u[2] += b[j].z; u[3] += b[j].w;
+      }
+  }
+  uint2 o;
+  o.x = pack_bf16x2(silu_f32(g[0]) * u[0], silu_f32(g[1]) * u[1]);
+  o.y = pack_bf16x2(silu_f32(g[2]) * u[2], silu_f32(g[3]) * u[3]);
+  *(uint2*)(H + row * ldh + c4) = o;
 }
 
 // K splits for a product whose row x column tiles are expected to number `tiles`: double while
@@ -606,6 +661,13 @@ ffn_f32_kernel(F32Args p) {
 
 }  // namespace
 
+hipError_t launch_gate_up_finish(const float* part, int64_t sstride, int64_t part_ld, int ks, int64_t Tk,
+                                 int64_t rows_total, int I, int Is, int ldh, bf16_t* H, hipStream_t s) {
+  const dim3 grid((unsigned)((ldh + 1023) / 1024), (unsigned)rows_total);
+  hipLaunchKernelGGL(gate_up_finish_kernel, grid, dim3(256), 0, s, part, sstride, part_ld, ks, Tk, I, Is, ldh, H);
+  return hipGetLastError();
+}
+
 int ffn_tile_rows(const moe_dims& dm) { return dm.dtype == MOE_F32 ? kF32BM : kMfmaBM; }
 
 hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s) {
@@ -741,6 +803,10 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     else
       hipLaunchKernelGGL(ffn_mfma_kernel<true>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (stream_ok && a.splits > 1 &&
+        (e = launch_gate_up_finish(a.part, a.part_sstride, a.part_ld, a.splits, dm.T * dm.k, L.rows_total, dm.I,
+                                   dm.I_shared, L.ldh, (bf16_t*)H, s)) != hipSuccess)
+      return e;
     if ((e = prof->end(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
     // ffn2: down
     a.a_src = (const bf16_t*)H;

@@ -252,7 +252,7 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
 
   if (GATED && p.ks > 1) {
     // gate/up with K split: the fp32 partials go out with plain stores and the follow-up kernel
-    // (skinny_gate_up_finish_kernel, next on the stream) adds them and applies silu * up. Ending
+    // (gate_up_finish_kernel, next on the stream) adds them and applies silu * up. Ending
     // here spares every workgroup the store-acknowledge, counter and reload round trips of the
     // last-arriver sum (T = 1 at the large shape: ~17 us of the product's ~135 us).
     if (mine) {
@@ -308,53 +308,15 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
   }
 }
 
-// H rows of the skinny gate/up product with K split: each split's fp32 gate and up sums (row
-// pitch 2 ldh: gate at column c, up at ldh + c) added in split order, then silu(gate) * up in bf16.
-// Row i < T*k is a routed slot (I columns), the rest shared rows (I_s columns). grid: (ldh / 1024
-// rounded up, rows_total); four columns per thread.
-__global__ void __launch_bounds__(256)
-skinny_gate_up_finish_kernel(const float* __restrict__ part, int64_t sstride, int64_t part_ld, int ks, int64_t Tk,
-                             int I, int Is, int ldh, bf16_t* __restrict__ H) {
-  const int64_t row = blockIdx.y;
-  const int c4 = (blockIdx.x * 256 + threadIdx.x) * 4;
-  const int N = row < Tk ? I : Is;
-  if (c4 >= N) return;
-  const float* q = part + row * part_ld + c4;
-  float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
-  constexpr int B = 8;  // splits loaded together
-  for (int s0 = 0; s0 < ks; s0 += B) {
-    float4 a[B], b[B];
-#pragma unroll
-    for (int j = 0; j < B; ++j)
-      if (s0 + j < ks) {
-        a[j] = *(const float4*)(q + (int64_t)(s0 + j) * sstride);
-        b[j] = *(const float4*)(q + (int64_t)(s0 + j) * sstride + ldh);
-      }
-#pragma unroll
-    for (int j = 0; j < B; ++j)
-      if (s0 + j < ks) {
-        g[0] += a[j].x; g[1] += a[j].y; g[2] += a[j].z; g[3] += a[j].w;
-        u[0] += b[j].x; u[1] += b[j].y; u[2] += b[j].z; u[3] += b[j].w;
-      }
-  }
-  uint2 o;
-  o.x = pack_bf16x2(silu_f32(g[0]) * u[0], silu_f32(g[1]) * u[1]);
-  o.y = pack_bf16x2(silu_f32(g[2]) * u[2], silu_f32(g[3]) * u[3]);
-  *(uint2*)(H + row * ldh + c4) = o;
-}
-
 template <int R>
 void launch_pair(const SkinnyArgs& a1, const SkinnyArgs& a2, unsigned grid1, unsigned grid2, int64_t rows_total,
                  hipStream_t s, const Prof* prof, hipError_t& e) {
   if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return;
   hipLaunchKernelGGL((ffn_skinny_kernel<true, R>), dim3(grid1), dim3(256), 0, s, a1);
   if ((e = hipGetLastError()) != hipSuccess) return;
-  if (a1.ks > 1) {
-    const dim3 fg((unsigned)((a1.ldh + 1023) / 1024), (unsigned)rows_total);
-    hipLaunchKernelGGL(skinny_gate_up_finish_kernel, fg, dim3(256), 0, s, a1.part, a1.part_sstride, a1.part_ld, a1.ks,
-                       a1.T * a1.k, a1.I, a1.Is, a1.ldh, a1.out);
-    if ((e = hipGetLastError()) != hipSuccess) return;
-  }
+  if (a1.ks > 1 && (e = launch_gate_up_finish(a1.part, a1.part_sstride, a1.part_ld, a1.ks, a1.T * a1.k, rows_total,
+                                                 a1.I, a1.Is, a1.ldh, a1.out, s)) != hipSuccess)
+    return;
   if ((e = prof->end(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return;
   if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return;
   hipLaunchKernelGGL((ffn_skinny_kernel<false, R>), dim3(grid2), dim3(256), 0, s, a2);

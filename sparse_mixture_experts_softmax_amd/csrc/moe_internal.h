@@ -200,6 +200,11 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
                               const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
                               hipStream_t s, const Prof* prof = nullptr, bool tiles_ready = false);
 
+// gate/up product with K split: H rows from the splits' fp32 partials (gate at column c, up at
+// ldh + c of part[split][row], row pitch part_ld), added in split order, then silu(gate) * up
+hipError_t launch_gate_up_finish(const float* part, int64_t sstride, int64_t part_ld, int ks, int64_t Tk,
+                                 int64_t rows_total, int I, int Is, int ldh, bf16_t* H, hipStream_t s);
+
 // few tokens (plan.skinny): both products on the vector ALUs with the weights streamed by plain
 // 16-byte loads; tile list and counters as for launch_grouped_ffn
 hipError_t launch_ffn_skinny(const moe_dims& dm, const Layout& L, const FfnPlan& P, const void* x,
