@@ -250,7 +250,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d, WORLD_SIZE %d)"
+        print("bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus %d, WORLD_SIZE %d)"
               % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
