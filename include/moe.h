@@ -4,9 +4,9 @@
  * One MoE block maps each token's hidden vector x_t (length d) to an output
  * vector of the same length. The block is the one the Qwen3.6 / Qwen3.8-Max
  * pages describe:
- *   - a linear router gives one score (logit) per expert ("a small linear
- *     network that takes the token embedding and produces one score per
- *     expert": Qwen3.6 neural-network explorer page, section on the MoE router);
+ *   - a linear router gives one score (logit) per expert from the token's
+ *     embedding (Qwen3.6 neural-network explorer page, section on the MoE
+ *     router);
  *   - a softmax over the experts and a per-token top-k keep the k most probable
  *     experts (same section), optionally renormalising their k probabilities to
  *     sum to one;
@@ -79,7 +79,10 @@ typedef struct {
 /* Bytes of device workspace every entry point below needs for these dims. */
 moe_status moe_workspace_size(const moe_dims* dims, size_t* bytes);
 
-/* Router and softmax top-k (explorer page, router section).
+/* Router and softmax top-k (Qwen3.6 neural-network explorer page, router section: a small
+ * linear network maps the token's embedding to one score per expert, a softmax turns the scores
+ * into one probability per expert, and the K most probable experts are kept; the configuration
+ * listing on the Qwen3.8-Max architecture page gives num_experts and num_experts_per_tok).
  *   x          [T, d]   dtype
  *   w_router   [d, E]   float; logits l = x w_router (+ router_bias) in fp32
  *   router_bias[E]      float or NULL
@@ -89,7 +92,13 @@ moe_status moe_workspace_size(const moe_dims* dims, size_t* bytes);
  *   topk_w     [T, k]   float, softmax probabilities over all E experts of the
  *                       kept ones; divided by their sum when renormalize = 1
  *   topk_gap   [T]      float or NULL: l_(k) - l_(k+1) (+inf when k = E), the
- *                       margin that decides the selection */
+ *                       margin that decides the selection
+ *   ws, ws_bytes        the caller's workspace (moe_workspace_size): the logits are summed over
+ *                       K splits, whose fp32 partials [splits][T][E] live there, as do the three
+ *                       bf16 parts of w_router the MFMA path multiplies by (an exact split of each
+ *                       fp32 weight). The function allocates nothing, so the scratch comes in here.
+ * Errors: MOE_ERR_INVALID_ARG for bad dims or pointers, MOE_ERR_WORKSPACE for a missing or short
+ * ws, MOE_ERR_HIP if a launch fails; nothing is enqueued on any error. */
 moe_status moe_router_topk(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
                            int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws, size_t ws_bytes,
                            hipStream_t stream);
@@ -105,7 +114,9 @@ moe_status moe_router_topk_stats(const moe_dims* dims, const void* x, const floa
                                  int32_t* topk_idx, float* topk_w, float* topk_gap, int32_t* expert_counts,
                                  float* prob_mean, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Dispatch: group the T*k (token, expert) pairs by expert.
+/* Dispatch: group the T*k (token, expert) pairs by expert (explorer page, router section: the
+ * token is sent to each of the experts it keeps, so every expert receives the tokens that chose
+ * it and can process them together).
  *   topk_idx        [T, k]  int32 (from moe_router_topk); a token's indices in
  *                           [0, E) must be distinct, as top-k selection makes them
  * Outputs:
@@ -115,11 +126,16 @@ moe_status moe_router_topk_stats(const moe_dims* dims, const void* x, const floa
  *                           tokens ascend (stable)
  *   slot_of         [T*k]   int32, slot_of[t*k + j] = sorted slot of (t, topk_idx[t, j])
  * Pairs whose index lies outside [0, E) are skipped: their slot_of is -1 and
- * offsets[E] counts only the others (moe_combine then leaves them out). */
+ * offsets[E] counts only the others (moe_combine then leaves them out).
+ * ws: the caller's workspace (per-chunk expert counts). Errors as moe_router_topk. */
 moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets,
                        int32_t* sorted_token, int32_t* slot_of, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Routed and shared SwiGLU experts, each row once, unweighted.
+/* Routed and shared SwiGLU experts, each row once, unweighted. Each expert is
+ * y = (silu(x Wg) * (x Wu)) Wd with no biases (Qwen3.8-Max architecture page, config.json listing:
+ * hidden_act "silu", moe_intermediate_size I, shared_expert_intermediate_size I_shared; the overview
+ * page's parameter table counts 3 d I parameters per expert); the shared expert runs on every token
+ * (explorer page, router section: one expert that is always active).
  *   x               [T, d]      dtype
  *   expert_offsets, sorted_token: from moe_permute
  *   wg, wu          [E, d, I]   dtype; wd [E, I, d] dtype
@@ -133,15 +149,21 @@ moe_status moe_grouped_ffn(const moe_dims* dims, const void* x, const int32_t* e
                            const void* wg_s, const void* wu_s, const void* wd_s, void* y, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
-/* Weighted combine plus shared expert:
+/* Weighted combine plus shared expert (explorer page, router section: the kept experts' outputs
+ * are summed with their routing weights; the always-active shared expert's output is added, with
+ * no weight since the pages name no gate for it):
  *   out[t] = sum_j topk_w[t, j] * y[slot_of[t*k + j]]  +  y[T*k + t] (if I_shared > 0)
  * summed in fp32 in the order j = 0..k-1 then the shared row; out [T, d] dtype.
  * Pairs with slot_of = -1 contribute nothing. */
 moe_status moe_combine(const moe_dims* dims, const void* y, const int32_t* slot_of, const float* topk_w, void* out,
                        hipStream_t stream);
 
-/* The whole block in one call: router/top-k, dispatch, experts, combine.
- * topk_idx, topk_w, topk_gap may be NULL (then kept in the workspace). */
+/* The whole block in one call: router/top-k, dispatch, experts, combine -- the MoE block of the
+ * explorer page's router section (scores, softmax, the K most probable experts weighted, plus the
+ * shared expert) with the expert shapes of the Qwen3.8-Max config.json listing.
+ * x [T, d] in, out [T, d] out (out may not alias x); the other arguments as in the step entry
+ * points above. topk_idx, topk_w, topk_gap may be NULL (then kept in the workspace). Errors as
+ * moe_router_topk. */
 moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
                        const void* wg, const void* wu, const void* wd, const void* wg_s, const void* wu_s,
                        const void* wd_s, void* out, int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws,
@@ -155,7 +177,8 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_route
  *
  * moe_quantize_fp8: w [batch, K, N] (dtype, N-contiguous as the bf16 expert weights are stored)
  *   -> q: batch x K*N uint8 codes in code tiles, scale [batch, N] float; s[n] is the smallest
- *   power of two with max_k |w[k, n]| / s[n] <= 448 (1 for an all-zero column).
+ *   power of two with max_k |w[k, n]| / s[n] <= 448 (1 for an all-zero column). A column that
+ *   holds a non-finite weight gets a NaN scale (its non-finite weights get the NaN code).
  *   Code tiles: 128 columns x 32 K values, 4096 bytes, ordered by (column tile, K tile), i.e.
  *   tile (n / 128) * (K / 32) + k / 32 of each matrix. In a tile, with r = n % 128,
  *   j = k % 32, h = j / 16: Q[n, k] is byte 32 r + 16 (h ^ ((r / 8) % 2)) + j % 16.

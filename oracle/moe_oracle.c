@@ -244,7 +244,6 @@ int moe_oracle_forward(int64_t T, int32_t d, int32_t E, int32_t k, int32_t I, in
   return err;
 }
 
-/* Threads the parallel regions above use (OpenMP's current maximum). */
 /* v rounded to bf16, round to nearest with ties to even, from the exact double
  * (not through fp32): significand scaled to [128, 256), rounded by rint in the
  * default rounding mode, scaled back. Normal range only (|v| >= 2^-126 or 0). */
@@ -284,4 +283,5 @@ int moe_oracle_rmsnorm(int64_t T, int32_t d, int32_t dtype, const void* x, const
   return ORACLE_OK;
 }
 
+/* Threads the parallel regions above use (OpenMP's current maximum). */
 int moe_oracle_threads(void) { return omp_get_max_threads(); }

@@ -74,13 +74,12 @@ struct MfmaArgs {
   int64_t T;
   int d, E, k, I, Is, ldh;
   int n_ntiles;
-  // split-K (streaming kernel): splits > 1 -> fp32 partial rows part[split][row][part_ld] and
-  // one arrival counter per tile
+  // split-K (streaming gate/up kernel): splits > 1 -> fp32 partial rows part[split][row][part_ld],
+  // added by gate_up_finish_kernel
   int splits;
   int balance;  // streaming kernel: split each group's rows evenly over its row tiles
   float* part;
   int64_t part_ld, part_sstride;
-  int32_t* cnt;
 };
 
 // Transpose a 4(K) x 8(N) block of bf16 (rows r[0..3], each 8 N-consecutive
@@ -379,71 +378,25 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
   const int col_in = lane & 31;
   const int row_hi = (lane >> 5) * 4;
 
-  if (GATED && nsp > 1) {
-    // Split K, gate/up: every split stores its fp32 partial rows with plain stores and ends; the
-    // next kernel on the stream (gate_up_finish_kernel) adds them in split order and applies
-    // silu * up. This spares each workgroup the acknowledge / counter / reload round trips of the
-    // last-arriver sum below.
-    float* mine = p.part + (int64_t)split * p.part_sstride;
+  if constexpr (GATED) {
+    if (nsp > 1) {
+      // Split K, gate/up: every split stores its fp32 partial rows with plain stores and ends; the
+      // next kernel on the stream (gate_up_finish_kernel) adds them in split order and applies
+      // silu * up. (The down product is launched with one split.)
+      float* mine = p.part + (int64_t)split * p.part_sstride;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t pc = (j >> 1) * p.ldh + n0 + wn * 64 + (j & 1) * 32 + col_in;
+        for (int j = 0; j < 4; ++j) {
+          const int64_t pc = (j >> 1) * p.ldh + n0 + wn * 64 + (j & 1) * 32 + col_in;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
-          if (row < mrows) mine[(G.row0 + m0 + row) * p.part_ld + pc] = acc[i][j][r];
-        }
-      }
-    return;
-  }
-  if (nsp > 1) {
-    // Split K (down product): every split stores its partial rows; the last to arrive (arrival
-    // counter per tile) adds all partials in split order -- the same order whichever split
-    // arrives last -- and runs the epilogue. The partials are written and read with device-scope (relaxed atomic) accesses,
-    // which stay coherent across the XCDs' L2s; a store wait orders them before the counter.
-    // (A device-scope fence instead would write back and invalidate the whole L2 of the XCD,
-    // throwing away the weight tiles other workgroups are streaming through it.)
-    auto pcol = [&](int j) {
-      return GATED ? (j >> 1) * p.ldh + n0 + wn * 64 + (j & 1) * 32 + col_in : n0 + wn * 128 + j * 32 + col_in;
-    };
-    float* mine = p.part + (int64_t)split * p.part_sstride;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
-          if (row < mrows)
-            __hip_atomic_store(&mine[(G.row0 + m0 + row) * p.part_ld + pcol(j)], acc[i][j][r], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
-    __syncthreads();  // ... and every wave's; every wave is past its mainloop: the LDS stages are free
-    int* last = (int*)smem;
-    if (tid == 0)
-      *last = __hip_atomic_fetch_add(&p.cnt[L], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsp - 1;
-    __syncthreads();
-    if (!*last) return;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
-          if (row < mrows) {
-            const int64_t at = (G.row0 + m0 + row) * p.part_ld + pcol(j);
-            float v = 0.f;
-            for (int sp = 0; sp < nsp; ++sp)
-              v += sp == split ? acc[i][j][r]
-                               : __hip_atomic_load(&p.part[sp * p.part_sstride + at], __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            acc[i][j][r] = v;
+          for (int r = 0; r < 16; ++r) {
+            const int row = sub_row(wm, i) + (r >> 2) * 8 + row_hi + (r & 3);
+            if (row < mrows) mine[(G.row0 + m0 + row) * p.part_ld + pc] = acc[i][j][r];
           }
         }
+      return;
+    }
   }
 
   // Epilogue through LDS: the output tile (silu(g)*u for gate/up) is staged in bf16, row-major, in
@@ -701,7 +654,7 @@ FfnPlan ffn_plan(const moe_dims& dm) {
   // Split the gate/up product's K when its tiles alone would leave CUs idle (few tokens: each
   // touched expert is one row tile). Expected row tiles: one per group that can be touched, plus
   // the full ones. The down product has 4x the column tiles and measured no faster split.
-  P.s1 = P.s2 = 1;
+  P.s1 = 1;
   if (P.stream) {
     const int64_t groups = (Tk < dm.E ? Tk : dm.E) + has_shared;
     const int64_t mt = groups + rows_total / kMfmaBM;
@@ -755,7 +708,6 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
   const FfnPlan P = ffn_plan(dm);
   const bool stream_ok = P.stream;
   const int bm = ffn_tile_rows(dm);
-  int32_t* cnt = (int32_t*)(ws + L.ffn_cnt);
   hipError_t e;
   if (!tiles_ready && (e = launch_build_tiles(dm, L, offsets, ws, s)) != hipSuccess) return e;
 
@@ -796,7 +748,6 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.splits = P.s1;
     a.part_ld = P.part_cols1;
     a.part_sstride = L.rows_total * P.part_cols1;
-    a.cnt = cnt;
     if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
     if (stream_ok)
       launch_stream<true>(P.wn1, (unsigned)(max_mt * a.n_ntiles * a.splits), s, a);
@@ -816,10 +767,10 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.w1_s = nullptr;
     a.out = (bf16_t*)y;
     a.n_ntiles = P.nt2;
-    a.splits = P.s2;
-    a.part_ld = P.part_cols2;
-    a.part_sstride = L.rows_total * P.part_cols2;
-    a.cnt = cnt + L.ffn_cnt_each;
+    a.splits = 1;
+    a.part = nullptr;
+    a.part_ld = 0;
+    a.part_sstride = 0;
     if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
     if (stream_ok)
       launch_stream<false>(P.wn2, (unsigned)(max_mt * a.n_ntiles * a.splits), s, a);

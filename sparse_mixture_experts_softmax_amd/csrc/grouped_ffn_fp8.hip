@@ -22,6 +22,7 @@
 // workgroups per CU. Schedule, DMA and the A operand as in stream_gemm.h. The B stage holds two
 // code tiles (gate and up at the same columns, or two adjacent column tiles of W_d); B instruction
 // q (0..7; wave w issues 2w, 2w+1) copies bytes 1024 (q % 4) .. +1023 of tile q / 4, 16 per lane.
+#include "fp8_codec.h"
 #include "moe_internal.h"
 #include "stream_gemm.h"
 
@@ -285,36 +286,6 @@ __global__ void __launch_bounds__(256, 2) ffn_fp8_stream_kernel(Fp8Args p) {
 // ------------------------------------------------------------------------------------------
 // quantiser: w [batch, K, N] -> codes [batch] x (N / 128 x K / 32 tiles of 4 KB), scales [batch, N]
 // ------------------------------------------------------------------------------------------
-// nearest e4m3 code of v (|v| <= 448), ties to even, by rounding exactly scaled values to integers
-__device__ __forceinline__ uint8_t e4m3_rne(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  int code;
-  if (a < 0x1p-6f) {
-    code = (int)rintf(a * 512.0f);  // multiples of 2^-9; 8 is the smallest normal's code
-  } else {
-    int e;
-    frexpf(a, &e);  // a in [2^(e-1), 2^e)
-    const int E = e - 1;
-    int m = (int)rintf(ldexpf(a, 3 - E)) - 8;  // 0 .. 8
-    int EE = E;
-    if (m == 8) {
-      m = 0;
-      EE += 1;
-    }
-    code = ((EE + 7) << 3) | m;
-  }
-  return code == 0 ? (uint8_t)0 : (uint8_t)(code | sign);
-}
-
-// smallest e with |amax| 2^-e <= 448 (0 for amax = 0): the column's scale is 2^e
-__device__ __forceinline__ int scale_exp(float amax) {
-  if (!(amax > 0.f)) return 0;
-  int e = ilogbf(amax) - 10;
-  while (ldexpf(amax, -e) > 448.0f) ++e;
-  return e;
-}
-
 template <typename WT>
 __device__ __forceinline__ float wval(const WT* p, int64_t i);
 template <>
@@ -339,14 +310,21 @@ quantize_fp8_kernel(const WT* __restrict__ w, int K, int N, uint8_t* __restrict_
   const int64_t b = blockIdx.y;
   const WT* wb = w + b * (int64_t)K * N;
   float amax = 0.f;
-  for (int k = r0; k < K; k += 4) amax = fmaxf(amax, fabsf(wval(wb, (int64_t)k * N + n)));
+  // maximum of magnitudes that keeps a NaN (fmaxf would drop it): a column holding a non-finite
+  // weight gets a NaN scale
+  for (int k = r0; k < K; k += 4) {
+    const float v = fabsf(wval(wb, (int64_t)k * N + n));
+    amax = (v > amax || isnan(v)) ? v : amax;
+  }
   red[r0][c] = amax;
   __syncthreads();
   if (r0 == 0) {
-    const float m = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
-    const int e = scale_exp(m);
+    float m = red[0][c];
+    for (int i = 1; i < 4; ++i) m = (red[i][c] > m || isnan(red[i][c])) ? red[i][c] : m;
+    int e;
+    const bool finite = fp8::scale_exp(m, &e);
     sexp[c] = e;
-    scale[b * N + n] = ldexpf(1.0f, e);
+    scale[b * N + n] = finite ? ldexpf(1.0f, e) : __builtin_nanf("");
   }
   __syncthreads();
   uint8_t* qb = q + b * (int64_t)N * K;
@@ -366,7 +344,7 @@ quantize_fp8_kernel(const WT* __restrict__ w, int K, int N, uint8_t* __restrict_
       uint32_t wd[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        wd[i >> 2] |= (uint32_t)e4m3_rne(ldexpf(tile[kk - k0 + i][cc], -e)) << (8 * (i & 3));
+        wd[i >> 2] |= (uint32_t)fp8::e4m3_rne(ldexpf(tile[kk - k0 + i][cc], -e)) << (8 * (i & 3));
       const int r = nn & 127;
       const int h = (kk >> 4) & 1;
       const int64_t at = ((int64_t)(nn >> 7) * (K >> 5) + (kk >> 5)) * 4096 + r * 32 + 16 * (h ^ ((r >> 3) & 1));

@@ -148,14 +148,15 @@ Layout make_layout(const moe_dims& dm) {
   const FfnPlan P = ffn_plan(dm);
   size_t part = 0;
   if (P.s1 > 1) part = (size_t)P.s1 * L.rows_total * P.part_cols1 * 4;
-  if (P.s2 > 1) part = std::max(part, (size_t)P.s2 * L.rows_total * P.part_cols2 * 4);
   if (P.skinny && P.ks1 > 1) part = std::max(part, (size_t)P.ks1 * L.rows_total * P.part_cols1 * 4);
   if (P.skinny && P.ks2 > 1) part = std::max(part, (size_t)P.ks2 * L.rows_total * P.part_cols2 * 4);
   L.ffn_part = take(part);
-  int64_t per_tile = (P.s1 > 1 || P.s2 > 1) ? std::max(P.nt1, P.nt2) : 0;
-  if (P.skinny) per_tile = std::max<int64_t>(per_tile, std::max(P.cb1, P.cb2));
+  // arrival counters of the skinny down product's K split (last-arriver sum), one per
+  // (group, column block)
+  const int64_t per_tile = P.skinny ? std::max(P.cb1, P.cb2) : 0;
   L.ffn_cnt_each = L.max_tiles * per_tile;
   L.ffn_cnt = take((size_t)2 * L.ffn_cnt_each * 4);
+  L.hnorm = take((size_t)T * dm.d * esz);
   L.total = off;
   return L;
 }
@@ -469,10 +470,10 @@ moe_status moe_forward_block(const moe_dims* dims, const void* x, const void* ga
   MOE_TRY(check_ptr(gamma, 16, "gamma"));
   const Layout L = make_layout(dm);
   MOE_TRY(check_ws(dm, L, ws, ws_bytes));
-  // the normalised rows live at the start of the Y buffer: the router and the gate/up product
-  // read them before the down product writes Y
+  // the normalised rows have a workspace region of their own: the router and the gate/up product
+  // read them, and no other step writes there
   char* w = (char*)ws;
-  void* h = w + L.Y;
+  void* h = w + L.hnorm;
   hipError_t e = launch_rmsnorm(dm, x, gamma, eps, h, stream);
   if (e != hipSuccess) return hip_fail(e, "moe_forward_block/rmsnorm");
   return forward_rows(dm, L, h, x, w_router, router_bias, wg, wu, wd, wg_s, wu_s, wd_s, out, topk_idx, topk_w,

@@ -64,7 +64,8 @@ struct Layout {
   size_t tile_group, tile_m0, tile_count, H, Y;
   size_t probs, stat_p, stat_c;  // router statistics: probabilities [T, E], per-chunk sums and counts
   size_t ffn_part;      // split-K partial sums of the grouped GEMMs (small T only)
-  size_t ffn_cnt;       // split-K arrival counters: gate/up tiles, then down tiles
+  size_t ffn_cnt;       // arrival counters of the skinny down product's K split
+  size_t hnorm;         // moe_forward_block: the normalised rows [T, d] the router and experts read
   int64_t ffn_cnt_each; // counters per product
   size_t total;
 };
@@ -72,13 +73,13 @@ struct Layout {
 Layout make_layout(const moe_dims& dm);
 
 // How the bf16 grouped GEMMs run for these dims: streaming kernel or not, tile widths (wave
-// columns), column tiles and K splits of the gate/up and of the down product.
+// columns), column tiles, and K splits of the gate/up product.
 struct FfnPlan {
   bool stream;
   bool balance;  // equal row tiles per group
   int wn1, wn2;
   int nt1, nt2;
-  int s1, s2;
+  int s1;  // K splits of the MFMA gate/up product (the MFMA down product is never split)
   int64_t part_cols1, part_cols2;  // columns of the fp32 partial rows (gate | up, or d)
   // few tokens (every group <= kSkinnyMaxT rows): the skinny kernels, 256-column blocks, K in
   // splits of kc1 / kc2 rows (multiples of 8, <= kSkinnyMaxKC)
