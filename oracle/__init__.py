@@ -33,6 +33,8 @@ def _load():
         lib.moe_oracle_forward.restype = ctypes.c_int
         lib.moe_oracle_rmsnorm.argtypes = [i64, i32, i32, p, p, ctypes.c_double, p]
         lib.moe_oracle_rmsnorm.restype = ctypes.c_int
+        lib.moe_oracle_expert_rows.argtypes = [i64, i32, i32, i32, p, p, p, p, p, p]
+        lib.moe_oracle_expert_rows.restype = ctypes.c_int
         lib.moe_oracle_threads.argtypes = []
         lib.moe_oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -123,6 +125,67 @@ def forward(x, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renorm=True, bias=None
                                     out.ctypes.data, idx.ctypes.data, w.ctypes.data, gap.ctypes.data)
     if rc != 0:
         raise RuntimeError("moe_oracle_forward failed: %d" % rc)
+    return out, idx, w, gap
+
+
+def expert_rows(x, rows, experts):
+    """One expert output per (row, expert) pair, unweighted: y[p] = (silu(x_r Wg) * (x_r Wu)) Wd for
+    r = rows[p] and experts[p] = (Wg [d,n], Wu [d,n], Wd [n,d]). Returns float64 [len(rows), d]."""
+    dt = _dtype_of(x)
+    npdt = np.float32 if dt == F32 else np.uint16
+    x = _c(x, npdt)
+    T, d = x.shape
+    rows = _c(rows, np.int64)
+    npairs = len(rows)
+    y = np.empty((npairs, d), np.float64)
+    if npairs == 0:
+        return y
+    assert rows.min() >= 0 and rows.max() < T
+    keep = {}
+
+    def ptrs(which):
+        arr = (ctypes.c_void_p * npairs)()
+        for i, ex in enumerate(experts):
+            m = ex[which]
+            key = (id(m), which)
+            if key not in keep:
+                keep[key] = _c(m, npdt)
+            arr[i] = keep[key].ctypes.data
+        return arr
+
+    n = experts[0][0].shape[1]
+    for ex in experts:
+        assert ex[0].shape == (d, n) and ex[1].shape == (d, n) and ex[2].shape == (n, d)
+    rc = _load().moe_oracle_expert_rows(npairs, d, n, dt, x.ctypes.data, rows.ctypes.data, ptrs(0), ptrs(1), ptrs(2),
+                                        y.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("moe_oracle_expert_rows failed: %d" % rc)
+    return y
+
+
+def forward_by_expert(x, w_router, k, load_expert, shared=None, renorm=True, bias=None, batch=16):
+    """The whole block, as forward() defines it, for inputs whose expert weights need not all be in
+    host memory at once: out_t = sum over the token's kept experts j of w_tj y_j(x_t), plus the
+    shared expert's output s(x_t). The routing is router()'s; the experts the tokens select are
+    visited `batch` at a time in ascending index, load_expert(e) returning (Wg [d,I], Wu [d,I],
+    Wd [I,d]), and each adds its weighted outputs to its tokens' rows (so a token's k terms are summed
+    in ascending expert index rather than in descending logit; the sum is in double either way).
+    shared: (Wg_s, Wu_s, Wd_s) or None.
+
+    Returns (out float64 [T,d], topk_idx, topk_w, gap) like forward()."""
+    idx, w, gap, _ = router(x, w_router, k, renorm=renorm, bias=bias)
+    T, d = np.asarray(x).shape
+    out = np.zeros((T, d), np.float64)
+    needed = np.unique(idx)
+    for b0 in range(0, len(needed), batch):
+        group = needed[b0:b0 + batch]
+        weights = {int(e): load_expert(int(e)) for e in group}
+        tt, jj = np.nonzero(np.isin(idx, group))
+        y = expert_rows(x, tt, [weights[int(e)] for e in idx[tt, jj]])
+        np.add.at(out, tt, w[tt, jj][:, None] * y)
+        del weights
+    if shared is not None:
+        out += expert_rows(x, np.arange(T), [shared] * T)
     return out, idx, w, gap
 
 

@@ -244,6 +244,44 @@ int moe_oracle_forward(int64_t T, int32_t d, int32_t E, int32_t k, int32_t I, in
   return err;
 }
 
+/* One expert's output for a list of (token row, expert) pairs: for pair p,
+ *   y[p] = (silu(x_r W_g) * (x_r W_u)) W_d  with r = rows[p] and the pair's own
+ * expert matrices wg[p], wu[p] ([d, n]) and wd[p] ([n, d]) -- the expert of the
+ * header, token by token, with no weighting. y: [npairs, d] double. The caller
+ * forms the weighted sums; this lets it visit the experts a few at a time when
+ * all of their weights do not fit in host memory at once. */
+int moe_oracle_expert_rows(int64_t npairs, int32_t d, int32_t n, int32_t dtype, const void* x, const int64_t* rows,
+                           const void* const* wg, const void* const* wu, const void* const* wd, double* y) {
+  if (npairs < 0 || d <= 0 || n <= 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return ORACLE_ERR_ARG;
+  if (npairs > 0 && (!x || !rows || !wg || !wu || !wd || !y)) return ORACLE_ERR_ARG;
+  int err = 0;
+  const int32_t rowlen = n > d ? n : d;
+#pragma omp parallel
+  {
+    double* xr = (double*)malloc(sizeof(double) * (size_t)d);
+    double* tmp = (double*)malloc(sizeof(double) * (3 * (size_t)n + (size_t)rowlen));
+    const int ok = xr && tmp;
+    if (!ok) {
+#pragma omp atomic write
+      err = ORACLE_ERR_NOMEM;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t p = 0; p < npairs; ++p) {
+      if (!ok) continue;
+      if (!wg[p] || !wu[p] || !wd[p] || rows[p] < 0) {
+#pragma omp atomic write
+        err = ORACLE_ERR_ARG;
+        continue;
+      }
+      widen_row(xr, x, dtype, (size_t)rows[p], (size_t)d);
+      swiglu_ffn(xr, d, n, dtype, wg[p], wu[p], wd[p], y + p * d, tmp);
+    }
+    free(xr);
+    free(tmp);
+  }
+  return err;
+}
+
 /* v rounded to bf16, round to nearest with ties to even, from the exact double
  * (not through fp32): significand scaled to [128, 256), rounded by rint in the
  * default rounding mode, scaled back. Normal range only (|v| >= 2^-126 or 0). */

@@ -51,9 +51,9 @@ moe_status check_dims(const moe_dims* dm) {
   if (dm->I < 8 || dm->I % 8) return fail(MOE_ERR_INVALID_ARG, "I = %d is not a positive multiple of 8", dm->I);
   if (dm->I_shared < 0 || dm->I_shared % 8)
     return fail(MOE_ERR_INVALID_ARG, "I_shared = %d is not 0 or a positive multiple of 8", dm->I_shared);
-  const long long rows = (long long)dm->T * dm->k + dm->T;
-  if (dm->T > 0 && rows >= (1LL << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "T*k + T = %lld does not fit in int32", rows);
+  // T*k + T < 2^31, tested without forming the product (T may be near INT64_MAX)
+  if (dm->T > ((1LL << 31) - 1) / (dm->k + 1))
+    return fail(MOE_ERR_UNSUPPORTED, "T*k + T with T = %lld, k = %d does not fit in int32", (long long)dm->T, dm->k);
   return MOE_OK;
 }
 

@@ -303,6 +303,48 @@ def test_per_expert_pointers_allow_missing_unselected_experts():
         oracle.forward(x, wr, missing, missing, missing, wgs, wus, wds, k=cfg.k)
 
 
+def test_expert_rows_match_numpy_per_pair():
+    # the per-pair expert output against the dense numpy SwiGLU, for pairs that repeat rows and
+    # experts in any order (fp32 and bf16 inputs)
+    rng = np.random.default_rng(21)
+    x, wr, wg, wu, wd, *_ = rand_layer(rng, 9, 40, 5, 24, 0)
+    rows = np.array([3, 0, 3, 8, 1, 1])
+    es = [4, 2, 2, 0, 4, 1]
+    y = oracle.expert_rows(x, rows, [(wg[e], wu[e], wd[e]) for e in es])
+    for p, (r, e) in enumerate(zip(rows, es)):
+        np.testing.assert_allclose(y[p], dense_swiglu(x[r:r + 1], wg[e], wu[e], wd[e])[0], rtol=1e-12, atol=1e-13)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    bits = lambda a: (a.view(np.uint32) >> 16).astype(np.uint16)  # noqa: E731
+    yb = oracle.expert_rows(xb, rows, [(bits(wg[e]), bits(wu[e]), bits(wd[e])) for e in es])
+    xw = oracle.widen(xb)
+    for p, (r, e) in enumerate(zip(rows, es)):
+        ref = dense_swiglu(xw[r:r + 1], oracle.widen(bits(wg[e])), oracle.widen(bits(wu[e])), oracle.widen(bits(wd[e])))
+        np.testing.assert_allclose(yb[p], ref[0], rtol=1e-12, atol=1e-13)
+    assert oracle.expert_rows(x, np.zeros(0, np.int64), []).shape == (0, 40)
+
+
+@pytest.mark.parametrize("renorm,shared,batch", [(True, True, 3), (False, True, 1), (True, False, 64)])
+def test_forward_by_expert_equals_forward(renorm, shared, batch):
+    # the expert-major visit order (bounded host memory for the large shapes) gives the per-token
+    # definition's result up to the order of a k-term double sum, and the same routing
+    rng = np.random.default_rng(22)
+    T, d, E, k, I, Is = 40, 48, 12, 3, 32, 24
+    x, wr, wg, wu, wd, wgs, wus, wds = rand_layer(rng, T, d, E, I, Is if shared else 0)
+    bias = rng.standard_normal(E).astype(np.float32) * 0.3
+    ref, ridx, rw, rgap = oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, k=k, renorm=renorm, bias=bias)
+    loaded = []
+
+    def load(e):
+        loaded.append(e)
+        return wg[e], wu[e], wd[e]
+
+    out, idx, w, gap = oracle.forward_by_expert(x, wr, k, load, shared=(wgs, wus, wds) if shared else None,
+                                                renorm=renorm, bias=bias, batch=batch)
+    assert np.array_equal(idx, ridx) and np.array_equal(w, rw) and np.array_equal(gap, rgap)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-13 * np.abs(ref).max())
+    assert sorted(loaded) == sorted(set(ridx.ravel().tolist()))  # each selected expert loaded once
+
+
 # --------------------------------------------------------------------------------------------
 # zero-centred RMSNorm in front of the block, and the residual add around it
 # --------------------------------------------------------------------------------------------
