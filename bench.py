@@ -5,12 +5,16 @@ One step = one moe_forward call: router GEMM + softmax top-k, dispatch, routed a
 experts, weighted combine -- the whole forward pass of the block over one batch of synthetic input
 that is already resident in HBM. Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload mid|decode|prefill|skew|tiny]
+  python bench.py [--steps K] [--warmup W] [--workload prefill|decode|mid|skew|tiny]
 
-The default workload is the mid-size bf16 layer (T=4096, d=2048, E=256, k=8, I=512, one shared
-expert with I=512). The dominant kernel (grouped gate/up GEMM) is timed with HIP events recorded
-around its launch inside every timed step; its algorithmic bytes / FLOPs give the roofline fraction.
-The CPU oracle is timed on a bounded token sample of the same workload as a reported baseline.
+The default workload is the prefill-shaped large layer (T=16384, d=8192, E=512, k=10,
+I=I_shared=2048, bf16, fp32 router), bound by the bf16 matrix cores; the line's "decode" key holds
+the decode-shaped run (T=32, the first 32 rows of the same input) on the same weights in the same
+process, bound by HBM. Step times are per-step HIP events on the library's stream; `value` is
+tokens / median step time. The dominant kernel (grouped gate/up GEMM) is timed with HIP events
+recorded around its launch inside every timed step; its algorithmic FLOPs (prefill) or bytes
+(decode) over its median launch time give the roofline fraction. The CPU oracle is timed on a
+bounded token sample of the headline workload as a reported baseline.
 """
 import argparse
 import ctypes
@@ -228,17 +232,132 @@ def sweep(steps, warmup):
                                      "I_shared": cfg.Is, "dtype": "bf16"}}), flush=True)
 
 
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+class Run:
+    """One forward variant over fixed inputs: bf16/fp32 experts, FP8 experts, or the block with
+    its norm and residual."""
+
+    def __init__(self, moe, cfg, x, inp, ws, out, dims, fp8=None, gamma=None):
+        self.moe, self.cfg, self.x, self.inp, self.ws, self.out, self.dims = moe, cfg, x, inp, ws, out, dims
+        self.fp8, self.gamma = fp8, gamma
+
+    def __call__(self, return_routing=False):
+        moe, cfg, inp = self.moe, self.cfg, self.inp
+        kw = dict(renormalize=bool(cfg.renorm), router_bias=inp["bias"], ws=self.ws, dims=self.dims,
+                  return_routing=return_routing)
+        if not return_routing:
+            kw["out"] = self.out
+        if self.fp8 is not None:
+            return moe.moe_forward_fp8(self.x, inp["w_router"], self.fp8, cfg.k, **kw)
+        if self.gamma is not None:
+            return moe.moe_forward_block(self.x, self.gamma, inp["w_router"], inp["wg"], inp["wu"], inp["wd"],
+                                         inp["wg_s"], inp["wu_s"], inp["wd_s"], cfg.k, **kw)
+        return moe.moe_forward(self.x, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"], inp["wu_s"],
+                               inp["wd_s"], cfg.k, **kw)
+
+
+def measure(run, lib, hip, stream, steps, warmup):
+    """Times `steps` forward calls after `warmup` untimed ones: per-step HIP events on the
+    library's stream (the steps run back to back; event k ends step k and starts step k+1), and
+    the dominant kernel's own pair of timing-only events inside every step. Returns (step times,
+    kernel times, wall seconds of the timed region, routing of the input)."""
+    import torch
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    marks = [hip.create(timing_only=True) for _ in range(steps + 1)]
+    pairs = [(hip.create(timing_only=True), hip.create(timing_only=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    hip.record(marks[0], stream)
+    for i, (a, b) in enumerate(pairs):
+        rc = lib.moe_profile_next_forward(KERNEL_FFN_GATE_UP, a, b)
+        if rc != 0:
+            raise RuntimeError(lib.moe_last_error().decode())
+        run()
+        hip.record(marks[i + 1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [hip.ms(marks[i], marks[i + 1]) for i in range(steps)]
+    kern_ms = [hip.ms(a, b) for a, b in pairs]
+    for ev in marks:
+        hip.destroy(ev)
+    for a, b in pairs:
+        hip.destroy(a)
+        hip.destroy(b)
+    _, idx, _, _ = run(return_routing=True)
+    torch.cuda.synchronize()
+    return step_ms, kern_ms, wall, idx.cpu().numpy()
+
+
+def roofline(wl, syn, cfg, kb, kf, kern_med_ms, fp8):
+    """The dominant kernel against its bound: HBM when its algorithmic bytes take longer at 8 TB/s
+    than its FLOPs at the matrix cores' peak, the matrix cores otherwise."""
+    peak_flops = wl.BF16_MFMA_PEAK_FLOPS if cfg.dtype == syn.BF16 else wl.FP32_VECTOR_PEAK_FLOPS
+    t_s = kern_med_ms * 1e-3
+    if kb / wl.HBM_PEAK_BPS >= kf / peak_flops:
+        roof = {"bound": "hbm", "achieved": kb / t_s / 1e9, "peak": wl.HBM_PEAK_BPS / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma" if cfg.dtype == syn.BF16 else "alu", "achieved": kf / t_s / 1e12,
+                "peak": peak_flops / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = ("ffn_fp8_stream_kernel<true, 4> (gate/up, e4m3 weights)" if fp8 else
+                      "ffn_mfma_stream_kernel<true, ...> (gate/up)" if cfg.dtype == syn.BF16 else "ffn_f32_kernel<true>")
+    roof["kernel_ms"] = kern_med_ms
+    roof["algorithmic_bytes"] = kb
+    roof["algorithmic_flops"] = kf
+    return roof
+
+
+def summarize(wl, syn, cfg, step_ms, kern_ms, idx, fp8):
+    """Tokens/s, the layer's fractions of both peaks, and the dominant kernel's roofline."""
+    touched = wl.touched_experts(idx, cfg.E)
+    ms = median(step_ms)
+    if fp8:
+        kb = wl.ffn1_algorithmic_bytes_fp8(cfg.T, cfg.d, cfg.I, cfg.Is, touched)
+        lb = wl.algorithmic_bytes_fp8(cfg.T, cfg.d, cfg.E, cfg.I, cfg.Is, touched)
+    else:
+        kb = wl.ffn1_algorithmic_bytes(cfg.T, cfg.d, cfg.I, cfg.Is, cfg.dtype, touched)
+        lb = wl.algorithmic_bytes(cfg.T, cfg.d, cfg.E, cfg.I, cfg.Is, cfg.dtype, touched)
+    kf = wl.ffn1_flops(cfg.T, cfg.d, cfg.k, cfg.I, cfg.Is)
+    lf = wl.expert_flops(cfg.T, cfg.d, cfg.k, cfg.I, cfg.Is)
+    peak_flops = wl.BF16_MFMA_PEAK_FLOPS if cfg.dtype == syn.BF16 else wl.FP32_VECTOR_PEAK_FLOPS
+    roof = roofline(wl, syn, cfg, kb, kf, median(kern_ms), fp8)
+    layer = {"touched_experts": touched, "algorithmic_bytes": lb, "expert_flops": lf,
+             "router_flops": wl.router_flops(cfg.T, cfg.d, cfg.E),
+             "hbm_frac": lb / (ms * 1e-3) / wl.HBM_PEAK_BPS, "mfma_frac": lf / (ms * 1e-3) / peak_flops,
+             "ms_per_step_mean": sum(step_ms) / len(step_ms), "ms_per_step_min": min(step_ms),
+             "ms_per_step_max": max(step_ms)}
+    return ms, cfg.T / (ms * 1e-3), roof, layer
+
+
+def workload_name(cfg, block=False, fp8=False):
+    return "%s MoE layer: T=%d, d=%d, E=%d, k=%d, I=%d, shared I=%d, %s, fp32 router%s%s" % (
+        cfg.name, cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.Is, cfg.dtype_name,
+        ", Zipf(%.1f) router bias" % cfg.zipf_alpha if cfg.zipf_alpha else "",
+        ", RMSNorm in front and residual add" if block else ", FP8 e4m3 expert weights" if fp8 else "")
+
+
+DECODE_STEPS = 50  # the decode leg's timed steps (its median is over 50 runs)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mid", choices=["tiny", "mid", "decode", "prefill", "skew"])
+    ap.add_argument("--workload", default="prefill", choices=["tiny", "mid", "decode", "prefill", "skew"])
     ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count T")
     ap.add_argument("--fp8", action="store_true",
                     help="expert weights in FP8 (e4m3, power-of-two column scales), quantised before timing")
     ap.add_argument("--block", action="store_true",
                     help="time the block between its neighbours: zero-centred RMSNorm in front, residual add after")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode leg of the prefill workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy, the reference kernel for HBM byte counters")
@@ -260,6 +379,9 @@ def main():
     if args.sweep:
         sweep(args.steps, args.warmup)
         return
+    if args.fp8 and args.block:
+        print("bench.py: --fp8 and --block are separate entry points; pick one", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
@@ -279,11 +401,7 @@ def main():
     dims = moe.dims_for(x, inp["w_router"], inp["wg"], inp["wg_s"], cfg.k, bool(cfg.renorm))
     ws = moe.workspace(dims, dev)
     out = torch.empty_like(x)
-
     gamma = syn.device_gamma(cfg, device=dev) if args.block else None
-    if args.fp8 and args.block:
-        print("bench.py: --fp8 and --block are separate entry points; pick one", file=sys.stderr)
-        sys.exit(2)
     fp8 = None
     if args.fp8:
         fp8 = moe.Fp8Experts(inp["wg"], inp["wu"], inp["wd"], inp["wg_s"], inp["wu_s"], inp["wd_s"])
@@ -291,60 +409,34 @@ def main():
             inp[key] = None
         torch.cuda.empty_cache()
 
-    def step():
-        if fp8 is not None:
-            moe.moe_forward_fp8(x, inp["w_router"], fp8, cfg.k, renormalize=bool(cfg.renorm), router_bias=inp["bias"],
-                                ws=ws, out=out, dims=dims)
-        elif args.block:
-            moe.moe_forward_block(x, gamma, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"],
-                                  inp["wu_s"], inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm),
-                                  router_bias=inp["bias"], ws=ws, out=out, dims=dims)
-        else:
-            moe.moe_forward(x, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"], inp["wu_s"],
-                            inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm), router_bias=inp["bias"], ws=ws, out=out,
-                            dims=dims)
-
     stream = torch.cuda.current_stream(dev).cuda_stream
     hip = HipEvents()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    run = Run(moe, cfg, x, inp, ws, out, dims, fp8=fp8, gamma=gamma)
+    print("bench: timing %d steps after %d warm-up steps" % (args.steps, args.warmup), file=sys.stderr, flush=True)
+    step_ms, kern_ms, wall, idx = measure(run, lib, hip, stream, args.steps, args.warmup)
+    ms, tps, roof, layer = summarize(wl, syn, cfg, step_ms, kern_ms, idx, fp8 is not None)
+    plain = fp8 is None and not args.block and args.tokens is None
+    roof["traffic"] = traffic_for(cfg.name) if plain else None
 
-    K = args.steps
-    pairs = [(hip.create(timing_only=True), hip.create(timing_only=True)) for _ in range(K)]
-    t_beg, t_end = hip.create(), hip.create()
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    hip.record(t_beg, stream)
-    for a, b in pairs:
-        rc = lib.moe_profile_next_forward(KERNEL_FFN_GATE_UP, a, b)
-        if rc != 0:
-            raise RuntimeError(lib.moe_last_error().decode())
-        step()
-    hip.record(t_end, stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = hip.ms(t_beg, t_end)
-    kern_ms = [hip.ms(a, b) for a, b in pairs]
-    kern_avg_ms = sum(kern_ms) / len(kern_ms)
-    for a, b in pairs:
-        hip.destroy(a)
-        hip.destroy(b)
-
-    # routing of this input, for the algorithmic work actually required
-    if fp8 is not None:
-        _, idx, _, _ = moe.moe_forward_fp8(x, inp["w_router"], fp8, cfg.k, renormalize=bool(cfg.renorm),
-                                           router_bias=inp["bias"], return_routing=True, ws=ws, dims=dims)
-    elif args.block:
-        _, idx, _, _ = moe.moe_forward_block(x, gamma, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"],
-                                             inp["wu_s"], inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm),
-                                             router_bias=inp["bias"], return_routing=True, ws=ws, dims=dims)
-    else:
-        _, idx, _, _ = moe.moe_forward(x, inp["w_router"], inp["wg"], inp["wu"], inp["wd"], inp["wg_s"],
-                                       inp["wu_s"], inp["wd_s"], cfg.k, renormalize=bool(cfg.renorm),
-                                       router_bias=inp["bias"], return_routing=True, ws=ws, dims=dims)
-    torch.cuda.synchronize()
-    touched = wl.touched_experts(idx.cpu().numpy(), cfg.E)
+    # the decode leg: the first 32 rows of the same input on the same weights (the decode
+    # workload's x is exactly those rows), its own median over DECODE_STEPS steps
+    decode = None
+    if args.workload == "prefill" and args.tokens is None and not args.no_decode:
+        dcfg = syn.CONFIGS["decode"]
+        if fp8 is not None:
+            dcfg = dcfg.with_(name="decode")
+        xd = x[:dcfg.T]
+        ddims = moe.MoeDims(dcfg.T, dims.d, dims.E, dims.k, dims.I, dims.I_shared, dims.dtype, dims.renormalize)
+        dws = moe.workspace(ddims, dev)
+        drun = Run(moe, dcfg, xd, inp, dws, torch.empty_like(xd), ddims, fp8=fp8,
+                   gamma=gamma)
+        print("bench: decode leg, %d steps" % DECODE_STEPS, file=sys.stderr, flush=True)
+        dstep, dkern, dwall, didx = measure(drun, lib, hip, stream, DECODE_STEPS, args.warmup)
+        dms, dtps, droof, dlayer = summarize(wl, syn, dcfg, dstep, dkern, didx, fp8 is not None)
+        droof["traffic"] = traffic_for("decode") if (fp8 is None and not args.block) else None
+        decode = {"workload": workload_name(dcfg, args.block, fp8 is not None), "T": dcfg.T, "steps": DECODE_STEPS,
+                  "ms_per_step": dms, "tokens_per_s": dtps, "layer_hbm_frac": dlayer["hbm_frac"],
+                  "roofline": droof, "layer": dlayer}
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -354,55 +446,19 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ms_per_step = total_ms / K
-    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
-    if fp8 is not None:
-        kb = wl.ffn1_algorithmic_bytes_fp8(cfg.T, cfg.d, cfg.I, cfg.Is, touched, cfg.k)
-    else:
-        kb = wl.ffn1_algorithmic_bytes(cfg.T, cfg.d, cfg.I, cfg.Is, cfg.dtype, touched, cfg.k)
-    kf = wl.ffn1_flops(cfg.T, cfg.d, cfg.k, cfg.I, cfg.Is)
-    peak_flops = wl.BF16_MFMA_PEAK_FLOPS if cfg.dtype == syn.BF16 else wl.FP32_VECTOR_PEAK_FLOPS
-    t_s = kern_avg_ms * 1e-3
-    if kb / wl.HBM_PEAK_BPS >= kf / peak_flops:
-        roof = {"bound": "hbm", "achieved": kb / t_s / 1e9, "peak": wl.HBM_PEAK_BPS / 1e9, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma" if cfg.dtype == syn.BF16 else "alu", "achieved": kf / t_s / 1e12,
-                "peak": peak_flops / 1e12, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None if (fp8 is not None or args.block or args.tokens is not None) else traffic_for(cfg.name)
-    roof["kernel"] = ("ffn_fp8_stream_kernel<true, 4> (gate/up, e4m3 weights)" if fp8 is not None else
-                      "ffn_mfma_stream_kernel<true, ...> (gate/up)" if cfg.dtype == syn.BF16 else "ffn_f32_kernel<true>")
-    roof["kernel_ms"] = kern_avg_ms
-    roof["algorithmic_bytes"] = kb
-    roof["algorithmic_flops"] = kf
-
-    if fp8 is not None:
-        lb = wl.algorithmic_bytes_fp8(cfg.T, cfg.d, cfg.E, cfg.I, cfg.Is, touched)
-    else:
-        lb = wl.algorithmic_bytes(cfg.T, cfg.d, cfg.E, cfg.I, cfg.Is, cfg.dtype, touched)
-    lf = wl.expert_flops(cfg.T, cfg.d, cfg.k, cfg.I, cfg.Is)
-    layer = {"touched_experts": touched, "algorithmic_bytes": lb, "expert_flops": lf,
-             "router_flops": wl.router_flops(cfg.T, cfg.d, cfg.E),
-             "hbm_frac": lb / (ms_per_step * 1e-3) / wl.HBM_PEAK_BPS,
-             "mfma_frac": lf / (ms_per_step * 1e-3) / peak_flops}
-
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(cfg, CPU_SAMPLE[cfg.name])
 
     res = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": tps, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if cfg.dtype == syn.BF16 else "f32", "data": "synthetic",
-        "config": {"workload": "%s MoE layer: T=%d, d=%d, E=%d, k=%d, I=%d, shared I=%d, %s, fp32 router%s%s"
-                   % (cfg.name, cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.Is, cfg.dtype_name,
-                      ", Zipf(%.1f) router bias" % cfg.zipf_alpha if cfg.zipf_alpha else "",
-                      ", RMSNorm in front and residual add" if args.block else
-                      ", FP8 e4m3 expert weights" if fp8 is not None else ""),
+        "config": {"workload": workload_name(cfg, args.block, fp8 is not None),
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "I": cfg.I, "I_shared": cfg.Is,
                    "renormalize": cfg.renorm, "seed": cfg.seed},
-        "roofline": roof, "layer": layer, "cpu_baseline": cpu, "wall_s_timed": wall,
+        "roofline": roof, "layer": layer, "decode": decode, "cpu_baseline": cpu, "wall_s_timed": wall,
     }
     print(json.dumps(res), flush=True)
 

@@ -37,10 +37,12 @@ def algorithmic_bytes(T, d, E, I, Is, dtype, touched):
     return touched * expert_params(d, I) * s + (expert_params(d, Is) * s if Is else 0) + 4 * d * E + 2 * T * d * s
 
 
-def ffn1_algorithmic_bytes(T, d, I, Is, dtype, touched, k):
-    """Gate/up step: W_g and W_u of the touched experts and the shared expert, x in, H out."""
+def ffn1_algorithmic_bytes(T, d, I, Is, dtype, touched, k=None):
+    """Gate/up step: W_g and W_u of the touched experts and of the shared expert, and x read once.
+    The intermediate H it writes is implementation traffic (a fused block would keep it on chip)
+    and is not counted."""
     s = elem_bytes(dtype)
-    return (touched * 2 * d * I + (2 * d * Is if Is else 0)) * s + T * d * s + (T * k * I + T * Is) * s
+    return (touched * 2 * d * I + (2 * d * Is if Is else 0)) * s + T * d * s
 
 
 def algorithmic_bytes_fp8(T, d, E, I, Is, touched):
@@ -50,10 +52,10 @@ def algorithmic_bytes_fp8(T, d, E, I, Is, touched):
     return w + 4 * d * E + 2 * T * d * 2
 
 
-def ffn1_algorithmic_bytes_fp8(T, d, I, Is, touched, k):
-    """Gate/up step with e4m3 weights: codes and scales of W_g, W_u, x in, H out (bf16)."""
-    return (touched * 2 * (d * I + 4 * I) + ((2 * (d * Is + 4 * Is)) if Is else 0)) + T * d * 2 + \
-        (T * k * I + T * Is) * 2
+def ffn1_algorithmic_bytes_fp8(T, d, I, Is, touched, k=None):
+    """Gate/up step with e4m3 weights: codes and column scales of W_g and W_u (touched experts and
+    the shared expert) and x read once (bf16); H is not counted."""
+    return (touched * 2 * (d * I + 4 * I) + ((2 * (d * Is + 4 * Is)) if Is else 0)) + T * d * 2
 
 
 def expert_flops(T, d, k, I, Is):

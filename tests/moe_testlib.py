@@ -84,22 +84,51 @@ def oracle_full(h, cfg):
                           renorm=bool(cfg.renorm), bias=h["bias"])
 
 
-def oracle_sample(cfg, tokens):
-    """Oracle outputs for the given token rows of a config, generating only the x rows, the router
-    and the experts those tokens select on the host."""
-    tokens = np.asarray(tokens, dtype=np.int64)
+def coverage_tokens(idx, E, n_min, budget, seed, band=64):
+    """Tokens to check against the oracle so that every 64-row band of every group's rows in the
+    grouped GEMMs -- each routed expert's slots (tokens ascending, as the dispatch orders them)
+    and the shared expert's T rows -- holds at least one checked row: every row tile, its first,
+    middle and last (partial) ones alike, and every 32-row sub-tile pair of the waves in it.
+    Greedy maximum coverage (each step takes the token adding the most uncovered bands; seeded
+    tie-break), then seeded random tokens up to n_min. Returns (sorted tokens, covered fraction)."""
+    T, k = idx.shape
+    flat_e = idx.reshape(-1).astype(np.int64)
+    flat_t = np.repeat(np.arange(T), k)
+    order = np.lexsort((flat_t, flat_e))
+    counts = np.bincount(flat_e, minlength=E)
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    rank = np.empty(T * k, np.int64)
+    rank[order] = np.arange(T * k) - offs[flat_e[order]]
+    nb = (counts + band - 1) // band
+    boff = np.concatenate([[0], np.cumsum(nb)])
+    pid = np.concatenate([(boff[flat_e] + rank // band).reshape(T, k), (boff[E] + np.arange(T) // band)[:, None]],
+                         axis=1)
+    covered = np.zeros(boff[E] + (T + band - 1) // band, bool)
+    rng = np.random.default_rng(seed)
+    tie = rng.random(T) * 1e-3
+    chosen = np.zeros(T, bool)
+    while chosen.sum() < budget:
+        gain = (~covered[pid]).sum(axis=1) + tie
+        gain[chosen] = -1.0
+        t = int(np.argmax(gain))
+        if gain[t] < 1.0:
+            break
+        chosen[t] = True
+        covered[pid[t]] = True
+    rest = np.flatnonzero(~chosen)
+    extra = max(0, min(n_min, T) - int(chosen.sum()))
+    chosen[rng.choice(rest, size=extra, replace=False)] = True
+    return np.flatnonzero(chosen), float(covered.mean())
+
+
+def oracle_tokens(cfg, tokens):
+    """The oracle on the given token rows of a configuration, visiting the selected experts a few at
+    a time (each generated on the host when its turn comes), so that host memory stays bounded at
+    the large shapes."""
     x = syn.host_x(cfg, rows=tokens)
-    wr = syn.host_router(cfg)
-    bias = syn.router_bias(cfg)
-    idx, _, _, _ = oracle.router(x, wr, cfg.k, renorm=bool(cfg.renorm), bias=bias)
-    need = sorted(set(idx.ravel().tolist()))
-    wg = [None] * cfg.E
-    wu = [None] * cfg.E
-    wd = [None] * cfg.E
-    for e in need:
-        wg[e], wu[e], wd[e] = syn.host_expert(cfg, e)
-    wgs, wus, wds = syn.host_shared(cfg)
-    return oracle.forward(x, wr, wg, wu, wd, wgs, wus, wds, cfg.k, renorm=bool(cfg.renorm), bias=bias)
+    return oracle.forward_by_expert(x, syn.host_router(cfg), cfg.k, lambda e: syn.host_expert(cfg, e),
+                                    shared=syn.host_shared(cfg) if cfg.Is else None, renorm=bool(cfg.renorm),
+                                    bias=syn.router_bias(cfg), batch=16)
 
 
 # final rounding of an output row to the element type, relative (half an ulp at bf16 / fp32)

@@ -4,8 +4,8 @@ import pytest
 
 import oracle
 import synthetic as syn
-from moe_testlib import (compare, device_from_host, host_inputs, oracle_full, oracle_sample, run_forward, to_host,
-                         torch_dtype)
+from moe_testlib import (compare, coverage_tokens, device_from_host, host_inputs, oracle_full, oracle_tokens, run_forward,
+                         to_host, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -258,31 +258,36 @@ def _device_inputs(cfg, cache={}):
     return dev
 
 
-def _full_size_check(torch, name, n_sample, T=None):
+def _full_size_check(torch, name, n_min, budget, T=None):
     cfg = syn.CONFIGS[name] if T is None else syn.CONFIGS[name].with_(T=T)
     _say("config", cfg)
     dev = _device_inputs(cfg)
     out, idx, w, gap = run_forward(dev, cfg)
     torch.cuda.synchronize()
-    idx_h, w_h = to_host(idx), to_host(w)
+    idx_h, w_h, out_h = to_host(idx), to_host(w), to_host(out)
     # properties on every token
     assert idx_h.min() >= 0 and idx_h.max() < cfg.E
     s = np.sort(idx_h, axis=1)
     assert np.all(s[:, 1:] != s[:, :-1]), "repeated expert within a token"
     np.testing.assert_allclose(w_h.sum(axis=1), 1.0, atol=1e-5)
-    assert np.all(np.isfinite(to_host(out)))
-    # oracle on a seeded token sample
-    rng = np.random.default_rng(1234)
-    tokens = np.sort(rng.choice(cfg.T, size=min(n_sample, cfg.T), replace=False))
-    ref_out, ref_idx, ref_w, ref_gap = oracle_sample(cfg, tokens)
-    st = compare(cfg, to_host(out)[tokens], idx_h[tokens], w_h[tokens], ref_out, ref_idx, ref_w, ref_gap, name)
+    assert np.all(np.isfinite(out_h))
+    # the oracle on every token, or on tokens covering every row band of every group
+    if n_min >= cfg.T:
+        tokens, cov = np.arange(cfg.T), 1.0
+    else:
+        tokens, cov = coverage_tokens(idx_h, cfg.E, n_min, budget, seed=1234)
+    _say(name, "checking", len(tokens), "tokens against the oracle; 64-row band coverage %.4f" % cov)
+    ref_out, ref_idx, ref_w, ref_gap = oracle_tokens(cfg, tokens)
+    st = compare(cfg, out_h[tokens], idx_h[tokens], w_h[tokens], ref_out, ref_idx, ref_w, ref_gap, name)
     load = np.bincount(idx_h.ravel(), minlength=cfg.E)
-    _say(name, st, "touched experts", int((load > 0).sum()), "max load", int(load.max()))
-    return cfg, idx_h, load
+    _say(name, st, "max rel err %.3e" % st["rel"], "touched experts", int((load > 0).sum()), "max load",
+         int(load.max()))
+    return cfg, idx_h, load, cov
 
 
-def test_mid_config_router_all_tokens_and_sampled_outputs(torch):
-    cfg, idx_h, load = _full_size_check(torch, "mid", 384)
+def test_mid_config_router_all_tokens_and_covering_outputs(torch):
+    cfg, idx_h, load, cov = _full_size_check(torch, "mid", 384, 1024)
+    assert cov == 1.0
     # router + top-k on every token against the oracle
     x = syn.host_x(cfg)
     ref_idx, _, ref_gap, _ = oracle.router(x, syn.host_router(cfg), cfg.k)
@@ -291,8 +296,8 @@ def test_mid_config_router_all_tokens_and_sampled_outputs(torch):
     _say("mid flagged tokens", int((~ok).sum()))
 
 
-def test_decode_config(torch):
-    cfg, idx_h, load = _full_size_check(torch, "decode", 8)
+def test_decode_config_every_token(torch):
+    cfg, idx_h, load, cov = _full_size_check(torch, "decode", 32, 32)
     assert (load > 0).sum() > 150
 
 
@@ -300,15 +305,17 @@ def test_decode_config(torch):
 def test_decode_shape_few_tokens(torch, T):
     # the large shape at T <= 2 runs the skinny kernels, at T = 3 the MFMA kernels with K split;
     # every token against the oracle
-    _full_size_check(torch, "decode", T, T=T)
+    _full_size_check(torch, "decode", T, T, T=T)
 
 
-def test_prefill_config(torch):
-    _full_size_check(torch, "prefill", 8)
+def test_prefill_config_covering_every_row_band(torch):
+    cfg, idx_h, load, cov = _full_size_check(torch, "prefill", 256, 640)
+    assert cov == 1.0
 
 
-def test_skew_config(torch):
-    cfg, idx_h, load = _full_size_check(torch, "skew", 8)
+def test_skew_config_covering_every_row_band(torch):
+    cfg, idx_h, load, cov = _full_size_check(torch, "skew", 256, 640)
+    assert cov == 1.0
     L = syn.zipf_targets(cfg.T, cfg.E, cfg.k, cfg.zipf_alpha)
     # the two heaviest experts take (almost) every token; popularity bands follow the Zipf targets
     assert load[0] >= 0.99 * cfg.T and load[1] >= 0.99 * cfg.T

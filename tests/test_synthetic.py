@@ -67,3 +67,27 @@ def test_zipf_targets_water_filled():
     r = np.arange(1, 513)[free]
     ratio = L[free] * r ** 1.2
     np.testing.assert_allclose(ratio, ratio[0], rtol=1e-12)
+
+
+def test_coverage_tokens_cover_every_row_band():
+    # the token selection of the full-size parity tests: on a routing shaped like the prefill and
+    # skew workloads, every 64-row band of every expert's slots and of the shared expert's rows
+    # holds a selected token, and at least n_min tokens are selected
+    from moe_testlib import coverage_tokens
+    rng = np.random.default_rng(0)
+    for T, E, k, skew in [(4096, 128, 6, False), (2048, 128, 6, True)]:
+        logits = rng.standard_normal((T, E))
+        if skew:
+            logits += 2.0 * np.log(1.0 / np.arange(1, E + 1))
+        idx = np.argsort(-logits, axis=1)[:, :k].astype(np.int32)
+        tokens, cov = coverage_tokens(idx, E, 300, 2000, seed=1)
+        assert cov == 1.0 and len(tokens) >= 300 and len(set(tokens.tolist())) == len(tokens)
+        # brute-force check of the claim
+        flat_e, flat_t = idx.reshape(-1), np.repeat(np.arange(T), k)
+        sel = set(tokens.tolist())
+        for e in range(E):
+            toks = np.sort(flat_t[flat_e == e])
+            for b0 in range(0, len(toks), 64):
+                assert sel & set(toks[b0:b0 + 64].tolist()), (e, b0)
+        for b0 in range(0, T, 64):
+            assert sel & set(range(b0, min(T, b0 + 64)))
