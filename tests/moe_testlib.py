@@ -11,6 +11,7 @@ import synthetic as syn
 
 TOL = {syn.F32: 1e-5, syn.BF16: 2e-2}
 WEIGHT_ATOL = 1e-5
+RESULTS = []  # (label, max relative error, tokens checked, tokens flagged) of every comparison
 
 
 def torch_dtype(cfg):
@@ -178,5 +179,6 @@ def compare(cfg, out, idx, w, ref_out, ref_idx, ref_w, ref_gap, label="", residu
         err = float(np.max(diff)) if ok.any() else 0.0
         worst = float(np.max(diff - bound)) if ok.any() else 0.0
         assert worst <= 0.0, "%s: |out-ref| exceeds tol*max|moe ref| + rounding by %g" % (label, worst)
+    RESULTS.append((label, err / ref_max if ref_max else 0.0, int(T), int(flagged.sum())))
     return dict(flagged=int(flagged.sum()), max_err=err, max_ref=ref_max, rel=err / ref_max if ref_max else 0.0,
                 weight_err=werr)
