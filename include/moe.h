@@ -225,6 +225,26 @@ moe_status moe_forward_block(const moe_dims* dims, const void* x, const void* ga
                              int32_t* topk_idx, float* topk_w, float* topk_gap, void* ws, size_t ws_bytes,
                              hipStream_t stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same block, with the scratch space
+ * taken from a buffer the library holds in device memory instead of a caller's workspace.
+ *   - Arguments and results as moe_forward, without ws / ws_bytes.
+ *   - The buffer is MOE_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, a static device array of the
+ *     library's code object: every GPU the library runs on holds it until the process ends. Its
+ *     address is looked up once per device, on the first call made with that device current.
+ *   - Dims whose moe_workspace_size exceeds the buffer are rejected (MOE_ERR_UNSUPPORTED) before
+ *     anything is enqueued: e.g. the d = 8192, E = 512, k = 10, I = I_shared = 2048 layer up to
+ *     T = 64 tokens, the d = 2048, E = 256, k = 8, I = I_shared = 512 layer up to T = 1024.
+ *   - No call allocates or frees memory (no hipMalloc, hipFree or allocating library routine).
+ *   - All calls on one GPU share its buffer, and each call leaves its contents behind: calls that
+ *     overlap in time on one GPU (several streams, several threads) race and must be serialised
+ *     by the caller. The stream must belong to the current device. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
+                               const void* wg, const void* wu, const void* wd, const void* wg_s, const void* wu_s,
+                               const void* wd_s, void* out, int32_t* topk_idx, float* topk_w, float* topk_gap,
+                               hipStream_t stream);
+
 /* Instrumentation for timing one kernel of the path while the whole path runs.
  * The next moe_forward call made by the calling thread records `start` on its
  * stream immediately before launching the selected kernel and `stop` right

@@ -75,6 +75,8 @@ def load_library(path=None):
     lib.moe_forward_block.argtypes = [D, _P, _P, ctypes.c_double, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, ctypes.c_size_t, _P]
     lib.moe_forward_block.restype = st
+    lib.moe_forward_noalloc.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.moe_forward_noalloc.restype = st
     lib.moe_profile_next_forward.argtypes = [ctypes.c_int32, _P, _P]
     lib.moe_profile_next_forward.restype = st
     lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -342,6 +344,35 @@ def moe_forward(x, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renormalize=True, 
                            _ptr(ws), ws.numel(), _stream(x)))
     if return_routing:
         return out, idx, w, gap
+    return out
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(x, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, out, renormalize=True, router_bias=None,
+                        topk_idx=None, topk_w=None, topk_gap=None, dims=None):
+    """moe_forward with the library's own per-GPU scratch buffer (MOE_NOALLOC_SCRATCH_BYTES) in place
+    of a workspace, for callers that cannot allocate: it allocates nothing, so the caller passes
+    out [T, d] and, optionally, the routing outputs. Returns out."""
+    import torch
+    dims = _block_dims(x, w_router, wg, wu, wd, wg_s, wu_s, wd_s, k, renormalize, dims)
+    dt = _torch_dtype(dims.dtype)
+    _need_router(dims, dt, x, w_router, router_bias)
+    _need_experts(dims, dt, wg, wu, wd, wg_s, wu_s, wd_s)
+    _need(out, "out", dt, (dims.T, dims.d))
+    if topk_idx is not None:
+        _need(topk_idx, "topk_idx", torch.int32, (dims.T, dims.k))
+    if topk_w is not None:
+        _need(topk_w, "topk_w", torch.float32, (dims.T, dims.k))
+    if topk_gap is not None:
+        _need(topk_gap, "topk_gap", torch.float32, (dims.T,))
+    _one_device(x=x, w_router=w_router, router_bias=router_bias, wg=wg, wu=wu, wd=wd, wg_s=wg_s, wu_s=wu_s, wd_s=wd_s,
+                out=out, topk_idx=topk_idx, topk_w=topk_w, topk_gap=topk_gap)
+    lib = load_library()
+    _check(lib.moe_forward_noalloc(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(wg),
+                                   _ptr(wu), _ptr(wd), _ptr(wg_s), _ptr(wu_s), _ptr(wd_s), _ptr(out), _ptr(topk_idx),
+                                   _ptr(topk_w), _ptr(topk_gap), _stream(x)))
     return out
 
 

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -17,6 +18,14 @@ namespace {
 
 thread_local std::string g_last_error;
 thread_local Prof g_prof;  // one-shot request from moe_profile_next_forward
+
+// Scratch space of moe_forward_noalloc: one copy per GPU, placed in device memory when the code
+// object is loaded there. In host code `scratch` names a host-side stand-in, never the device
+// memory: host code uses only the per-device address hipGetSymbolAddress returns (g_scratch_at).
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_at[kMaxDevices] = {};
 
 moe_status fail(moe_status st, const char* fmt, ...) {
   char buf[512];
@@ -371,6 +380,26 @@ moe_status forward_rows(const moe_dims& dm, const Layout& L, const void* xin, co
   return MOE_OK;
 }
 
+// Device address of the current device's scratch array, looked up on its first use there.
+moe_status scratch_address(void** at) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward_noalloc/hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d: moe_forward_noalloc supports devices 0 .. %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_at[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "moe_forward_noalloc/hipGetSymbolAddress");
+    if (!p || ((uintptr_t)p & 255u))
+      return fail(MOE_ERR_HIP, "moe_forward_noalloc: scratch address %p is not 256-byte aligned", p);
+    g_scratch_at[dev] = p;
+  }
+  *at = g_scratch_at[dev];
+  return MOE_OK;
+}
+
 moe_status check_block_ptrs(const moe_dims& dm, const void* x, const float* w_router, const float* router_bias,
                             const void* wg, const void* wu, const void* wd, const void* wg_s, const void* wu_s,
                             const void* wd_s, const void* out, const int32_t* topk_idx, const float* topk_w,
@@ -407,6 +436,27 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const float* w_route
                            topk_gap));
   const Layout L = make_layout(dm);
   MOE_TRY(check_ws(dm, L, ws, ws_bytes));
+  return forward_rows(dm, L, x, nullptr, w_router, router_bias, wg, wu, wd, wg_s, wu_s, wd_s, out, topk_idx, topk_w,
+                      topk_gap, (char*)ws, stream);
+}
+
+moe_status moe_forward_noalloc(const moe_dims* dims, const void* x, const float* w_router, const float* router_bias,
+                               const void* wg, const void* wu, const void* wd, const void* wg_s, const void* wu_s,
+                               const void* wd_s, void* out, int32_t* topk_idx, float* topk_w, float* topk_gap,
+                               hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const moe_dims& dm = *dims;
+  if (dm.T == 0) return MOE_OK;
+  MOE_TRY(check_block_ptrs(dm, x, w_router, router_bias, wg, wu, wd, wg_s, wu_s, wd_s, out, topk_idx, topk_w,
+                           topk_gap));
+  const Layout L = make_layout(dm);
+  if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_forward_noalloc: these dims need %zu bytes of scratch, more than the %zu the library holds "
+                "per GPU (use moe_forward with a workspace)",
+                L.total, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  MOE_TRY(scratch_address(&ws));
   return forward_rows(dm, L, x, nullptr, w_router, router_bias, wg, wu, wd, wg_s, wu_s, wd_s, out, topk_idx, topk_w,
                       topk_gap, (char*)ws, stream);
 }

@@ -196,3 +196,20 @@ def test_binding_argument_lists_match_the_header():
         n = 0 if params in ("", "void") else len(params.split(","))
         at = getattr(lib, name).argtypes
         assert at is not None and len(at) == n, (name, n, at)
+
+
+def test_noalloc_forward_rejects_dims_beyond_its_scratch():
+    # checked on the host before the scratch buffer is looked up or anything is enqueued
+    import sparse_mixture_experts_softmax_amd as moe
+    lib = moe.load_library()
+    big = moe.MoeDims(4096, 8192, 512, 10, 2048, 2048, moe.MOE_BF16, 1)
+    p = ctypes.c_void_p(FAKE)
+    args = [p] * 10 + [None, None, None, None]
+    assert moe.moe_workspace_size(big) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(ctypes.byref(big), *args) == UNSUPPORTED
+    assert b"scratch" in lib.moe_last_error()
+    zero = moe.MoeDims(0, 8192, 512, 10, 2048, 2048, moe.MOE_BF16, 1)
+    assert lib.moe_forward_noalloc(ctypes.byref(zero), *([None] * 14)) == OK
+    # the decode-sized layer fits
+    assert moe.moe_workspace_size(moe.MoeDims(64, 8192, 512, 10, 2048, 2048, moe.MOE_BF16, 1)) <= \
+        moe.MOE_NOALLOC_SCRATCH_BYTES
