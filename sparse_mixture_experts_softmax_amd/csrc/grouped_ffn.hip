@@ -442,6 +442,147 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Tall-tile variant of the streaming kernel for groups of a few hundred rows (prefill-sized
+// batches): 160 x 512 tiles (stream_gemm.h, namespace tall), eight wavefronts each holding all
+// rows of the tile and 64 columns; for the gate/up product 32 gate and the matching 32 up columns.
+// A group's rows are split over ceil(rows / 160) row tiles in whole 32-row sub-tiles as evenly as
+// possible, so its row tiles do equal work and stream each weight panel in step. Tiles are ordered
+// (group, column tile, row tile) and remapped per XCD as in the 128-row kernel.
+// ------------------------------------------------------------------------------------------
+template <bool GATED, int S>
+__global__ void __launch_bounds__(512, 1) ffn_mfma_tall_kernel(MfmaArgs p) {
+  using namespace stream;
+  constexpr int TM = tall::ROWS;
+  constexpr int TN = GATED ? 256 : 512;  // output columns per tile
+  __shared__ __attribute__((aligned(1024))) char smem[S * tall::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int L = xcd_remap(blockIdx.x, *p.tile_count * p.n_ntiles);
+  if (L < 0) return;
+  const int probe = L / p.n_ntiles;
+  const int g = p.tile_group[probe];
+  const int first = probe - p.tile_m0[probe] / TM;  // the group's first row tile
+  const Group G = group_info(g, p.offsets, p.T, p.k, p.E, p.I, p.Is);
+  const int cnt = (G.rows + TM - 1) / TM;
+  const int local = L - p.n_ntiles * first;
+  const int nt = local / cnt;
+  const int mt = local % cnt;
+  // the group's S32 sub-tiles of 32 rows, split as evenly as possible over its cnt row tiles
+  const int S32 = (G.rows + 31) / 32;
+  const int m0 = 32 * (mt * S32 / cnt);
+  const int mrows = min(32 * ((mt + 1) * S32 / cnt), G.rows) - m0;
+
+  const int K = GATED ? p.d : G.n_inter;
+  const int N = GATED ? G.n_inter : p.d;
+  const int n0 = nt * TN;
+  if (n0 >= N) return;
+
+  const bf16_t* W0;
+  const bf16_t* W1 = nullptr;
+  if (GATED) {
+    W0 = G.shared ? p.w0_s : p.w0 + (size_t)g * p.d * p.I;
+    W1 = G.shared ? p.w1_s : p.w1 + (size_t)g * p.d * p.I;
+  } else {
+    W0 = G.shared ? p.w0_s : p.w0 + (size_t)g * p.I * p.d;
+  }
+
+  // A: this wave's instructions q = wave and wave + 8 (16 rows each); rows past the tile re-read
+  // its first row
+  const int64_t a_pitch = (GATED ? (int64_t)p.d : (int64_t)p.ldh) * 2;
+  uint32_t a_off[tall::A_DMA];
+#pragma unroll
+  for (int i = 0; i < tall::A_DMA; ++i) {
+    const int m = (wave + tall::NW * i) * 16 + (lane >> 2);
+    const int r = m < mrows ? m : 0;
+    int64_t src_row;
+    if (GATED)
+      src_row = G.shared ? (int64_t)(m0 + r) : (int64_t)p.sorted_token[G.row0 + m0 + r];
+    else
+      src_row = G.row0 + m0 + r;
+    a_off[i] = (uint32_t)(src_row * a_pitch) + a_dma_chunk_bytes(lane);
+  }
+  const int nk = K / SBK;
+  const char* a_src = uniform_ptr((const char*)p.a_src);
+  auto a_base = [=](int kt) { return a_src + kt * (SBK * 2); };
+
+  // B: four 128-column blocks; wave w fills rows 16 (w % 2) .. +16 of block w / 2. For gate/up,
+  // blocks 0, 1 are W_g columns n0 .. n0 + 255 and blocks 2, 3 the W_u columns with the same indices.
+  const int64_t b_pitch = (int64_t)N * 2;
+  const int blk = wave >> 1;
+  const char* b_mat;
+  if (GATED)
+    b_mat = (const char*)(blk < 2 ? W0 : W1) + (int64_t)(n0 + 128 * (blk & 1)) * 2;
+  else
+    b_mat = (const char*)W0 + (int64_t)(n0 + 128 * blk) * 2;
+  const int64_t b_kstep = (int64_t)SBK * b_pitch;
+  const char* b0 = uniform_ptr(b_mat + (int64_t)(16 * (wave & 1)) * b_pitch);
+  auto b_base = [=](int kt, int i) { return b0 + kt * b_kstep + i * 4 * b_pitch; };
+  const uint32_t b_off = b_dma_lane_offset(lane, (uint32_t)b_pitch);
+
+  // the wave's two 32-wide column sub-tiles: gate and up columns wave*32 (gate/up), or
+  // wave*64 .. +64 (down)
+  int bcol[2];
+  if (GATED) {
+    bcol[0] = wave * 32;
+    bcol[1] = TN + wave * 32;
+  } else {
+    bcol[0] = wave * 64;
+    bcol[1] = wave * 64 + 32;
+  }
+
+  f32x16_t acc[tall::SUB][2];
+  tall::zero(acc);
+  if (nk > 0) tall::mainloop<S>(nk, mrows, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+
+  // epilogue through LDS (see the 128-row kernel): the output rows staged in bf16, then written
+  // with 16-byte row stores; the down tile's 512 columns go in two halves of 256
+  const int col_in = lane & 31;
+  const int row_hi = (lane >> 5) * 4;
+  constexpr int HALF = 256;
+  constexpr int PITCH = HALF * 2 + 16;
+  static_assert(TM * PITCH <= S * tall::STAGE, "a staged half-tile fits the LDS stages");
+  const int64_t ld = GATED ? p.ldh : p.d;
+  bf16_t* out = p.out + (G.row0 + m0) * ld + n0;
+  char* st = smem;
+  constexpr int CH = HALF / 8;  // 16-byte chunks per staged row
+#pragma unroll
+  for (int h = 0; h < TN / HALF; ++h) {
+    __syncthreads();  // every wave is past its mainloop (h = 0) or its previous half's copy
+    if (GATED) {
+      const int c = wave * 32 + col_in;
+#pragma unroll
+      for (int u = 0; u < tall::SUB; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = u * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+          if (row < mrows)
+            *(bf16_t*)(st + row * PITCH + c * 2) = f32_to_bf16(silu_f32(acc[u][0][r]) * acc[u][1][r]);
+        }
+    } else if ((wave >> 2) == h) {  // waves 4h .. 4h+3 hold columns 256h .. +256
+#pragma unroll
+      for (int u = 0; u < tall::SUB; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int c = (wave & 3) * 64 + j * 32 + col_in;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = u * 32 + (r >> 2) * 8 + row_hi + (r & 3);
+            if (row < mrows) *(bf16_t*)(st + row * PITCH + c * 2) = f32_to_bf16(acc[u][j][r]);
+          }
+        }
+    }
+    __syncthreads();
+    for (int c = tid; c < mrows * CH; c += 512) {
+      const int row = c / CH, ch = c - row * CH;
+      *(uint4*)(out + row * ld + h * HALF + ch * 8) = *(const uint4*)(st + row * PITCH + ch * 16);
+    }
+  }
+}
+
 // H rows of a gate/up product with K split (streaming MFMA or skinny kernels): each split's fp32
 // gate and up sums (row pitch 2 ldh: gate at column c, up at ldh + c) added in split order, then
 // silu(gate) * up in bf16.
@@ -621,7 +762,10 @@ hipError_t launch_gate_up_finish(const float* part, int64_t sstride, int64_t par
   return hipGetLastError();
 }
 
-int ffn_tile_rows(const moe_dims& dm) { return dm.dtype == MOE_F32 ? kF32BM : kMfmaBM; }
+int ffn_tile_rows(const moe_dims& dm) {
+  if (dm.dtype == MOE_F32) return kF32BM;
+  return ffn_plan(dm).tall ? stream::tall::ROWS : kMfmaBM;
+}
 
 hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s) {
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, dm.T, dm.E, dm.I_shared > 0 ? 1 : 0,
@@ -645,10 +789,13 @@ FfnPlan ffn_plan(const moe_dims& dm) {
   // expert on average. Short K loops (and the near-empty row tiles of decode) run faster on
   // 128 x 256 tiles, two workgroups per CU, whose prologues and epilogues overlap.
   const double rows_per_expert = (double)Tk / dm.E;
+  // Tall 160-row tiles for both products when experts hold a few hundred rows each (prefill-sized
+  // batches): ~320 rows are then two row tiles rather than three.
+  P.tall = P.stream && rows_per_expert >= 256.0 && dm.I % 256 == 0 && dm.I_shared % 256 == 0 && dm.d % 512 == 0;
   P.wn1 = P.stream && dm.I % 256 == 0 && dm.I_shared % 256 == 0 && dm.d >= 4096 ? 4 : 2;
   P.wn2 = P.stream && dm.d % 512 == 0 && dm.I >= 2048 && rows_per_expert >= 64.0 ? 4 : 2;
-  const int tn1 = P.stream ? 64 * P.wn1 : kMfmaBN1;
-  const int tn2 = P.stream ? 128 * P.wn2 : kMfmaBN2;
+  const int tn1 = P.tall ? 256 : P.stream ? 64 * P.wn1 : kMfmaBN1;
+  const int tn2 = P.tall ? 512 : P.stream ? 128 * P.wn2 : kMfmaBN2;
   P.nt1 = (ldh + tn1 - 1) / tn1;
   P.nt2 = (dm.d + tn2 - 1) / tn2;
   // Split the gate/up product's K when its tiles alone would leave CUs idle (few tokens: each
@@ -658,7 +805,7 @@ FfnPlan ffn_plan(const moe_dims& dm) {
   if (P.stream) {
     const int64_t groups = (Tk < dm.E ? Tk : dm.E) + has_shared;
     const int64_t mt = groups + rows_total / kMfmaBM;
-    P.s1 = pick_splits(mt * P.nt1, dm.d / 32);
+    P.s1 = P.tall ? 1 : pick_splits(mt * P.nt1, dm.d / 32);
   }
   // Equal row tiles where experts hold one to two tiles' worth of rows (HBM-bound shapes): an
   // expert's two tiles then run at the same pace and share each weight panel through L2, instead
@@ -749,7 +896,9 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.part_ld = P.part_cols1;
     a.part_sstride = L.rows_total * P.part_cols1;
     if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
-    if (stream_ok)
+    if (P.tall)
+      hipLaunchKernelGGL((ffn_mfma_tall_kernel<true, 3>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(512), 0, s, a);
+    else if (stream_ok)
       launch_stream<true>(P.wn1, (unsigned)(max_mt * a.n_ntiles * a.splits), s, a);
     else
       hipLaunchKernelGGL(ffn_mfma_kernel<true>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
@@ -772,7 +921,9 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.part_ld = 0;
     a.part_sstride = 0;
     if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
-    if (stream_ok)
+    if (P.tall)
+      hipLaunchKernelGGL((ffn_mfma_tall_kernel<false, 3>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(512), 0, s, a);
+    else if (stream_ok)
       launch_stream<false>(P.wn2, (unsigned)(max_mt * a.n_ntiles * a.splits), s, a);
     else
       hipLaunchKernelGGL(ffn_mfma_kernel<false>, dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);

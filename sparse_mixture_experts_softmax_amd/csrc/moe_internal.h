@@ -77,6 +77,7 @@ Layout make_layout(const moe_dims& dm);
 struct FfnPlan {
   bool stream;
   bool balance;  // equal row tiles per group
+  bool tall;     // 160-row tiles for both products (groups of a few hundred rows)
   int wn1, wn2;
   int nt1, nt2;
   int s1;  // K splits of the MFMA gate/up product (the MFMA down product is never split)

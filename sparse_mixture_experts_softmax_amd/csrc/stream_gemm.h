@@ -309,6 +309,154 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[2][4]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
+// ------------------------------------------------------------------------------------------------
+// Tall tiles for groups of a few hundred rows: 160 x 512, eight wavefronts, each holding every row
+// of the tile (five 32-row sub-tiles) and 64 columns (two 32-wide sub-tiles), 160 fp32
+// accumulators per lane. An expert's rows are split over ceil(rows / 160) row tiles in whole
+// 32-row sub-tiles, as evenly as possible: ~320 rows take two row tiles instead of the three of
+// 128 rows, so the weight panels are streamed from L2 into LDS twice instead of three times, and
+// the two tiles do equal work, run in step and share each panel through L2. Per K step the CU
+// moves 10 KB of A and 32 KB of B for 5.2 MFLOP (128 x 512 tiles: 40 KB for 4.2 MFLOP).
+//   LDS per stage: A [160 rows][32 K] (10 instructions of 16 rows; wave w issues instructions w
+//   and w + 8) in the layout and swizzle of the 128-row tiles, then the same B tile of four
+//   128-column blocks (wave w fills rows 16 (w % 2) .. +16 of block w / 2).
+// ------------------------------------------------------------------------------------------------
+namespace tall {
+constexpr int ROWS = 160;                  // tile rows: five 32-row sub-tiles
+constexpr int SUB = ROWS / 32;
+constexpr int NW = 8;                      // wavefronts
+constexpr int A_BYTES = ROWS * SBK * 2;    // 10 KB
+constexpr int A_INSTR = A_BYTES / 1024;    // 10
+constexpr int B_BYTES = 4 * BLOCK_BYTES;   // 32 KB
+constexpr int B_DMA = B_BYTES / 1024 / NW; // 4 per wave
+constexpr int STAGE = A_BYTES + B_BYTES;   // 42 KB
+constexpr int A_DMA = (A_INSTR + NW - 1) / NW;  // at most 2 A instructions per wave
+
+// A instructions this wave issues for a tile with `rows` valid rows: instructions w and w + 8,
+// those whose 16 rows hold a valid row
+__device__ __forceinline__ int needed_a(int rows, int wave) {
+  const int n = (rows + 15) / 16;  // instructions 0 .. n-1 hold valid rows
+  return (wave < n) + (wave + NW < n);
+}
+
+template <int S, int NL, int NAD, bool NT, class ABase, class BBase>
+__device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base, const uint32_t (&a_off)[A_DMA],
+                                           BBase b_base, uint32_t b_off, const int (&bcol)[2],
+                                           f32x16_t (&acc)[SUB][2]) {
+  static_assert(S >= 2 && S <= 3, "stages");
+  static_assert(NL >= 0 && NL <= SUB, "sub-tiles");
+  constexpr int DMA = NAD + B_DMA;
+  constexpr int NA = NL > 0 ? NL : 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g16 = lane >> 4;
+  const int i16 = lane & 15;
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  // a wave with three or more live sub-tiles issues its DMAs behind its second sub-step's
+  // MFMAs, so that a stalled DMA issue does not idle the matrix unit (as in the 128 x 512 tiles)
+  constexpr bool late = NL >= 3;
+
+  auto issue = [&](int kt, int stage) {
+    const uint32_t dst = lds_base + stage * STAGE;
+    const char* ab = a_base(kt);
+#pragma unroll
+    for (int i = 0; i < NAD; ++i) dma16(ab, a_off[i], dst + (wave + NW * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) dma16<NT>(b_base(kt, i), b_off, dst + A_BYTES + (wave * B_DMA + i) * 1024);
+  };
+  auto read = [&](const lds_char* st, int s, bf16x8_t (&a)[NA], bf16x8_t (&b)[2]) {
+    if constexpr (NL > 0) {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) a[u] = read_a(st, u * 32 + (lane & 31), 2 * s + (lane >> 5));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int kb = 16 * s + 8 * (g16 >> 1) + (i16 >> 2);
+        const int n = bcol[j] + 16 * (g16 & 1) + 4 * (i16 & 3);
+        const s16x4_t lo = read_b_tr(st + A_BYTES, kb, n);
+        const s16x4_t hi = read_b_tr(st + A_BYTES, kb + 4, n);
+        b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+  };
+  auto mma = [&](const bf16x8_t (&a)[NA], const bf16x8_t (&b)[2]) {
+    if constexpr (NL > 0) {
+#pragma unroll
+      for (int u = 0; u < NL; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[j], acc[u][j], 0, 0, 0);
+    }
+  };
+
+  // prologue: S stages in flight, stage 0 complete
+#pragma unroll
+  for (int i = 0; i < S; ++i)
+    if (i < nk) issue(i, i);
+  wait_groups<DMA>(min(S - 1, nk - 1));
+  barrier_lds_only();
+
+  bf16x8_t a0[NA], b0[2], a1[NA], b1[2];
+  read(lds, 0, a0, b0);
+  // k-steps 0 .. nk-2 cross the barrier; the last one is peeled (see the 128-row mainloop)
+  int stage = 0;
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    const lds_char* cur = lds + stage * STAGE;
+    const int next = stage == S - 1 ? 0 : stage + 1;
+    read(cur, 1, a1, b1);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_groups<DMA>(min(S - 2, nk - kt - 2));
+    barrier_after_lds_reads();
+    if (!late && kt + S < nk) issue(kt + S, stage);
+    read(lds + next * STAGE, 0, a0, b0);
+    mma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (late && kt + S < nk) issue(kt + S, stage);
+    stage = next;
+  }
+  if (nk >= 1) {
+    read(lds + stage * STAGE, 1, a1, b1);
+    mma(a0, b0);
+    mma(a1, b1);
+  }
+}
+
+template <int S, int NL, bool NT, class ABase, class BBase>
+__device__ __forceinline__ void mainloop_a(int nad, int nk, lds_char* lds, ABase a_base,
+                                           const uint32_t (&a_off)[A_DMA], BBase b_base, uint32_t b_off,
+                                           const int (&bcol)[2], f32x16_t (&acc)[SUB][2]) {
+  if (nad >= 2) mainloop_v<S, NL, 2, NT>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else if (nad == 1) mainloop_v<S, NL, 1, NT>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else mainloop_v<S, NL, 0, NT>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+}
+
+// acc[u][j] += A * B over nk K-steps for a tile with `rows` valid rows (1 .. 160): dispatch on the
+// live sub-tiles (every wave multiplies all of them) and on this wave's A instructions
+template <int S, class ABase, class BBase>
+__device__ __forceinline__ void mainloop(int nk, int rows, lds_char* lds, ABase a_base,
+                                         const uint32_t (&a_off)[A_DMA], BBase b_base, uint32_t b_off,
+                                         const int (&bcol)[2], f32x16_t (&acc)[SUB][2]) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nad = needed_a(rows, wave);
+  const int nl = (rows + 31) / 32;
+  switch (nl) {
+    case 5: mainloop_a<S, 5, false>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+    case 4: mainloop_a<S, 4, false>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+    case 3: mainloop_a<S, 3, false>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+    case 2: mainloop_a<S, 2, false>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+    default: mainloop_a<S, 1, false>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+  }
+}
+
+__device__ __forceinline__ void zero(f32x16_t (&acc)[SUB][2]) {
+#pragma unroll
+  for (int i = 0; i < SUB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+}  // namespace tall
+
 // Workgroup-index remap so that consecutive logical tiles run on the same XCD: workgroups are
 // dispatched round-robin over the 8 XCDs, so physical block b runs on XCD b % 8. Logical tiles
 // [x*q + min(x, r), ...) of n = 8q + r go to XCD x, in order. Returns -1 for b >= n.

@@ -106,6 +106,12 @@ SMALL_CASES = [
     ("topk_wide_f32", 20, 64, 130, 4, 32, 32, syn.F32, 1, 0.0),
     # equal row tiles (<= 192 rows per expert on average) under Zipf-skewed loads of ~50 .. ~650 rows
     ("balanced_tiles_skewed", 700, 512, 16, 4, 256, 128, syn.BF16, 1, 0.8),
+    # 160-row tall tiles (>= 256 rows per expert on average): three row tiles of 4, 4, 3 sub-tiles;
+    # a shared expert wider than the routed ones over four row tiles (4, 4, 4, 5 sub-tiles); and
+    # Zipf-skewed loads from every token down to a few rows (one partial sub-tile)
+    ("tall_tiles", 700, 512, 8, 4, 256, 256, syn.BF16, 1, 0.0),
+    ("tall_tiles_wide_shared", 513, 1024, 4, 2, 256, 512, syn.BF16, 1, 0.0),
+    ("tall_tiles_skewed", 2000, 512, 16, 4, 256, 0, syn.BF16, 0, 1.2),
 ]
 
 
