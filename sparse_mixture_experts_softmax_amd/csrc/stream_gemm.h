@@ -431,20 +431,30 @@ __device__ __forceinline__ void mainloop_a(int nad, int nk, lds_char* lds, ABase
 
 // acc[u][j] += A * B over nk K-steps for a tile with `rows` valid rows (1 .. 160): dispatch on the
 // live sub-tiles (every wave multiplies all of them) and on this wave's A instructions
-template <int S, class ABase, class BBase>
-__device__ __forceinline__ void mainloop(int nk, int rows, lds_char* lds, ABase a_base,
-                                         const uint32_t (&a_off)[A_DMA], BBase b_base, uint32_t b_off,
-                                         const int (&bcol)[2], f32x16_t (&acc)[SUB][2]) {
+template <int S, bool NT, class ABase, class BBase>
+__device__ __forceinline__ void mainloop_n(int nk, int rows, lds_char* lds, ABase a_base,
+                                           const uint32_t (&a_off)[A_DMA], BBase b_base, uint32_t b_off,
+                                           const int (&bcol)[2], f32x16_t (&acc)[SUB][2]) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nad = needed_a(rows, wave);
   const int nl = (rows + 31) / 32;
   switch (nl) {
-    case 5: mainloop_a<S, 5, false>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
-    case 4: mainloop_a<S, 4, false>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
-    case 3: mainloop_a<S, 3, false>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
-    case 2: mainloop_a<S, 2, false>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
-    default: mainloop_a<S, 1, false>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+    case 5: mainloop_a<S, 5, NT>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+    case 4: mainloop_a<S, 4, NT>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+    case 3: mainloop_a<S, 3, NT>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+    case 2: mainloop_a<S, 2, NT>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+    default: mainloop_a<S, 1, NT>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
   }
+}
+
+// nt: B (weight) DMAs with the non-temporal hint, for a group with a single row tile (the only
+// reader of its weight panels)
+template <int S, class ABase, class BBase>
+__device__ __forceinline__ void mainloop(int nk, int rows, lds_char* lds, ABase a_base,
+                                         const uint32_t (&a_off)[A_DMA], BBase b_base, uint32_t b_off,
+                                         const int (&bcol)[2], f32x16_t (&acc)[SUB][2], bool nt) {
+  if (nt) mainloop_n<S, true>(nk, rows, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else mainloop_n<S, false>(nk, rows, lds, a_base, a_off, b_base, b_off, bcol, acc);
 }
 
 __device__ __forceinline__ void zero(f32x16_t (&acc)[SUB][2]) {
