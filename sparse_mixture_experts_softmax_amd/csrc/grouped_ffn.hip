@@ -540,9 +540,12 @@ __global__ void __launch_bounds__(512, 1) ffn_mfma_tall_kernel(MfmaArgs p) {
   if (nk > 0) tall::mainloop<S>(nk, mrows, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc, cnt == 1);
 
   // epilogue through LDS (see the 128-row kernel): the output rows staged in bf16, then written
-  // with 16-byte row stores; the down tile's 512 columns go in two halves of 256
-  const int col_in = lane & 31;
-  const int row_hi = (lane >> 5) * 4;
+  // with 16-byte row stores; the down tile's 512 columns go in two halves of 256. The mainloop's
+  // accumulators hold transposed 32 x 32 blocks: lane l has row 32 u + (l & 31) and, in register
+  // 4 g + q, column 8 g + 4 (l >> 5) + q of its 32-wide sub-tile -- four consecutive columns of one
+  // row per g, staged with one 8-byte store.
+  const int rl = lane & 31;
+  const int cq = 4 * (lane >> 5);
   constexpr int HALF = 256;
   constexpr int PITCH = HALF * 2 + 16;
   static_assert(TM * PITCH <= S * tall::STAGE, "a staged half-tile fits the LDS stages");
@@ -554,27 +557,34 @@ __global__ void __launch_bounds__(512, 1) ffn_mfma_tall_kernel(MfmaArgs p) {
   for (int h = 0; h < TN / HALF; ++h) {
     __syncthreads();  // every wave is past its mainloop (h = 0) or its previous half's copy
     if (GATED) {
-      const int c = wave * 32 + col_in;
 #pragma unroll
-      for (int u = 0; u < tall::SUB; ++u)
+      for (int u = 0; u < tall::SUB; ++u) {
+        const int row = u * 32 + rl;
+        if (row < mrows)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = u * 32 + (r >> 2) * 8 + row_hi + (r & 3);
-          if (row < mrows)
-            *(bf16_t*)(st + row * PITCH + c * 2) = f32_to_bf16(silu_f32(acc[u][0][r]) * acc[u][1][r]);
-        }
+          for (int g = 0; g < 4; ++g) {
+            const int c = wave * 32 + 8 * g + cq;
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = silu_f32(acc[u][0][4 * g + q]) * acc[u][1][4 * g + q];
+            *(uint2*)(st + row * PITCH + c * 2) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          }
+      }
     } else if ((wave >> 2) == h) {  // waves 4h .. 4h+3 hold columns 256h .. +256
 #pragma unroll
-      for (int u = 0; u < tall::SUB; ++u)
+      for (int u = 0; u < tall::SUB; ++u) {
+        const int row = u * 32 + rl;
+        if (row < mrows)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int c = (wave & 3) * 64 + j * 32 + col_in;
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = u * 32 + (r >> 2) * 8 + row_hi + (r & 3);
-            if (row < mrows) *(bf16_t*)(st + row * PITCH + c * 2) = f32_to_bf16(acc[u][j][r]);
-          }
-        }
+            for (int g = 0; g < 4; ++g) {
+              const int c = (wave & 3) * 64 + j * 32 + 8 * g + cq;
+              const f32x16_t& a = acc[u][j];
+              *(uint2*)(st + row * PITCH + c * 2) =
+                  make_uint2(pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3]));
+            }
+      }
     }
     __syncthreads();
     for (int c = tid; c < mrows * CH; c += 512) {

@@ -378,12 +378,15 @@ __device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base, 
       }
     }
   };
+  // operands swapped (B fragment first): each accumulator holds the transposed 32 x 32 block, so
+  // that a lane ends up with four consecutive columns of one row per register group (the
+  // epilogue then stages 8 bytes per store instead of 2)
   auto mma = [&](const bf16x8_t (&a)[NA], const bf16x8_t (&b)[2]) {
     if constexpr (NL > 0) {
 #pragma unroll
       for (int u = 0; u < NL; ++u)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[j], acc[u][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[u], acc[u][j], 0, 0, 0);
     }
   };
 
