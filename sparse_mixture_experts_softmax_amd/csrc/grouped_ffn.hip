@@ -511,6 +511,8 @@ __global__ void __launch_bounds__(512, 1) ffn_mfma_tall_kernel(MfmaArgs p) {
 
   // B: four 128-column blocks; wave w fills rows 16 (w % 2) .. +16 of block w / 2. For gate/up,
   // blocks 0, 1 are W_g columns n0 .. n0 + 255 and blocks 2, 3 the W_u columns with the same indices.
+  // B: four 128-column blocks; wave w fills rows 16 (w % 2) .. +16 of block w / 2. For gate/up,
+  // blocks 0, 1 are W_g columns n0 .. n0 + 255 and blocks 2, 3 the W_u columns with the same indices.
   const int64_t b_pitch = (int64_t)N * 2;
   const int blk = wave >> 1;
   const char* b_mat;
@@ -580,6 +582,155 @@ __global__ void __launch_bounds__(512, 1) ffn_mfma_tall_kernel(MfmaArgs p) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const int c = (wave & 3) * 64 + j * 32 + 8 * g + cq;
+              const f32x16_t& a = acc[u][j];
+              *(uint2*)(st + row * PITCH + c * 2) =
+                  make_uint2(pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3]));
+            }
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < mrows * CH; c += 512) {
+      const int row = c / CH, ch = c - row * CH;
+      *(uint4*)(out + row * ld + h * HALF + ch * 8) = *(const uint4*)(st + row * PITCH + ch * 16);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Wide-tile variant for groups of ~250 rows and more (prefill-sized batches): 192 x 512 tiles on
+// eight wavefronts (stream_gemm.h, namespace wide). Row split (whole 32-row sub-tiles, as evenly
+// as possible over ceil(rows / 192) row tiles), tile order, XCD remap, non-temporal weight streams
+// for single-row-tile groups and the staged epilogue as in the tall kernel.
+// ------------------------------------------------------------------------------------------
+template <bool GATED, int S>
+__global__ void __launch_bounds__(512, 1) ffn_mfma_wide_kernel(MfmaArgs p) {
+  using namespace stream;
+  constexpr int TM = wide::ROWS;
+  constexpr int TN = GATED ? 256 : 512;  // output columns per tile
+  __shared__ __attribute__((aligned(1024))) char smem[S * wide::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+
+  const int L = xcd_remap(blockIdx.x, *p.tile_count * p.n_ntiles);
+  if (L < 0) return;
+  const int probe = L / p.n_ntiles;
+  const int g = p.tile_group[probe];
+  const int first = probe - p.tile_m0[probe] / TM;  // the group's first row tile
+  const Group G = group_info(g, p.offsets, p.T, p.k, p.E, p.I, p.Is);
+  const int cnt = (G.rows + TM - 1) / TM;
+  const int local = L - p.n_ntiles * first;
+  const int nt = local / cnt;
+  const int mt = local % cnt;
+  // the group's S32 sub-tiles of 32 rows, split as evenly as possible over its cnt row tiles
+  const int S32 = (G.rows + 31) / 32;
+  const int m0 = 32 * (mt * S32 / cnt);
+  const int mrows = min(32 * ((mt + 1) * S32 / cnt), G.rows) - m0;
+
+  const int K = GATED ? p.d : G.n_inter;
+  const int N = GATED ? G.n_inter : p.d;
+  const int n0 = nt * TN;
+  if (n0 >= N) return;
+
+  const bf16_t* W0;
+  const bf16_t* W1 = nullptr;
+  if (GATED) {
+    W0 = G.shared ? p.w0_s : p.w0 + (size_t)g * p.d * p.I;
+    W1 = G.shared ? p.w1_s : p.w1 + (size_t)g * p.d * p.I;
+  } else {
+    W0 = G.shared ? p.w0_s : p.w0 + (size_t)g * p.I * p.d;
+  }
+
+  // A: this wave's instructions q = wave and wave + 8 (16 rows each; q < 12 only for waves 0 .. 3);
+  // rows past the tile re-read its first row
+  const int64_t a_pitch = (GATED ? (int64_t)p.d : (int64_t)p.ldh) * 2;
+  uint32_t a_off[wide::A_DMA];
+#pragma unroll
+  for (int i = 0; i < wide::A_DMA; ++i) {
+    const int m = min((wave + wide::NW * i) * 16 + (lane >> 2), TM - 1);
+    const int r = m < mrows ? m : 0;
+    int64_t src_row;
+    if (GATED)
+      src_row = G.shared ? (int64_t)(m0 + r) : (int64_t)p.sorted_token[G.row0 + m0 + r];
+    else
+      src_row = G.row0 + m0 + r;
+    a_off[i] = (uint32_t)(src_row * a_pitch) + a_dma_chunk_bytes(lane);
+  }
+  const int nk = K / SBK;
+  const char* a_src = uniform_ptr((const char*)p.a_src);
+  auto a_base = [=](int kt) { return a_src + kt * (SBK * 2); };
+
+  const int64_t b_pitch = (int64_t)N * 2;
+  const int blk = wave >> 1;
+  const char* b_mat;
+  if (GATED)
+    b_mat = (const char*)(blk < 2 ? W0 : W1) + (int64_t)(n0 + 128 * (blk & 1)) * 2;
+  else
+    b_mat = (const char*)W0 + (int64_t)(n0 + 128 * blk) * 2;
+  const int64_t b_kstep = (int64_t)SBK * b_pitch;
+  const char* b0 = uniform_ptr(b_mat + (int64_t)(16 * (wave & 1)) * b_pitch);
+  auto b_base = [=](int kt, int i) { return b0 + kt * b_kstep + i * 4 * b_pitch; };
+  const uint32_t b_off = b_dma_lane_offset(lane, (uint32_t)b_pitch);
+
+  // the wave's four 32-wide column sub-tiles: gate columns 64 wn, 64 wn + 32 and the up columns
+  // with the same indices (gate/up), or columns 128 wn .. +128 (down)
+  int bcol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bcol[j] = GATED ? (j >> 1) * 256 + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+
+  f32x16_t acc[3][4];
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[u][j][r] = 0.f;
+  // a group with a single row tile is the only reader of its weight panels: non-temporal hint
+  if (nk > 0) wide::mainloop<S>(nk, mrows, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc, cnt == 1);
+
+  // epilogue through LDS as in the tall kernel: accumulator u holds transposed 32 x 32 blocks of
+  // tile rows 32 (wm + 2u) .. +32, staged 8 bytes per store, copied out with 16-byte row stores;
+  // the down tile's 512 columns in two halves of 256
+  const int rl = lane & 31;
+  const int cq = 4 * (lane >> 5);
+  constexpr int HALF = 256;
+  constexpr int PITCH = HALF * 2 + 16;
+  static_assert(TM * PITCH <= S * wide::STAGE, "a staged half-tile fits the LDS stages");
+  const int64_t ld = GATED ? p.ldh : p.d;
+  bf16_t* out = p.out + (G.row0 + m0) * ld + n0;
+  char* st = smem;
+  constexpr int CH = HALF / 8;  // 16-byte chunks per staged row
+#pragma unroll
+  for (int h = 0; h < TN / HALF; ++h) {
+    __syncthreads();  // every wave is past its mainloop (h = 0) or its previous half's copy
+    if (GATED) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int row = (wm + 2 * u) * 32 + rl;
+        if (row < mrows)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int c = wn * 64 + j * 32 + 8 * g + cq;
+              float v[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = silu_f32(acc[u][j][4 * g + q]) * acc[u][j + 2][4 * g + q];
+              *(uint2*)(st + row * PITCH + c * 2) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
+      }
+    } else if ((wn >> 1) == h) {  // wave columns 2h, 2h + 1 hold columns 256h .. +256
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int row = (wm + 2 * u) * 32 + rl;
+        if (row < mrows)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int c = (wn & 1) * 128 + j * 32 + 8 * g + cq;
               const f32x16_t& a = acc[u][j];
               *(uint2*)(st + row * PITCH + c * 2) =
                   make_uint2(pack_bf16x2(a[4 * g], a[4 * g + 1]), pack_bf16x2(a[4 * g + 2], a[4 * g + 3]));
@@ -775,7 +926,8 @@ hipError_t launch_gate_up_finish(const float* part, int64_t sstride, int64_t par
 
 int ffn_tile_rows(const moe_dims& dm) {
   if (dm.dtype == MOE_F32) return kF32BM;
-  return ffn_plan(dm).tall ? stream::tall::ROWS : kMfmaBM;
+  const FfnPlan P = ffn_plan(dm);
+  return P.wide ? stream::wide::ROWS : P.tall ? stream::tall::ROWS : kMfmaBM;
 }
 
 hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s) {
@@ -806,6 +958,10 @@ FfnPlan ffn_plan(const moe_dims& dm) {
   // fewer row tiles (skew layer 14.5 -> 13.7 ms). At ~128 rows per expert the 128 x 256 tiles stay
   // faster (mid: down product 0.17 vs 0.18 ms).
   P.tall = P.stream && rows_per_expert >= 150.0 && dm.I % 256 == 0 && dm.I_shared % 256 == 0 && dm.d % 512 == 0;
+  // 192-row tiles from ~256 rows per expert on average: experts of 321 .. 384 rows then take two
+  // row tiles instead of three (prefill layer 20.2 -> 19.9 ms). Under skewed routing (~160 rows on
+  // average, most experts a few dozen) they measured slower than the tall ones (13.5 -> 14.4 ms).
+  P.wide = P.tall && rows_per_expert >= 256.0;
   P.wn1 = P.stream && dm.I % 256 == 0 && dm.I_shared % 256 == 0 && dm.d >= 4096 ? 4 : 2;
   P.wn2 = P.stream && dm.d % 512 == 0 && dm.I >= 2048 && rows_per_expert >= 64.0 ? 4 : 2;
   const int tn1 = P.tall ? 256 : P.stream ? 64 * P.wn1 : kMfmaBN1;
@@ -910,7 +1066,9 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.part_ld = P.part_cols1;
     a.part_sstride = L.rows_total * P.part_cols1;
     if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
-    if (P.tall)
+    if (P.wide)
+      hipLaunchKernelGGL((ffn_mfma_wide_kernel<true, 3>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(512), 0, s, a);
+    else if (P.tall)
       hipLaunchKernelGGL((ffn_mfma_tall_kernel<true, 3>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(512), 0, s, a);
     else if (stream_ok)
       launch_stream<true>(P.wn1, (unsigned)(max_mt * a.n_ntiles * a.splits), s, a);
@@ -935,7 +1093,9 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.part_ld = 0;
     a.part_sstride = 0;
     if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
-    if (P.tall)
+    if (P.wide)
+      hipLaunchKernelGGL((ffn_mfma_wide_kernel<false, 3>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(512), 0, s, a);
+    else if (P.tall)
       hipLaunchKernelGGL((ffn_mfma_tall_kernel<false, 3>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(512), 0, s, a);
     else if (stream_ok)
       launch_stream<false>(P.wn2, (unsigned)(max_mt * a.n_ntiles * a.splits), s, a);

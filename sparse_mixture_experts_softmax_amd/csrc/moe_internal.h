@@ -78,6 +78,7 @@ struct FfnPlan {
   bool stream;
   bool balance;  // equal row tiles per group
   bool tall;     // 160-row tiles for both products (groups of a few hundred rows)
+  bool wide;     // 192-row tiles instead of the 160-row ones (groups of ~250 rows and more)
   int wn1, wn2;
   int nt1, nt2;
   int s1;  // K splits of the MFMA gate/up product (the MFMA down product is never split)

@@ -29,6 +29,8 @@
 // 16 bytes per lane) on distinct banks of the 64 x 4-byte LDS banks.
 #pragma once
 
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -469,6 +471,147 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[SUB][2]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 }  // namespace tall
+
+// ------------------------------------------------------------------------------------------------
+// Wide tiles for groups of ~250 rows and more: 192 x 512 on eight wavefronts in two wave rows of
+// four. Wave (wm, wn) holds the 32-row sub-tiles wm, wm + 2, wm + 4 (a partly filled tile keeps
+// its live rows spread over both wave rows, so over every SIMD) and columns 128 wn .. +128
+// (gate/up: gate columns 64 wn .. +64 and the up columns with the same indices), 192 accumulators
+// per lane, two wavefronts per SIMD. Against the 160-row tiles: an expert of 321 .. 384 rows takes
+// two row tiles instead of three, so its weight panels cross from L2 into LDS twice, and per FLOP
+// the CU moves 7.0 instead of 8.0 KB per MFLOP from L2 into LDS -- the prefill GEMMs run
+// power-limited, with the clock set mostly by that traffic.
+//   LDS per stage: A [192 rows][32 K] (12 instructions of 16 rows; wave w issues w and w + 8 when
+//   < 12) in the swizzle of the 128-row tiles, then the B tile of four 128-column blocks (wave w
+//   fills rows 16 (w % 2) .. +16 of block w / 2).
+// ------------------------------------------------------------------------------------------------
+namespace wide {
+constexpr int ROWS = 192;
+constexpr int NW = 8;
+constexpr int A_BYTES = ROWS * SBK * 2;     // 12 KB
+constexpr int A_INSTR = A_BYTES / 1024;     // 12
+constexpr int A_DMA = 2;                    // at most two A instructions per wave
+constexpr int B_BYTES = 4 * BLOCK_BYTES;    // 32 KB
+constexpr int B_DMA = B_BYTES / 1024 / NW;  // 4 per wave
+constexpr int STAGE = A_BYTES + B_BYTES;    // 44 KB
+
+// this wave row's live sub-tiles (a prefix of u = 0, 1, 2: tile sub-tile wm + 2u) given the rows
+__device__ __forceinline__ int live(int rows, int wm) {
+  const int n = (rows + 31) / 32;
+  return (wm < n) + (wm + 2 < n) + (wm + 4 < n);
+}
+__device__ __forceinline__ int needed_a(int rows, int wave) {
+  const int n = (rows + 15) / 16;
+  return (wave < n) + (wave + NW < n);
+}
+
+template <int S, int NL, int NAD, bool NT, class ABase, class BBase>
+__device__ __forceinline__ void mainloop_v(int nk, lds_char* lds, ABase a_base, const uint32_t (&a_off)[A_DMA],
+                                           BBase b_base, uint32_t b_off, const int (&bcol)[4],
+                                           f32x16_t (&acc)[3][4]) {
+  static_assert(S >= 2 && S <= 3, "stages");
+  static_assert(NL >= 0 && NL <= 3, "sub-tiles");
+  constexpr int DMA = NAD + B_DMA;
+  constexpr int NA = NL > 0 ? NL : 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2;
+  const int g16 = lane >> 4;
+  const int i16 = lane & 15;
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  constexpr bool late = NL >= 2;
+
+  auto issue = [&](int kt, int stage) {
+    const uint32_t dst = lds_base + stage * STAGE;
+    const char* ab = a_base(kt);
+#pragma unroll
+    for (int i = 0; i < NAD; ++i) dma16(ab, a_off[i], dst + (wave + NW * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) dma16<NT>(b_base(kt, i), b_off, dst + A_BYTES + (wave * B_DMA + i) * 1024);
+  };
+  auto read = [&](const lds_char* st, int s, bf16x8_t (&a)[NA], bf16x8_t (&b)[4]) {
+    if constexpr (NL > 0) {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) a[u] = read_a(st, (wm + 2 * u) * 32 + (lane & 31), 2 * s + (lane >> 5));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kb = 16 * s + 8 * (g16 >> 1) + (i16 >> 2);
+        const int n = bcol[j] + 16 * (g16 & 1) + 4 * (i16 & 3);
+        const s16x4_t lo = read_b_tr(st + A_BYTES, kb, n);
+        const s16x4_t hi = read_b_tr(st + A_BYTES, kb + 4, n);
+        b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+  };
+  auto mma = [&](const bf16x8_t (&a)[NA], const bf16x8_t (&b)[4]) {
+    if constexpr (NL > 0) {
+#pragma unroll
+      for (int u = 0; u < NL; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[u], acc[u][j], 0, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < S; ++i)
+    if (i < nk) issue(i, i);
+  wait_groups<DMA>(min(S - 1, nk - 1));
+  barrier_lds_only();
+
+  bf16x8_t a0[NA], b0[4], a1[NA], b1[4];
+  read(lds, 0, a0, b0);
+  int stage = 0;
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    const lds_char* cur = lds + stage * STAGE;
+    const int next = stage == S - 1 ? 0 : stage + 1;
+    read(cur, 1, a1, b1);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_groups<DMA>(min(S - 2, nk - kt - 2));
+    barrier_after_lds_reads();
+    if (!late && kt + S < nk) issue(kt + S, stage);
+    read(lds + next * STAGE, 0, a0, b0);
+    mma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (late && kt + S < nk) issue(kt + S, stage);
+    stage = next;
+  }
+  if (nk >= 1) {
+    read(lds + stage * STAGE, 1, a1, b1);
+    mma(a0, b0);
+    mma(a1, b1);
+  }
+}
+
+template <int S, int NL, bool NT, class ABase, class BBase>
+__device__ __forceinline__ void mainloop_a(int nad, int nk, lds_char* lds, ABase a_base,
+                                           const uint32_t (&a_off)[A_DMA], BBase b_base, uint32_t b_off,
+                                           const int (&bcol)[4], f32x16_t (&acc)[3][4]) {
+  if (nad >= 2) mainloop_v<S, NL, 2, NT>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else if (nad == 1) mainloop_v<S, NL, 1, NT>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+  else mainloop_v<S, NL, 0, NT>(nk, lds, a_base, a_off, b_base, b_off, bcol, acc);
+}
+
+template <int S, class ABase, class BBase>
+__device__ __forceinline__ void mainloop(int nk, int rows, lds_char* lds, ABase a_base,
+                                         const uint32_t (&a_off)[A_DMA], BBase b_base, uint32_t b_off,
+                                         const int (&bcol)[4], f32x16_t (&acc)[3][4], bool nt) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nad = needed_a(rows, wave);
+  const int nl = live(rows, wave >> 2);
+  auto go = [&](auto ntc) {
+    constexpr bool N = decltype(ntc)::value;
+    switch (nl) {
+      case 3: mainloop_a<S, 3, N>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+      case 2: mainloop_a<S, 2, N>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+      case 1: mainloop_a<S, 1, N>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+      default: mainloop_a<S, 0, N>(nad, nk, lds, a_base, a_off, b_base, b_off, bcol, acc); break;
+    }
+  };
+  if (nt) go(std::true_type());
+  else go(std::false_type());
+}
+}  // namespace wide
 
 // Workgroup-index remap so that consecutive logical tiles run on the same XCD: workgroups are
 // dispatched round-robin over the 8 XCDs, so physical block b runs on XCD b % 8. Logical tiles

@@ -106,12 +106,22 @@ SMALL_CASES = [
     ("topk_wide_f32", 20, 64, 130, 4, 32, 32, syn.F32, 1, 0.0),
     # equal row tiles (<= 192 rows per expert on average) under Zipf-skewed loads of ~50 .. ~650 rows
     ("balanced_tiles_skewed", 700, 512, 16, 4, 256, 128, syn.BF16, 1, 0.8),
-    # 160-row tall tiles (>= 256 rows per expert on average): three row tiles of 4, 4, 3 sub-tiles;
-    # a shared expert wider than the routed ones over four row tiles (4, 4, 4, 5 sub-tiles); and
-    # Zipf-skewed loads from every token down to a few rows (one partial sub-tile)
-    ("tall_tiles", 700, 512, 8, 4, 256, 256, syn.BF16, 1, 0.0),
-    ("tall_tiles_wide_shared", 513, 1024, 4, 2, 256, 512, syn.BF16, 1, 0.0),
-    ("tall_tiles_skewed", 2000, 512, 16, 4, 256, 0, syn.BF16, 0, 1.2),
+    # 160-row tall tiles (150 .. 256 rows per expert on average): ~200-row experts as two row tiles
+    # of 3 and 4 sub-tiles and the 400 shared rows as three (4, 4, 5); Zipf-skewed loads from
+    # ~500 rows down to a few (one partial sub-tile)
+    ("tall_tiles", 400, 512, 8, 4, 256, 256, syn.BF16, 1, 0.0),
+    ("tall_tiles_skewed", 700, 512, 16, 4, 256, 0, syn.BF16, 0, 1.2),
+    # 192-row wide tiles (>= 256 rows per expert on average): ~350-row experts as two row tiles of
+    # 5 and 6 sub-tiles; a shared expert wider than the routed ones over three row tiles (5, 6, 6);
+    # Zipf-skewed loads from every token down to a few rows; k = E, so that every group holds T
+    # rows: 576 as three full tiles, 257 as two (4 and 5 sub-tiles, one row in the last), 384 as two
+    # full tiles
+    ("wide_tiles", 700, 512, 8, 4, 256, 256, syn.BF16, 1, 0.0),
+    ("wide_tiles_wide_shared", 513, 1024, 4, 2, 256, 512, syn.BF16, 1, 0.0),
+    ("wide_tiles_skewed", 2000, 512, 16, 4, 256, 0, syn.BF16, 0, 1.2),
+    ("wide_tiles_576", 576, 512, 4, 4, 256, 256, syn.BF16, 1, 0.0),
+    ("wide_tiles_257", 257, 512, 4, 4, 256, 512, syn.BF16, 1, 0.0),
+    ("wide_tiles_384", 384, 1024, 4, 4, 512, 256, syn.BF16, 0, 0.0),
 ]
 
 
