@@ -930,9 +930,10 @@ int ffn_tile_rows(const moe_dims& dm) {
   return P.wide ? stream::wide::ROWS : P.tall ? stream::tall::ROWS : kMfmaBM;
 }
 
-hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s) {
+hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s,
+                              int bm) {
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, dm.T, dm.E, dm.I_shared > 0 ? 1 : 0,
-                     ffn_tile_rows(dm), (int32_t*)(ws + L.tile_group), (int32_t*)(ws + L.tile_m0),
+                     bm > 0 ? bm : ffn_tile_rows(dm), (int32_t*)(ws + L.tile_group), (int32_t*)(ws + L.tile_m0),
                      (int32_t*)(ws + L.tile_count), (int32_t*)(ws + L.ffn_cnt), 2 * L.ffn_cnt_each);
   return hipGetLastError();
 }

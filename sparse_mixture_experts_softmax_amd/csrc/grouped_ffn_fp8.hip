@@ -22,6 +22,10 @@
 // workgroups per CU. Schedule, DMA and the A operand as in stream_gemm.h. The B stage holds two
 // code tiles (gate and up at the same columns, or two adjacent column tiles of W_d); B instruction
 // q (0..7; wave w issues 2w, 2w+1) copies bytes 1024 (q % 4) .. +1023 of tile q / 4, 16 per lane.
+// With 32 tokens or fewer every group holds at most 32 rows, only the first 32-row sub-tile is ever
+// live, and the stages keep A room for 32 rows (2 KB): four stages of 10 KB per workgroup, four
+// workgroups per CU, 128 instead of 80 KB of codes in flight per CU (decode layer 2.00 -> 1.96 ms;
+// two workgroups of eight such stages, the same bytes in flight, measured 2.10 ms).
 #include "fp8_codec.h"
 #include "moe_internal.h"
 #include "stream_gemm.h"
@@ -32,11 +36,16 @@ namespace {
 using namespace stream;
 
 constexpr int F8_COLS = 256;
-constexpr int F8_A_BYTES = SBM * SBK * 2;    // 8 KB
 constexpr int F8_B_BYTES = F8_COLS * SBK;    // 8 KB
-constexpr int F8_STAGE = F8_A_BYTES + F8_B_BYTES;
-constexpr int F8_A_DMA = 2;                  // per wave per stage
+constexpr int F8_A_DMA = 2;                  // per wave per stage (at most)
 constexpr int F8_B_DMA = 2;
+// A room per stage for AR rows (128: the full tile; 32: few-token launches), and the stage
+template <int AR>
+struct F8Geo {
+  static_assert(AR == 128 || AR == 32, "A rows");
+  static constexpr int A_BYTES = AR * SBK * 2;  // 8 KB or 2 KB
+  static constexpr int STAGE = A_BYTES + F8_B_BYTES;
+};
 
 // 8 e4m3 codes (K-consecutive) -> 8 bf16: exact through fp32 (the top half of each fp32 value)
 __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
@@ -67,11 +76,15 @@ __device__ __forceinline__ bf16x8_t read_b_f8(const lds_char* sb, int n, int s, 
 // a_off / b_off[i]: per-lane byte offsets. Same schedule as stream::mainloop_v.
 // NAD: A instructions this wave issues (those whose 16 rows hold a valid row of the tile).
 // NT: code DMAs with the non-temporal hint (the group's only row tile reads them).
-template <int S, int NL, int NAD, bool NT, class ABase, class BBase>
+// AR: A rows per stage (F8Geo); with 32, only the first sub-tile of wave row 0 may be live.
+template <int S, int NL, int NAD, bool NT, int AR, class ABase, class BBase>
 __device__ __forceinline__ void mainloop_f8(int nk, lds_char* lds, ABase a_base, const uint32_t (&a_off)[F8_A_DMA],
                                             BBase b_base, const uint32_t (&b_off)[F8_B_DMA], const int (&bcol)[4],
                                             f32x16_t (&acc)[2][4]) {
-  static_assert(S >= 3 && S <= 6, "stages");
+  static_assert(S >= 3 && S <= 8, "stages");
+  static_assert(AR == SBM || NL <= 1, "32 A rows hold one sub-tile");
+  constexpr int F8_A_BYTES = F8Geo<AR>::A_BYTES;
+  constexpr int F8_STAGE = F8Geo<AR>::STAGE;
   constexpr int F8_DMA = NAD + F8_B_DMA;
   constexpr int NA = NL > 0 ? NL : 1;
   const int lane = threadIdx.x & 63;
@@ -157,10 +170,11 @@ struct Fp8Args {
   int n_ntiles;
 };
 
-template <bool GATED, int S>
+// AR = 32: launched only when every group holds at most 32 rows (T <= 32)
+template <bool GATED, int S, int AR>
 __global__ void __launch_bounds__(256, 2) ffn_fp8_stream_kernel(Fp8Args p) {
   constexpr int TN = GATED ? F8_COLS / 2 : F8_COLS;  // output columns per tile
-  __shared__ __attribute__((aligned(1024))) char smem[S * F8_STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[S * F8Geo<AR>::STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -237,14 +251,19 @@ __global__ void __launch_bounds__(256, 2) ffn_fp8_stream_kernel(Fp8Args p) {
   auto run = [&](auto nlc, auto ntc) {
     constexpr int NL = decltype(nlc)::value;
     constexpr bool NT = decltype(ntc)::value;
-    if (nad >= 2) mainloop_f8<S, NL, 2, NT>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
-    else if (nad == 1) mainloop_f8<S, NL, 1, NT>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
-    else mainloop_f8<S, NL, 0, NT>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+    if (nad >= 2) mainloop_f8<S, NL, 2, NT, AR>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+    else if (nad == 1) mainloop_f8<S, NL, 1, NT, AR>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+    else mainloop_f8<S, NL, 0, NT, AR>(nk, (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
   };
   auto run_nt = [&](auto ntc) {
-    if (nl >= 2) run(std::integral_constant<int, 2>(), ntc);
-    else if (nl == 1) run(std::integral_constant<int, 1>(), ntc);
-    else run(std::integral_constant<int, 0>(), ntc);
+    if constexpr (AR == SBM) {
+      if (nl >= 2) run(std::integral_constant<int, 2>(), ntc);
+      else if (nl == 1) run(std::integral_constant<int, 1>(), ntc);
+      else run(std::integral_constant<int, 0>(), ntc);
+    } else {
+      if (nl >= 1) run(std::integral_constant<int, 1>(), ntc);
+      else run(std::integral_constant<int, 0>(), ntc);
+    }
   };
   if (cnt == 1) run_nt(std::true_type());
   else run_nt(std::false_type());
@@ -368,9 +387,12 @@ hipError_t launch_grouped_ffn_fp8(const moe_dims& dm, const Layout& L, const voi
   const Prof none;
   if (!prof) prof = &none;
   // five stages of 16 KB (80 KB of LDS, still two workgroups per CU): with the non-temporal code
-  // stream, the deeper lookahead took decode gate/up from 1.34 to 1.29 ms
-  constexpr int S = 5;
-  hipError_t e = launch_build_tiles(dm, L, offsets, ws, s);
+  // stream, the deeper lookahead took decode gate/up from 1.34 to 1.29 ms. At most 32 tokens:
+  // four stages of 10 KB (32 A rows), four workgroups per CU.
+  constexpr int S = 5, S_THIN = 4;
+  const bool thin = dm.T <= 32;
+  // 128-row tiles, whatever the bf16 GEMMs would use for these dims
+  hipError_t e = launch_build_tiles(dm, L, offsets, ws, s, SBM);
   if (e != hipSuccess) return e;
   const int has_shared = dm.I_shared > 0 ? 1 : 0;
   const int64_t Tk = dm.T * dm.k;
@@ -402,7 +424,12 @@ hipError_t launch_grouped_ffn_fp8(const moe_dims& dm, const Layout& L, const voi
   a.out = H;
   a.n_ntiles = (L.ldh + F8_COLS / 2 - 1) / (F8_COLS / 2);
   if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((ffn_fp8_stream_kernel<true, S>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
+  if (thin)
+    hipLaunchKernelGGL((ffn_fp8_stream_kernel<true, S_THIN, 32>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((ffn_fp8_stream_kernel<true, S, SBM>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s,
+                       a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = prof->end(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
   // down
@@ -418,7 +445,12 @@ hipError_t launch_grouped_ffn_fp8(const moe_dims& dm, const Layout& L, const voi
   a.out = (bf16_t*)y;
   a.n_ntiles = dm.d / F8_COLS;
   if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((ffn_fp8_stream_kernel<false, S>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s, a);
+  if (thin)
+    hipLaunchKernelGGL((ffn_fp8_stream_kernel<false, S_THIN, 32>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((ffn_fp8_stream_kernel<false, S, SBM>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(256), 0, s,
+                       a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return prof->end(MOE_KERNEL_FFN_DOWN, s);
 }

@@ -217,7 +217,9 @@ hipError_t launch_ffn_skinny(const moe_dims& dm, const Layout& L, const FfnPlan&
 
 // row-tile list of the grouped GEMMs (rows per tile ffn_tile_rows) and zeroed split-K counters
 int ffn_tile_rows(const moe_dims& dm);
-hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s);
+// bm: rows per tile of the list (0: ffn_tile_rows(dm), the bf16 grouped GEMMs' choice)
+hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s,
+                              int bm = 0);
 
 // FP8 (e4m3) expert weights: codes in 4 KB tiles of 128 columns x 32 K values (moe_quantize_fp8
 // layout) with one fp32 scale per output column

@@ -153,13 +153,20 @@ __device__ __forceinline__ s16x4_t read_b_tr(const lds_char* sb, int k, int n) {
 // k-step kt+S go into it, and the next stage's first fragments are read while the second
 // sub-step's MFMAs run: LDS latency after the barrier hides behind MFMAs.
 
-// wait until at most n (0 .. 3) DMA groups of DMA instructions are outstanding
+// wait until at most n (0 .. 7; more counts as 7) DMA groups of DMA instructions are outstanding
 template <int DMA>
 __device__ __forceinline__ void wait_groups(int n) {
-  if (n >= 3) wait_vmcnt<3 * DMA>();
-  else if (n == 2) wait_vmcnt<2 * DMA>();
-  else if (n == 1) wait_vmcnt<DMA>();
-  else wait_vmcnt<0>();
+  static_assert(7 * DMA < 64, "vmcnt range");
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<DMA>(); break;
+    case 2: wait_vmcnt<2 * DMA>(); break;
+    case 3: wait_vmcnt<3 * DMA>(); break;
+    case 4: wait_vmcnt<4 * DMA>(); break;
+    case 5: wait_vmcnt<5 * DMA>(); break;
+    case 6: wait_vmcnt<6 * DMA>(); break;
+    default: wait_vmcnt<7 * DMA>(); break;
+  }
 }
 
 template <int WN, int S, int NL, int NAD, bool NT, class ABase, class BBase>

@@ -497,6 +497,10 @@ FP8_CASES = [
     # few tokens: 32-row tiles (T <= 32; the shared expert fills one) and 64-row tiles (T <= 64)
     syn.MoEConfig("fp8_T32", T=32, d=2048, E=64, k=6, I=512, Is=512, dtype=syn.BF16, seed=65),
     syn.MoEConfig("fp8_T48", T=48, d=1024, E=32, k=4, I=256, Is=384, dtype=syn.BF16, seed=66),
+    # row counts at which the bf16 GEMMs take 160-row (~150 per expert) and 192-row (~350) tiles:
+    # the FP8 GEMMs keep their own 128-row tile list
+    syn.MoEConfig("fp8_tall_rows", T=300, d=512, E=8, k=4, I=256, Is=256, dtype=syn.BF16, seed=67),
+    syn.MoEConfig("fp8_wide_rows", T=700, d=512, E=8, k=4, I=256, Is=256, dtype=syn.BF16, seed=68),
 ]
 
 
