@@ -6,7 +6,8 @@
 //   out[t] = sum_{j<k} w[t,j] * y[slot_of[t*k+j]]  +  y[T*k + t]  (+ residual[t])
 //
 // One workgroup per token (256 threads; up to 1024 for few tokens); each thread owns
-// 8 consecutive hidden elements at a time (16-byte bf16 or 2x16-byte fp32 loads),
+// 8 consecutive hidden elements at a time (16-byte bf16 or 2x16-byte fp32 loads; bf16 expert rows
+// with the non-temporal hint when they far exceed the last-level cache),
 // issues the loads of all k+1 rows before the first add, accumulates in fp32 in the fixed order j = 0..k-1,
 // the shared row, then the residual row (the block's input, when the caller
 // asks for the residual add), and rounds once on store. Pairs with slot_of = -1 (an
@@ -19,7 +20,17 @@ namespace {
 // 8 consecutive elements, raw (loaded) and widened to fp32
 struct Raw8bf { uint4 w; };
 struct Raw8f { float4 a, b; };
-__device__ __forceinline__ void load_raw(const bf16_t* p, Raw8bf& r) { r.w = *(const uint4*)p; }
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+template <bool NT = false>
+__device__ __forceinline__ void load_raw(const bf16_t* p, Raw8bf& r) {
+  if constexpr (NT) {
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+    r.w = make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    r.w = *(const uint4*)p;
+  }
+}
+template <bool NT = false>
 __device__ __forceinline__ void load_raw(const float* p, Raw8f& r) {
   r.a = *(const float4*)p;
   r.b = *(const float4*)(p + 4);
@@ -51,7 +62,9 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
   *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-template <typename ET, int MAXT>
+// NT: the expert output rows y with the non-temporal hint (each is read once here, and at the
+// prefill shape they span ~3 GB, past any cache)
+template <typename ET, int MAXT, bool NT = false>
 __global__ void __launch_bounds__(MAXT)
 combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, const float* __restrict__ topk_w,
                const ET* __restrict__ residual, ET* __restrict__ out, int64_t T, int d, int k, int has_shared) {
@@ -70,8 +83,8 @@ combine_kernel(const ET* __restrict__ y, const int32_t* __restrict__ slot_of, co
     Raw raw[kMaxK + 2];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
-      if (j < k && s_slot[j] >= 0) load_raw(y + (int64_t)s_slot[j] * d + c, raw[j]);
-    if (has_shared) load_raw(y + shared_row * d + c, raw[kMaxK]);
+      if (j < k && s_slot[j] >= 0) load_raw<NT>(y + (int64_t)s_slot[j] * d + c, raw[j]);
+    if (has_shared) load_raw<NT>(y + shared_row * d + c, raw[kMaxK]);
     if (residual) load_raw(residual + t * d + c, raw[kMaxK + 1]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -113,6 +126,12 @@ hipError_t launch_combine(const moe_dims& dm, const void* y, const int32_t* slot
     while (threads < 1024 && threads * 8 < dm.d) threads *= 2;
   if (dm.dtype == MOE_BF16 && threads > 256)
     hipLaunchKernelGGL((combine_kernel<bf16_t, 1024>), dim3((unsigned)dm.T), dim3(threads), 0, s, (const bf16_t*)y,
+                       slot_of, topk_w, (const bf16_t*)residual, (bf16_t*)out, dm.T, dm.d, dm.k, hs);
+  else if (dm.dtype == MOE_BF16 && (uint64_t)(dm.T * dm.k + (hs ? dm.T : 0)) * dm.d * 2 > (512ull << 20))
+    // expert outputs at least twice the 256 MB last-level cache: non-temporal reads (prefill
+    // combine 636 -> 577 us, skew 322 -> 281 us; at the mid shape, ~150 MB, the rows come from the
+    // cache and stay on plain loads)
+    hipLaunchKernelGGL((combine_kernel<bf16_t, 256, true>), dim3((unsigned)dm.T), dim3(256), 0, s, (const bf16_t*)y,
                        slot_of, topk_w, (const bf16_t*)residual, (bf16_t*)out, dm.T, dm.d, dm.k, hs);
   else if (dm.dtype == MOE_BF16)
     hipLaunchKernelGGL((combine_kernel<bf16_t, 256>), dim3((unsigned)dm.T), dim3(256), 0, s, (const bf16_t*)y,

@@ -106,6 +106,10 @@ SMALL_CASES = [
     ("topk_wide_f32", 20, 64, 130, 4, 32, 32, syn.F32, 1, 0.0),
     # equal row tiles (<= 192 rows per expert on average) under Zipf-skewed loads of ~50 .. ~650 rows
     ("balanced_tiles_skewed", 700, 512, 16, 4, 256, 128, syn.BF16, 1, 0.8),
+    # one or two tokens with more than 64 experts (top-k on four wavefronts per token, skinny
+    # GEMMs); a shared expert wider than the routed ones (three column blocks of 256 against two)
+    ("skinny_many_experts_T1", 1, 1024, 128, 6, 512, 512, syn.BF16, 1, 0.0),
+    ("skinny_many_experts_T2", 2, 2048, 96, 8, 512, 768, syn.BF16, 0, 0.0),
     # 160-row tall tiles (150 .. 256 rows per expert on average): ~200-row experts as two row tiles
     # of 3 and 4 sub-tiles and the 400 shared rows as three (4, 4, 5); Zipf-skewed loads from
     # ~500 rows down to a few (one partial sub-tile)
@@ -535,6 +539,8 @@ def test_fp8_forward_matches_oracle(torch, cfg):
 GRAPH_CASES = [
     ("bf16_split_k", syn.MoEConfig("graph_split_k", T=3, d=2048, E=32, k=6, I=512, Is=256, dtype=syn.BF16, seed=71)),
     ("bf16_skinny", syn.MoEConfig("graph_skinny", T=1, d=2048, E=32, k=6, I=512, Is=512, dtype=syn.BF16, seed=75)),
+    ("bf16_skinny_many_experts", syn.MoEConfig("graph_skinny_e96", T=2, d=2048, E=96, k=6, I=512, Is=512,
+                                               dtype=syn.BF16, seed=76)),
     ("bf16_mid_width", syn.MoEConfig("graph_mid", T=300, d=2048, E=64, k=8, I=512, Is=512, dtype=syn.BF16, seed=72)),
     ("fp8", syn.MoEConfig("graph_fp8", T=40, d=1024, E=32, k=4, I=256, Is=256, dtype=syn.BF16, seed=73)),
     ("block", syn.MoEConfig("graph_block", T=200, d=512, E=24, k=4, I=256, Is=128, dtype=syn.BF16, seed=74)),
