@@ -295,6 +295,15 @@ def measure(run, lib, hip, stream, steps, warmup):
     return step_ms, kern_ms, wall, idx.cpu().numpy()
 
 
+def kernel_label(cfg, fp8):
+    """The gate/up kernel the library launches for this workload, as a trace names it."""
+    import sparse_mixture_experts_softmax_amd as moe
+    dims = moe.MoeDims(T=cfg.T, d=cfg.d, E=cfg.E, k=cfg.k, I=cfg.I, I_shared=cfg.Is, dtype=cfg.dtype,
+                       renormalize=cfg.renorm)
+    name = moe.moe_kernel_name(dims, moe.KERNEL_FFN_GATE_UP, fp8)
+    return name + (" (gate/up, e4m3 weights)" if fp8 else " (gate/up)")
+
+
 def roofline(wl, syn, cfg, kb, kf, kern_med_ms, fp8):
     """The dominant kernel against its bound: HBM when its algorithmic bytes take longer at 8 TB/s
     than its FLOPs at the matrix cores' peak, the matrix cores otherwise."""
@@ -306,8 +315,7 @@ def roofline(wl, syn, cfg, kb, kf, kern_med_ms, fp8):
         roof = {"bound": "mfma" if cfg.dtype == syn.BF16 else "alu", "achieved": kf / t_s / 1e12,
                 "peak": peak_flops / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = ("ffn_fp8_stream_kernel<true, 4> (gate/up, e4m3 weights)" if fp8 else
-                      "ffn_mfma_stream_kernel<true, ...> (gate/up)" if cfg.dtype == syn.BF16 else "ffn_f32_kernel<true>")
+    roof["kernel"] = kernel_label(cfg, fp8)
     roof["kernel_ms"] = kern_med_ms
     roof["algorithmic_bytes"] = kb
     roof["algorithmic_flops"] = kf

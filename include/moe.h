@@ -262,6 +262,13 @@ typedef enum {
 
 moe_status moe_profile_next_forward(int32_t kernel, hipEvent_t start, hipEvent_t stop);
 
+/* Name of the main kernel that moe_forward (fp8 = 0) or moe_forward_fp8 (fp8 = 1) launches with
+ * these dims for one step of the path (kernel: a moe_kernel_id other than MOE_KERNEL_NONE), as
+ * it appears in a kernel trace, for labelling measurements. Host only: launches nothing, sets no
+ * error text. Returns a static string, or NULL for invalid dims, an unknown id, or dims the FP8
+ * path does not take. */
+const char* moe_kernel_name(const moe_dims* dims, int32_t kernel, int32_t fp8);
+
 /* Static name of a status code. */
 const char* moe_status_string(moe_status status);
 

@@ -79,6 +79,8 @@ def load_library(path=None):
     lib.moe_forward_noalloc.restype = st
     lib.moe_profile_next_forward.argtypes = [ctypes.c_int32, _P, _P]
     lib.moe_profile_next_forward.restype = st
+    lib.moe_kernel_name.argtypes = [D, ctypes.c_int32, ctypes.c_int32]
+    lib.moe_kernel_name.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
@@ -221,6 +223,18 @@ def moe_workspace_size(dims):
     n = ctypes.c_size_t(0)
     _check(load_library().moe_workspace_size(ctypes.byref(dims), ctypes.byref(n)))
     return n.value
+
+
+KERNEL_ROUTER, KERNEL_PERMUTE, KERNEL_FFN_GATE_UP, KERNEL_FFN_DOWN, KERNEL_COMBINE = 1, 2, 3, 4, 5
+
+
+def moe_kernel_name(dims, kernel, fp8=False):
+    """Name of the kernel the forward launches for one step with these dims (moe_kernel_name)."""
+    _need_dims(dims)
+    name = load_library().moe_kernel_name(ctypes.byref(dims), int(kernel), 1 if fp8 else 0)
+    if name is None:
+        raise ValueError("no kernel name for kernel id %r with these dims" % (kernel,))
+    return name.decode()
 
 
 def workspace(dims, device):

@@ -924,6 +924,23 @@ hipError_t launch_gate_up_finish(const float* part, int64_t sstride, int64_t par
   return hipGetLastError();
 }
 
+const char* ffn_kernel_name(const moe_dims& dm, bool gate_up) {
+  if (dm.dtype == MOE_F32) return gate_up ? "ffn_f32_kernel<true>" : "ffn_f32_kernel<false>";
+  const FfnPlan P = ffn_plan(dm);
+  if (P.skinny) {
+    if (P.skinny_rows == 1) return gate_up ? "ffn_skinny_kernel<true, 1>" : "ffn_skinny_kernel<false, 1>";
+    return gate_up ? "ffn_skinny_kernel<true, 2>" : "ffn_skinny_kernel<false, 2>";
+  }
+  if (P.wide) return gate_up ? "ffn_mfma_wide_kernel<true, 3>" : "ffn_mfma_wide_kernel<false, 3>";
+  if (P.tall) return gate_up ? "ffn_mfma_tall_kernel<true, 3>" : "ffn_mfma_tall_kernel<false, 3>";
+  if (P.stream) {
+    if ((gate_up ? P.wn1 : P.wn2) == 4)
+      return gate_up ? "ffn_mfma_stream_kernel<true, 4, 4>" : "ffn_mfma_stream_kernel<false, 4, 4>";
+    return gate_up ? "ffn_mfma_stream_kernel<true, 2, 3>" : "ffn_mfma_stream_kernel<false, 2, 3>";
+  }
+  return gate_up ? "ffn_mfma_kernel<true>" : "ffn_mfma_kernel<false>";
+}
+
 int ffn_tile_rows(const moe_dims& dm) {
   if (dm.dtype == MOE_F32) return kF32BM;
   const FfnPlan P = ffn_plan(dm);

@@ -381,6 +381,11 @@ bool fp8_shape_ok(const moe_dims& dm) {
          (uint64_t)(dm.T * dm.k + dm.T) * (dm.I > dm.I_shared ? dm.I : dm.I_shared) * 2 < (1ull << 32);
 }
 
+const char* ffn_fp8_kernel_name(const moe_dims& dm, bool gate_up) {
+  if (dm.T <= 32) return gate_up ? "ffn_fp8_stream_kernel<true, 4, 32>" : "ffn_fp8_stream_kernel<false, 4, 32>";
+  return gate_up ? "ffn_fp8_stream_kernel<true, 5, 128>" : "ffn_fp8_stream_kernel<false, 5, 128>";
+}
+
 hipError_t launch_grouped_ffn_fp8(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
                                   const int32_t* sorted_token, const Fp8Weights& W, void* y, char* ws, hipStream_t s,
                                   const Prof* prof) {

@@ -189,6 +189,27 @@ const char* moe_status_string(moe_status st) {
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
+const char* moe_kernel_name(const moe_dims* dims, int32_t kernel, int32_t fp8) {
+  if (check_dims(dims) != MOE_OK) return nullptr;
+  const moe_dims& dm = *dims;
+  if (fp8 && !fp8_shape_ok(dm)) return nullptr;
+  const Layout L = make_layout(dm);
+  switch (kernel) {
+    case MOE_KERNEL_ROUTER:
+      return L.router_mfma ? "router_mfma_kernel" : dm.T <= 64 ? "router_small_kernel" : "router_logits_kernel";
+    case MOE_KERNEL_PERMUTE:
+      return L.nchunks == 1 ? "permute_one_chunk_kernel" : "permute_count_kernel";
+    case MOE_KERNEL_FFN_GATE_UP:
+      return fp8 ? ffn_fp8_kernel_name(dm, true) : ffn_kernel_name(dm, true);
+    case MOE_KERNEL_FFN_DOWN:
+      return fp8 ? ffn_fp8_kernel_name(dm, false) : ffn_kernel_name(dm, false);
+    case MOE_KERNEL_COMBINE:
+      return "combine_kernel";
+    default:
+      return nullptr;
+  }
+}
+
 moe_status moe_profile_next_forward(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
   if (kernel == MOE_KERNEL_NONE) {
     g_prof = Prof();

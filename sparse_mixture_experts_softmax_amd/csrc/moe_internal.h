@@ -215,6 +215,10 @@ hipError_t launch_ffn_skinny(const moe_dims& dm, const Layout& L, const FfnPlan&
                              const void* wd, const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
                              hipStream_t s, const Prof* prof);
 
+// names of the grouped GEMM kernels these dims launch (static strings)
+const char* ffn_kernel_name(const moe_dims& dm, bool gate_up);
+const char* ffn_fp8_kernel_name(const moe_dims& dm, bool gate_up);
+
 // row-tile list of the grouped GEMMs (rows per tile ffn_tile_rows) and zeroed split-K counters
 int ffn_tile_rows(const moe_dims& dm);
 // bm: rows per tile of the list (0: ffn_tile_rows(dm), the bf16 grouped GEMMs' choice)
