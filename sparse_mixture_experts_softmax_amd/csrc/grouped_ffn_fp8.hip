@@ -303,6 +303,219 @@ __global__ void __launch_bounds__(256, 2) ffn_fp8_stream_kernel(Fp8Args p) {
 }
 
 // ------------------------------------------------------------------------------------------
+// One or two tokens: weight streams over the code tiles on the vector ALUs, as the bf16 skinny
+// kernels do (grouped_ffn_skinny.hip). One workgroup (256 threads) per (group, 128-column code
+// panel, K split); thread t reads the 16-byte chunk t of every 4 KB code tile of its split --
+// column t / 2, one half of the column's 32 K values -- so a wavefront reads 1 KB of contiguous
+// codes, and the two threads of a column add their halves at the end. The x (or H) values of the
+// split sit in LDS as fp32. Column scales are powers of two, so scaling each split's sums is
+// exact: the gate/up product's splits go out scaled, as fp32 partial rows that
+// gate_up_finish_kernel adds in split order and finishes with silu * up (H directly with a single
+// split); the down product runs unsplit (K = I <= 2048) and writes Y.
+// ------------------------------------------------------------------------------------------
+struct Fp8SkinnyArgs {
+  const bf16_t* a_src;  // gate/up: x [T, d]; down: H [rows_total, ldh]
+  const int32_t* offsets;
+  const int32_t* sorted_token;
+  const uint8_t* w0;
+  const uint8_t* w1;
+  const float* s0;
+  const float* s1;
+  const uint8_t* w0_s;
+  const uint8_t* w1_s;
+  const float* s0_s;
+  const float* s1_s;
+  bf16_t* out;
+  const int32_t* tile_group;
+  const int32_t* tile_count;
+  int64_t T;
+  int d, E, k, I, Is, ldh;
+  int n_cblk;  // 128-column panels of the widest group
+  int ks, kc;  // K splits, K rows per split (multiple of 32, <= kSkinnyMaxKC)
+  float* part;  // gate/up with ks > 1: scaled fp32 partial rows part[split][row][part_ld]
+  int64_t part_ld, part_sstride;
+};
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_codes16(const uint8_t* q) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)q);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// four e4m3 codes (bytes 0 .. 3 of w, in K order) -> fp32, exactly
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* f) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  f[0] = a[0];
+  f[1] = a[1];
+  f[2] = b[0];
+  f[3] = b[1];
+}
+
+template <bool GATED, int R>
+__global__ void __launch_bounds__(256, 2) ffn_fp8_skinny_kernel(Fp8SkinnyArgs p) {
+  constexpr int NM = GATED ? 2 : 1;  // code matrices
+  constexpr int KU = 8;              // code tiles in flight per thread and matrix
+  __shared__ __attribute__((aligned(16))) float s_a[R][kSkinnyMaxKC];
+  const int tid = threadIdx.x;
+
+  const int per_tile = p.n_cblk * p.ks;
+  const int mt = blockIdx.x / per_tile;
+  if (mt >= *p.tile_count) return;
+  const int rem = blockIdx.x - mt * per_tile;
+  const int cb = rem / p.ks;
+  const int split = rem - cb * p.ks;
+  const int g = p.tile_group[mt];
+  const Group G = group_info(g, p.offsets, p.T, p.k, p.E, p.I, p.Is);
+  const int K = GATED ? p.d : G.n_inter;
+  const int N = GATED ? G.n_inter : p.d;
+  const int n0 = cb * 128;
+  if (n0 >= N) return;
+  const int rows = G.rows;  // <= R
+  const int k0 = split * p.kc;
+  const int k1 = min(K, k0 + p.kc);  // k1 <= k0: an empty split (partials of zero)
+
+  const uint8_t *W0, *W1 = nullptr;
+  const float *S0, *S1 = nullptr;
+  if (GATED) {
+    W0 = G.shared ? p.w0_s : p.w0 + (size_t)g * p.I * p.d;
+    W1 = G.shared ? p.w1_s : p.w1 + (size_t)g * p.I * p.d;
+    S0 = G.shared ? p.s0_s : p.s0 + (size_t)g * p.I;
+    S1 = G.shared ? p.s1_s : p.s1 + (size_t)g * p.I;
+  } else {
+    W0 = G.shared ? p.w0_s : p.w0 + (size_t)g * p.d * p.I;
+    S0 = G.shared ? p.s0_s : p.s0 + (size_t)g * p.d;
+  }
+  // chunk tid of each code tile of panel cb: column col, K values 16 half .. +16 of the tile
+  const uint8_t* q0 = W0 + (int64_t)cb * K * 128 + 16 * tid;
+  const uint8_t* q1 = GATED ? W1 + (int64_t)cb * K * 128 + 16 * tid : nullptr;
+  const int col = tid >> 1;
+  const int half = (tid & 1) ^ ((col >> 3) & 1);
+  const int kt0 = k0 / 32;
+  const int ntl = k1 > k0 ? (k1 - k0) / 32 : 0;  // code tiles of this split (K, kc multiples of 32)
+
+  // A rows of this split as fp32 (rows past the group's are zero), as in the bf16 skinny kernel
+  const int64_t a_ld = GATED ? p.d : p.ldh;
+  int64_t srow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rr = r < rows ? r : 0;
+    srow[r] = GATED ? (G.shared ? (int64_t)rr : (int64_t)p.sorted_token[G.row0 + rr]) : G.row0 + rr;
+  }
+  const int cpr = p.kc / 8;  // A chunks (8 values) per row; R * cpr <= R * 256
+  uint4 av[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = tid + 256 * j;
+    const int r = i / cpr;
+    const int c = i - r * cpr;
+    int64_t sr = srow[0];
+#pragma unroll
+    for (int q = 1; q < R; ++q)
+      if (r == q) sr = srow[q];
+    const bool valid = r < rows && k0 + 8 * c < k1;
+    av[j] = *(const uint4*)(p.a_src + (valid ? sr * a_ld + k0 + 8 * c : 0));
+    if (!valid) av[j] = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  uint4 buf[NM][KU];
+  auto load = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int64_t at = (int64_t)(kt0 + KU * b + u) * 4096;
+      buf[0][u] = load_codes16(q0 + at);
+      if (GATED) buf[NM - 1][u] = load_codes16(q1 + at);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the batch's loads go out before the work that follows
+  };
+  float acc[NM][R];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[m][r] = 0.f;
+  // this thread's 16 K values of code tile t (from k0) against the staged rows
+  auto tile = [&](const uint4 (&c)[NM], int t) {
+    const int kk = t * 32 + 16 * half;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      float w[16];
+      e4m3x4_to_f32(c[m].x, w);
+      e4m3x4_to_f32(c[m].y, w + 4);
+      e4m3x4_to_f32(c[m].z, w + 8);
+      e4m3x4_to_f32(c[m].w, w + 12);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const float4 a = *(const float4*)&s_a[r][kk + 4 * i4];
+          acc[m][r] = fmaf(a.x, w[4 * i4], acc[m][r]);
+          acc[m][r] = fmaf(a.y, w[4 * i4 + 1], acc[m][r]);
+          acc[m][r] = fmaf(a.z, w[4 * i4 + 2], acc[m][r]);
+          acc[m][r] = fmaf(a.w, w[4 * i4 + 3], acc[m][r]);
+        }
+    }
+  };
+  const int nbw = ntl / KU;  // whole batches
+  if (nbw > 0) load(0);  // the first batch goes out before the A rows are staged
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = tid + 256 * j;
+    const int r = i / cpr;
+    const int c = i - r * cpr;
+    if (r < R) {
+      float* dst = &s_a[r][8 * c];
+      *(float4*)dst = make_float4(bf16lo_to_f32(av[j].x), bf16hi_to_f32(av[j].x), bf16lo_to_f32(av[j].y),
+                                  bf16hi_to_f32(av[j].y));
+      *(float4*)(dst + 4) = make_float4(bf16lo_to_f32(av[j].z), bf16hi_to_f32(av[j].z), bf16lo_to_f32(av[j].w),
+                                        bf16hi_to_f32(av[j].w));
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the code loads stay in flight
+  for (int b = 0; b < nbw; ++b) {
+    if (b > 0) load(b);
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      uint4 c[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) c[m] = buf[m][u];
+      tile(c, KU * b + u);
+    }
+  }
+  for (int t = nbw * KU; t < ntl; ++t) {  // tiles past the whole batches, one at a time
+    uint4 c[NM];
+    const int64_t at = (int64_t)(kt0 + t) * 4096;
+    c[0] = load_codes16(q0 + at);
+    if (GATED) c[NM - 1] = load_codes16(q1 + at);
+    tile(c, t);
+  }
+
+  // the column's two halves, then one thread per column writes
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[m][r] += __shfl_xor(acc[m][r], 1, 64);
+  if (tid & 1) return;
+  const int n = n0 + col;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= rows) break;
+    const int64_t row = G.row0 + r;
+    if (GATED) {
+      const float gs = acc[0][r] * S0[n], us = acc[NM - 1][r] * S1[n];
+      if (p.ks > 1) {
+        float* q = p.part + (int64_t)split * p.part_sstride + row * p.part_ld + n;
+        q[0] = gs;
+        q[p.ldh] = us;
+      } else {
+        p.out[row * p.ldh + n] = f32_to_bf16(silu_f32(gs) * us);
+      }
+    } else {
+      p.out[row * (int64_t)p.d + n] = f32_to_bf16(acc[0][r] * S0[n]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // quantiser: w [batch, K, N] -> codes [batch] x (N / 128 x K / 32 tiles of 4 KB), scales [batch, N]
 // ------------------------------------------------------------------------------------------
 template <typename WT>
@@ -381,7 +594,110 @@ bool fp8_shape_ok(const moe_dims& dm) {
          (uint64_t)(dm.T * dm.k + dm.T) * (dm.I > dm.I_shared ? dm.I : dm.I_shared) * 2 < (1ull << 32);
 }
 
+namespace {
+
+// K split of the skinny gate/up product over the code streams (one or two tokens, ldh <=
+// kSkinnyMaxKC): ~1024 workgroups (what the CUs hold at once) with 256 to kSkinnyMaxKC K values
+// per split and no more splits than the workspace's partial rows hold. 0: the skinny path does
+// not apply (the MFMA tiles run instead).
+int fp8_skinny_splits(const moe_dims& dm, const Layout& L) {
+  if (dm.T < 1 || dm.T > kSkinnyMaxT || L.ldh > kSkinnyMaxKC) return 0;
+  const int64_t Tk = dm.T * dm.k;
+  const int64_t groups = (Tk < dm.E ? Tk : dm.E) + (dm.I_shared > 0 ? 1 : 0);
+  const int64_t sstride = L.rows_total * 2 * (int64_t)L.ldh;
+  const int64_t room = (int64_t)(L.ffn_cnt - L.ffn_part) / (sstride * 4);
+  int64_t ks = 1024 / (groups * (L.ldh / 128));
+  if (ks > dm.d / 256) ks = dm.d / 256;
+  if (ks > room) ks = room;
+  const int64_t least = (dm.d + kSkinnyMaxKC - 1) / kSkinnyMaxKC;
+  if (ks < least) ks = least;
+  if (ks < 1) ks = 1;
+  if (ks > 1 && ks > room) return 0;
+  const int64_t kc = ((dm.d + ks - 1) / ks + 31) / 32 * 32;
+  return (int)((dm.d + kc - 1) / kc);
+}
+
+// one or two tokens: the skinny code streams; the down product runs unsplit
+hipError_t launch_fp8_skinny(const moe_dims& dm, const Layout& L, int ks, const void* x, const int32_t* offsets,
+                             const int32_t* sorted_token, const Fp8Weights& W, void* y, char* ws, hipStream_t s,
+                             const Prof* prof) {
+  const int has_shared = dm.I_shared > 0 ? 1 : 0;
+  const int64_t Tk = dm.T * dm.k;
+  const int64_t groups = (Tk < dm.E ? Tk : dm.E) + has_shared;  // tiles: one per group with rows
+  Fp8SkinnyArgs a{};
+  a.offsets = offsets;
+  a.sorted_token = sorted_token;
+  a.tile_group = (const int32_t*)(ws + L.tile_group);
+  a.tile_count = (const int32_t*)(ws + L.tile_count);
+  a.T = dm.T;
+  a.d = dm.d;
+  a.E = dm.E;
+  a.k = dm.k;
+  a.I = dm.I;
+  a.Is = dm.I_shared;
+  a.ldh = L.ldh;
+  bf16_t* H = (bf16_t*)(ws + L.H);
+  // gate/up
+  const int cb1 = L.ldh / 128;
+  const int64_t part_ld = 2 * (int64_t)L.ldh;
+  const int64_t sstride = L.rows_total * part_ld;
+  const int kc = (int)(((dm.d + ks - 1) / ks + 31) / 32 * 32);
+  a.a_src = (const bf16_t*)x;
+  a.w0 = W.wg;
+  a.w1 = W.wu;
+  a.s0 = W.sg;
+  a.s1 = W.su;
+  a.w0_s = W.wg_s;
+  a.w1_s = W.wu_s;
+  a.s0_s = W.sg_s;
+  a.s1_s = W.su_s;
+  a.out = H;
+  a.n_cblk = cb1;
+  a.ks = (int)ks;
+  a.kc = kc;
+  a.part = (float*)(ws + L.ffn_part);
+  a.part_ld = part_ld;
+  a.part_sstride = sstride;
+  hipError_t e;
+  if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
+  const dim3 grid1((unsigned)(groups * cb1 * ks));
+  if (dm.T <= 1) hipLaunchKernelGGL((ffn_fp8_skinny_kernel<true, 1>), grid1, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_fp8_skinny_kernel<true, 2>), grid1, dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ks > 1 && (e = launch_gate_up_finish(a.part, sstride, part_ld, (int)ks, Tk, L.rows_total, dm.I, dm.I_shared,
+                                           L.ldh, H, s)) != hipSuccess)
+    return e;
+  if ((e = prof->end(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
+  // down: K = the group's intermediate width <= ldh <= kSkinnyMaxKC, one split
+  a.a_src = H;
+  a.w0 = W.wd;
+  a.w1 = nullptr;
+  a.s0 = W.sd;
+  a.s1 = nullptr;
+  a.w0_s = W.wd_s;
+  a.w1_s = nullptr;
+  a.s0_s = W.sd_s;
+  a.s1_s = nullptr;
+  a.out = (bf16_t*)y;
+  a.n_cblk = dm.d / 128;
+  a.ks = 1;
+  a.kc = L.ldh;
+  a.part = nullptr;
+  if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
+  const dim3 grid2((unsigned)(groups * a.n_cblk));
+  if (dm.T <= 1) hipLaunchKernelGGL((ffn_fp8_skinny_kernel<false, 1>), grid2, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_fp8_skinny_kernel<false, 2>), grid2, dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return prof->end(MOE_KERNEL_FFN_DOWN, s);
+}
+
+}  // namespace
+
 const char* ffn_fp8_kernel_name(const moe_dims& dm, bool gate_up) {
+  if (fp8_skinny_splits(dm, make_layout(dm)) > 0) {
+    if (dm.T <= 1) return gate_up ? "ffn_fp8_skinny_kernel<true, 1>" : "ffn_fp8_skinny_kernel<false, 1>";
+    return gate_up ? "ffn_fp8_skinny_kernel<true, 2>" : "ffn_fp8_skinny_kernel<false, 2>";
+  }
   if (dm.T <= 32) return gate_up ? "ffn_fp8_stream_kernel<true, 4, 32>" : "ffn_fp8_stream_kernel<false, 4, 32>";
   return gate_up ? "ffn_fp8_stream_kernel<true, 5, 128>" : "ffn_fp8_stream_kernel<false, 5, 128>";
 }
@@ -399,6 +715,8 @@ hipError_t launch_grouped_ffn_fp8(const moe_dims& dm, const Layout& L, const voi
   // 128-row tiles, whatever the bf16 GEMMs would use for these dims
   hipError_t e = launch_build_tiles(dm, L, offsets, ws, s, SBM);
   if (e != hipSuccess) return e;
+  const int ks_skinny = fp8_skinny_splits(dm, L);
+  if (ks_skinny > 0) return launch_fp8_skinny(dm, L, ks_skinny, x, offsets, sorted_token, W, y, ws, s, prof);
   const int has_shared = dm.I_shared > 0 ? 1 : 0;
   const int64_t Tk = dm.T * dm.k;
   const int64_t max_mt = Tk / SBM + (Tk < dm.E ? Tk : dm.E) + (has_shared ? dm.T / SBM + 1 : 0);

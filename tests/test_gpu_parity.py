@@ -503,6 +503,10 @@ FP8_CASES = [
     syn.MoEConfig("fp8_T48", T=48, d=1024, E=32, k=4, I=256, Is=384, dtype=syn.BF16, seed=66),
     # row counts at which the bf16 GEMMs take 160-row (~150 per expert) and 192-row (~350) tiles:
     # the FP8 GEMMs keep their own 128-row tile list
+    # one or two tokens: the skinny code streams (gate/up split over K at d = 4096 and finished by
+    # the follow-up kernel; 384-wide experts beside a 640-wide shared one)
+    syn.MoEConfig("fp8_two_tokens", T=2, d=1024, E=96, k=6, I=384, Is=640, dtype=syn.BF16, seed=69),
+    syn.MoEConfig("fp8_one_token_split", T=1, d=4096, E=32, k=4, I=512, Is=512, dtype=syn.BF16, seed=70),
     syn.MoEConfig("fp8_tall_rows", T=300, d=512, E=8, k=4, I=256, Is=256, dtype=syn.BF16, seed=67),
     syn.MoEConfig("fp8_wide_rows", T=700, d=512, E=8, k=4, I=256, Is=256, dtype=syn.BF16, seed=68),
 ]

@@ -45,6 +45,8 @@ def test_few_token_and_fp8_kernels(lib):
     assert moe.moe_kernel_name(_dims(cfg, T=1), moe.KERNEL_FFN_GATE_UP) == "ffn_skinny_kernel<true, 1>"
     assert moe.moe_kernel_name(_dims(cfg, T=2), moe.KERNEL_FFN_DOWN) == "ffn_skinny_kernel<false, 2>"
     assert moe.moe_kernel_name(_dims(cfg), moe.KERNEL_FFN_GATE_UP, fp8=True) == "ffn_fp8_stream_kernel<true, 4, 32>"
+    assert moe.moe_kernel_name(_dims(cfg, T=1), moe.KERNEL_FFN_GATE_UP, fp8=True) == "ffn_fp8_skinny_kernel<true, 1>"
+    assert moe.moe_kernel_name(_dims(cfg, T=2), moe.KERNEL_FFN_DOWN, fp8=True) == "ffn_fp8_skinny_kernel<false, 2>"
     pre = syn.CONFIGS["prefill"]
     assert moe.moe_kernel_name(_dims(pre), moe.KERNEL_FFN_DOWN, fp8=True) == "ffn_fp8_stream_kernel<false, 5, 128>"
     assert moe.moe_kernel_name(_dims(pre), moe.KERNEL_ROUTER) == "router_mfma_kernel"
