@@ -970,12 +970,13 @@ FfnPlan ffn_plan(const moe_dims& dm) {
   // expert on average. Short K loops (and the near-empty row tiles of decode) run faster on
   // 128 x 256 tiles, two workgroups per CU, whose prologues and epilogues overlap.
   const double rows_per_expert = (double)Tk / dm.E;
-  // Tall 160-row tiles for both products when experts hold ~150 rows or more on average: ~320 rows
-  // are then two row tiles rather than three (prefill), and under skewed routing the many experts
-  // with a few dozen rows stream their weights once, non-temporally, while the heavy ones take
-  // fewer row tiles (skew layer 14.5 -> 13.7 ms). At ~128 rows per expert the 128 x 256 tiles stay
-  // faster (mid: down product 0.17 vs 0.18 ms).
-  P.tall = P.stream && rows_per_expert >= 150.0 && dm.I % 256 == 0 && dm.I_shared % 256 == 0 && dm.d % 512 == 0;
+  // Tall 160-row tiles for both products when experts hold ~100 rows or more on average: an
+  // expert's rows up to 160 stay in one row tile (its weight panels stream once), ~320 rows are two
+  // row tiles rather than three, and under skewed routing the many experts with a few dozen rows
+  // stream their weights once, non-temporally. Measured against the 128-row tiles: mid (128 rows
+  // per expert) 0.547 -> 0.504 ms, the large shape at T = 6144 (120 rows) 10.7 -> 9.9 ms, skew
+  // 14.5 -> 13.7 ms; equal at 64-80 rows; at 48 rows the 128-row tiles are ~2 % faster.
+  P.tall = P.stream && rows_per_expert >= 96.0 && dm.I % 256 == 0 && dm.I_shared % 256 == 0 && dm.d % 512 == 0;
   // 192-row tiles from ~256 rows per expert on average: experts of 321 .. 384 rows then take two
   // row tiles instead of three (prefill layer 20.2 -> 19.9 ms). Under skewed routing (~160 rows on
   // average, most experts a few dozen) they measured slower than the tall ones (13.5 -> 14.4 ms).

@@ -110,10 +110,12 @@ SMALL_CASES = [
     # GEMMs); a shared expert wider than the routed ones (three column blocks of 256 against two)
     ("skinny_many_experts_T1", 1, 1024, 128, 6, 512, 512, syn.BF16, 1, 0.0),
     ("skinny_many_experts_T2", 2, 2048, 96, 8, 512, 768, syn.BF16, 0, 0.0),
-    # 160-row tall tiles (150 .. 256 rows per expert on average): ~200-row experts as two row tiles
-    # of 3 and 4 sub-tiles and the 400 shared rows as three (4, 4, 5); Zipf-skewed loads from
-    # ~500 rows down to a few (one partial sub-tile)
+    # 160-row tall tiles (96 .. 256 rows per expert on average): ~200-row experts as two row tiles
+    # of 3 and 4 sub-tiles and the 400 shared rows as three (4, 4, 5); ~100-row experts in one row
+    # tile of four sub-tiles (the last one partial); Zipf-skewed loads from ~500 rows down to a few
+    # (one partial sub-tile)
     ("tall_tiles", 400, 512, 8, 4, 256, 256, syn.BF16, 1, 0.0),
+    ("tall_tiles_one_row_tile", 200, 512, 8, 4, 256, 256, syn.BF16, 0, 0.0),
     ("tall_tiles_skewed", 700, 512, 16, 4, 256, 0, syn.BF16, 0, 1.2),
     # 192-row wide tiles (>= 256 rows per expert on average): ~350-row experts as two row tiles of
     # 5 and 6 sub-tiles; a shared expert wider than the routed ones over three row tiles (5, 6, 6);

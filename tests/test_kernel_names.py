@@ -25,7 +25,7 @@ def lib():
 EXPECTED = {
     # workload: (gate/up, down)
     "tiny": ("ffn_f32_kernel<true>", "ffn_f32_kernel<false>"),
-    "mid": ("ffn_mfma_stream_kernel<true, 2, 3>", "ffn_mfma_stream_kernel<false, 2, 3>"),
+    "mid": ("ffn_mfma_tall_kernel<true, 3>", "ffn_mfma_tall_kernel<false, 3>"),
     "decode": ("ffn_mfma_stream_kernel<true, 4, 4>", "ffn_mfma_stream_kernel<false, 2, 3>"),
     "prefill": ("ffn_mfma_wide_kernel<true, 3>", "ffn_mfma_wide_kernel<false, 3>"),
     "skew": ("ffn_mfma_tall_kernel<true, 3>", "ffn_mfma_tall_kernel<false, 3>"),
