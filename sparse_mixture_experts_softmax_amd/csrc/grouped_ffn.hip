@@ -40,7 +40,7 @@ using stream::f32x16_t;
 // tile list: for each group with n rows, ceil(n / BM) tiles (group, first row)
 // ------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024)
-build_tiles_kernel(const int32_t* __restrict__ offsets, int64_t T, int E, int has_shared, int BM,
+build_tiles_kernel(const int32_t* __restrict__ offsets, int64_t T, int E, int has_shared, int BM, int BM2,
                    int32_t* __restrict__ tile_group, int32_t* __restrict__ tile_m0, int32_t* __restrict__ tile_count,
                    int32_t* __restrict__ split_cnt, int64_t n_cnt) {
   __shared__ int s_rows[kMaxGroups];
@@ -48,7 +48,7 @@ build_tiles_kernel(const int32_t* __restrict__ offsets, int64_t T, int E, int ha
   const int G = E + has_shared;
   for (int g = threadIdx.x; g < G; g += 1024) s_rows[g] = g < E ? offsets[g + 1] - offsets[g] : (int)T;
   __syncthreads();
-  build_tile_list(s_rows, G, BM, s_w, tile_group, tile_m0, tile_count, split_cnt, n_cnt);
+  build_tile_list(s_rows, G, BM, BM2, s_w, tile_group, tile_m0, tile_count, split_cnt, n_cnt);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -443,29 +443,30 @@ __global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) ffn_mfma_stream_ker
 }
 
 // ------------------------------------------------------------------------------------------
-// Tall-tile variant of the streaming kernel for groups of a few hundred rows (prefill-sized
-// batches): 160 x 512 tiles (stream_gemm.h, namespace tall), eight wavefronts each holding all
-// rows of the tile and 64 columns; for the gate/up product 32 gate and the matching 32 up columns.
-// A group's rows are split over ceil(rows / 160) row tiles in whole 32-row sub-tiles as evenly as
-// possible, so its row tiles do equal work and stream each weight panel in step. Tiles are ordered
-// (group, column tile, row tile) and remapped per XCD as in the 128-row kernel.
+// Tall tiles for groups of about a hundred rows and more: 160 x 512 (stream_gemm.h, namespace
+// tall: eight wavefronts each holding all rows of the tile and 64 columns; for the gate/up
+// product 32 gate and the matching 32 up columns) or 192 x 512 (namespace wide: a 2 x 4 grid of
+// wavefronts, each 96 rows x 128 columns), chosen per group by the tile list (kTileRows192 on the
+// group's entries): 192 rows where that takes fewer row tiles, at most two, 160 otherwise. A
+// group's rows are split over its row tiles in whole 32-row sub-tiles as evenly as possible, so
+// its row tiles do equal work and stream each weight panel in step. Tiles are ordered (group,
+// column tile, row tile) and remapped per XCD as in the 128-row kernel.
 // ------------------------------------------------------------------------------------------
+// Logical tile L of a 160-row group.
 template <bool GATED, int S>
-__global__ void __launch_bounds__(512, 1) ffn_mfma_tall_kernel(MfmaArgs p) {
+__device__ __forceinline__ void tile160(const MfmaArgs& p, int L, char* smem) {
   using namespace stream;
   constexpr int TM = tall::ROWS;
   constexpr int TN = GATED ? 256 : 512;  // output columns per tile
-  __shared__ __attribute__((aligned(1024))) char smem[S * tall::STAGE];
+  static_assert(S * tall::STAGE <= S * wide::STAGE, "the kernel's LDS holds either tile's stages");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const int L = xcd_remap(blockIdx.x, *p.tile_count * p.n_ntiles);
-  if (L < 0) return;
   const int probe = L / p.n_ntiles;
   const int g = p.tile_group[probe];
-  const int first = probe - p.tile_m0[probe] / TM;  // the group's first row tile
+  const int first = probe - (p.tile_m0[probe] & ~kTileRows192) / TM;  // the group's first row tile
   const Group G = group_info(g, p.offsets, p.T, p.k, p.E, p.I, p.Is);
   const int cnt = (G.rows + TM - 1) / TM;
   const int local = L - p.n_ntiles * first;
@@ -596,29 +597,22 @@ __global__ void __launch_bounds__(512, 1) ffn_mfma_tall_kernel(MfmaArgs p) {
   }
 }
 
-// ------------------------------------------------------------------------------------------
-// Wide-tile variant for groups of ~250 rows and more (prefill-sized batches): 192 x 512 tiles on
-// eight wavefronts (stream_gemm.h, namespace wide). Row split (whole 32-row sub-tiles, as evenly
-// as possible over ceil(rows / 192) row tiles), tile order, XCD remap, non-temporal weight streams
-// for single-row-tile groups and the staged epilogue as in the tall kernel.
-// ------------------------------------------------------------------------------------------
+// Logical tile L of a 192-row group: row split, weight streams and the staged epilogue as in
+// tile160.
 template <bool GATED, int S>
-__global__ void __launch_bounds__(512, 1) ffn_mfma_wide_kernel(MfmaArgs p) {
+__device__ __forceinline__ void tile192(const MfmaArgs& p, int L, char* smem) {
   using namespace stream;
   constexpr int TM = wide::ROWS;
   constexpr int TN = GATED ? 256 : 512;  // output columns per tile
-  __shared__ __attribute__((aligned(1024))) char smem[S * wide::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
 
-  const int L = xcd_remap(blockIdx.x, *p.tile_count * p.n_ntiles);
-  if (L < 0) return;
   const int probe = L / p.n_ntiles;
   const int g = p.tile_group[probe];
-  const int first = probe - p.tile_m0[probe] / TM;  // the group's first row tile
+  const int first = probe - (p.tile_m0[probe] & ~kTileRows192) / TM;  // the group's first row tile
   const Group G = group_info(g, p.offsets, p.T, p.k, p.E, p.I, p.Is);
   const int cnt = (G.rows + TM - 1) / TM;
   const int local = L - p.n_ntiles * first;
@@ -743,6 +737,15 @@ __global__ void __launch_bounds__(512, 1) ffn_mfma_wide_kernel(MfmaArgs p) {
       *(uint4*)(out + row * ld + h * HALF + ch * 8) = *(const uint4*)(st + row * PITCH + ch * 16);
     }
   }
+}
+
+template <bool GATED, int S>
+__global__ void __launch_bounds__(512, 1) ffn_mfma_tall_kernel(MfmaArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem[S * stream::wide::STAGE];
+  const int L = stream::xcd_remap(blockIdx.x, *p.tile_count * p.n_ntiles);
+  if (L < 0) return;
+  if (p.tile_m0[L / p.n_ntiles] & kTileRows192) tile192<GATED, S>(p, L, smem);
+  else tile160<GATED, S>(p, L, smem);
 }
 
 // H rows of a gate/up product with K split (streaming MFMA or skinny kernels): each split's fp32
@@ -931,7 +934,6 @@ const char* ffn_kernel_name(const moe_dims& dm, bool gate_up) {
     if (P.skinny_rows == 1) return gate_up ? "ffn_skinny_kernel<true, 1>" : "ffn_skinny_kernel<false, 1>";
     return gate_up ? "ffn_skinny_kernel<true, 2>" : "ffn_skinny_kernel<false, 2>";
   }
-  if (P.wide) return gate_up ? "ffn_mfma_wide_kernel<true, 3>" : "ffn_mfma_wide_kernel<false, 3>";
   if (P.tall) return gate_up ? "ffn_mfma_tall_kernel<true, 3>" : "ffn_mfma_tall_kernel<false, 3>";
   if (P.stream) {
     if ((gate_up ? P.wn1 : P.wn2) == 4)
@@ -943,14 +945,19 @@ const char* ffn_kernel_name(const moe_dims& dm, bool gate_up) {
 
 int ffn_tile_rows(const moe_dims& dm) {
   if (dm.dtype == MOE_F32) return kF32BM;
-  const FfnPlan P = ffn_plan(dm);
-  return P.wide ? stream::wide::ROWS : P.tall ? stream::tall::ROWS : kMfmaBM;
+  return ffn_plan(dm).tall ? stream::tall::ROWS : kMfmaBM;
+}
+
+int ffn_tile_rows_alt(const moe_dims& dm) {
+  if (dm.dtype == MOE_F32) return 0;
+  return ffn_plan(dm).tall ? stream::wide::ROWS : 0;
 }
 
 hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s,
                               int bm) {
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, dm.T, dm.E, dm.I_shared > 0 ? 1 : 0,
-                     bm > 0 ? bm : ffn_tile_rows(dm), (int32_t*)(ws + L.tile_group), (int32_t*)(ws + L.tile_m0),
+                     bm > 0 ? bm : ffn_tile_rows(dm), bm > 0 ? 0 : ffn_tile_rows_alt(dm),
+                     (int32_t*)(ws + L.tile_group), (int32_t*)(ws + L.tile_m0),
                      (int32_t*)(ws + L.tile_count), (int32_t*)(ws + L.ffn_cnt), 2 * L.ffn_cnt_each);
   return hipGetLastError();
 }
@@ -977,10 +984,12 @@ FfnPlan ffn_plan(const moe_dims& dm) {
   // per expert) 0.547 -> 0.504 ms, the large shape at T = 6144 (120 rows) 10.7 -> 9.9 ms, skew
   // 14.5 -> 13.7 ms; equal at 64-80 rows; at 48 rows the 128-row tiles are ~2 % faster.
   P.tall = P.stream && rows_per_expert >= 96.0 && dm.I % 256 == 0 && dm.I_shared % 256 == 0 && dm.d % 512 == 0;
-  // 192-row tiles from ~256 rows per expert on average: experts of 321 .. 384 rows then take two
-  // row tiles instead of three (prefill layer 20.2 -> 19.9 ms). Under skewed routing (~160 rows on
-  // average, most experts a few dozen) they measured slower than the tall ones (13.5 -> 14.4 ms).
-  P.wide = P.tall && rows_per_expert >= 256.0;
+  // With the tall tiles each group takes 160- or 192-row tiles, chosen per group when the tile
+  // list is built (build_tile_list): 192 rows where they need fewer row tiles and at most two
+  // (161-192 and 321-384 rows), 160 otherwise. Against one height per launch chosen from the
+  // average rows per expert (192 from 256): prefill 19.9-20.0 -> 19.4 ms, 160 rows per expert
+  // under uniform routing 12.3 -> 11.1 ms, mid 0.52 -> 0.51 ms, skew unchanged (192-row tiles on
+  // its two 8192-row experts, 43 instead of 52 row tiles, measured 2 % slower).
   P.wn1 = P.stream && dm.I % 256 == 0 && dm.I_shared % 256 == 0 && dm.d >= 4096 ? 4 : 2;
   P.wn2 = P.stream && dm.d % 512 == 0 && dm.I >= 2048 && rows_per_expert >= 64.0 ? 4 : 2;
   const int tn1 = P.tall ? 256 : P.stream ? 64 * P.wn1 : kMfmaBN1;
@@ -1085,9 +1094,7 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.part_ld = P.part_cols1;
     a.part_sstride = L.rows_total * P.part_cols1;
     if ((e = prof->begin(MOE_KERNEL_FFN_GATE_UP, s)) != hipSuccess) return e;
-    if (P.wide)
-      hipLaunchKernelGGL((ffn_mfma_wide_kernel<true, 3>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(512), 0, s, a);
-    else if (P.tall)
+    if (P.tall)
       hipLaunchKernelGGL((ffn_mfma_tall_kernel<true, 3>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(512), 0, s, a);
     else if (stream_ok)
       launch_stream<true>(P.wn1, (unsigned)(max_mt * a.n_ntiles * a.splits), s, a);
@@ -1112,9 +1119,7 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
     a.part_ld = 0;
     a.part_sstride = 0;
     if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
-    if (P.wide)
-      hipLaunchKernelGGL((ffn_mfma_wide_kernel<false, 3>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(512), 0, s, a);
-    else if (P.tall)
+    if (P.tall)
       hipLaunchKernelGGL((ffn_mfma_tall_kernel<false, 3>), dim3((unsigned)(max_mt * a.n_ntiles)), dim3(512), 0, s, a);
     else if (stream_ok)
       launch_stream<false>(P.wn2, (unsigned)(max_mt * a.n_ntiles * a.splits), s, a);

@@ -77,8 +77,7 @@ Layout make_layout(const moe_dims& dm);
 struct FfnPlan {
   bool stream;
   bool balance;  // equal row tiles per group
-  bool tall;     // 160-row tiles for both products (groups of a few hundred rows)
-  bool wide;     // 192-row tiles instead of the 160-row ones (groups of ~250 rows and more)
+  bool tall;     // 160- or 192-row tiles for both products, per group (groups of ~100 rows and more)
   int wn1, wn2;
   int nt1, nt2;
   int s1;  // K splits of the MFMA gate/up product (the MFMA down product is never split)
@@ -156,29 +155,45 @@ __device__ inline int block_exclusive_scan_1024t(int x, int* s_w, int* total) {
   return before + incl - x;
 }
 
+// Flag on a tile list entry's first row: the group runs 192-row tiles (its first row is then the
+// tile index times 192); without it, tiles of the list's BM rows
+constexpr int32_t kTileRows192 = 1 << 30;
+
 // Row-tile list of the grouped GEMMs: group g with s_rows[g] rows gets ceil(rows / BM) tiles,
-// listed group after group as (group, first row). One workgroup of 1024 threads; s_rows and s_w
-// (17 ints) are LDS arrays (G <= 2048 groups). Also zeroes the split-K arrival counters.
-__device__ inline void build_tile_list(const int* s_rows, int G, int BM, int* s_w, int32_t* tile_group,
+// listed group after group as (group, first row). BM2 > 0 (192, the tall tiles): a group whose
+// rows fit fewer tiles of BM2 rows than of BM, and at most two, takes those, its entries flagged
+// kTileRows192 (larger groups measured faster on the 160-row tiles, more of them or not). One
+// workgroup of 1024 threads; s_rows and s_w (17 ints) are LDS arrays (G <= 2048 groups). Also
+// zeroes the split-K arrival counters.
+__device__ inline void build_tile_list(const int* s_rows, int G, int BM, int BM2, int* s_w, int32_t* tile_group,
                                        int32_t* tile_m0, int32_t* tile_count, int32_t* split_cnt, int64_t n_cnt) {
   const int tid = threadIdx.x;
   for (int64_t i = tid; i < n_cnt; i += 1024) split_cnt[i] = 0;
-  // tile counts of groups 2 tid and 2 tid + 1, and their exclusive prefix
-  const int a = 2 * tid < G ? (s_rows[2 * tid] + BM - 1) / BM : 0;
-  const int b = 2 * tid + 1 < G ? (s_rows[2 * tid + 1] + BM - 1) / BM : 0;
-  const int excl = block_exclusive_scan_1024t(a + b, s_w, &s_w[16]);
-  const int starts[2] = {excl, excl + a};
-  const int cnts[2] = {a, b};
+  // tile heights and counts of groups 2 tid and 2 tid + 1, and their exclusive prefix
+  int bm[2], cnts[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int g = 2 * tid + h;
+    const int rows = g < G ? s_rows[g] : 0;
+    const int c1 = (rows + BM - 1) / BM;
+    const int c2 = BM2 > 0 ? (rows + BM2 - 1) / BM2 : c1;
+    const bool alt = c2 < c1 && c2 <= 2;
+    bm[h] = alt ? BM2 : BM;
+    cnts[h] = alt ? c2 : c1;
+  }
+  const int excl = block_exclusive_scan_1024t(cnts[0] + cnts[1], s_w, &s_w[16]);
+  const int starts[2] = {excl, excl + cnts[0]};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int g = 2 * tid + h;
+    const int32_t flag = bm[h] == BM2 && BM2 != BM ? kTileRows192 : 0;
     if (g < G)
       for (int i = 0; i < cnts[h]; ++i) {
         tile_group[starts[h] + i] = g;
-        tile_m0[starts[h] + i] = i * BM;
+        tile_m0[starts[h] + i] = (i * bm[h]) | flag;
       }
   }
-  if (tid == 1023) *tile_count = excl + a + b;
+  if (tid == 1023) *tile_count = excl + cnts[0] + cnts[1];
 }
 
 // ------------------------------------------------------------------------------------------
@@ -221,6 +236,8 @@ const char* ffn_fp8_kernel_name(const moe_dims& dm, bool gate_up);
 
 // row-tile list of the grouped GEMMs (rows per tile ffn_tile_rows) and zeroed split-K counters
 int ffn_tile_rows(const moe_dims& dm);
+// the second tile height a group may take instead (192 with the tall tiles), else 0
+int ffn_tile_rows_alt(const moe_dims& dm);
 // bm: rows per tile of the list (0: ffn_tile_rows(dm), the bf16 grouped GEMMs' choice)
 hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t* offsets, char* ws, hipStream_t s,
                               int bm = 0);

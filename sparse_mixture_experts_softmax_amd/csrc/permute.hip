@@ -35,6 +35,7 @@ struct TileListArgs {
   int64_t T;
   int has_shared;
   int BM;
+  int BM2;  // second tile height a group may take (0: none)
 };
 
 __global__ void __launch_bounds__(kPermuteChunk)
@@ -133,7 +134,7 @@ permute_scan_kernel(int32_t* __restrict__ chunk_counts, int64_t nchunks, int E, 
     // the grouped GEMM's tile list from the same group sizes (the shared expert last)
     if (tid == 0 && tl.has_shared) s_rows[E] = (int)tl.T;
     __syncthreads();
-    build_tile_list(s_rows, E + tl.has_shared, tl.BM, s_w, tl.tile_group, tl.tile_m0, tl.tile_count, tl.split_cnt,
+    build_tile_list(s_rows, E + tl.has_shared, tl.BM, tl.BM2, s_w, tl.tile_group, tl.tile_m0, tl.tile_count, tl.split_cnt,
                     tl.n_cnt);
   }
 }
@@ -208,7 +209,7 @@ permute_one_chunk_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E,
   if (tl.tile_group) {
     if (tid == 0 && tl.has_shared) s_rows[E] = (int)tl.T;
     __syncthreads();
-    build_tile_list(s_rows, E + tl.has_shared, tl.BM, s_w, tl.tile_group, tl.tile_m0, tl.tile_count, tl.split_cnt,
+    build_tile_list(s_rows, E + tl.has_shared, tl.BM, tl.BM2, s_w, tl.tile_group, tl.tile_m0, tl.tile_count, tl.split_cnt,
                     tl.n_cnt);
   }
 }
@@ -227,6 +228,7 @@ hipError_t launch_permute(const moe_dims& dm, const Layout& L, const int32_t* to
     tl.T = dm.T;
     tl.has_shared = dm.I_shared > 0 ? 1 : 0;
     tl.BM = ffn_tile_rows(dm);
+    tl.BM2 = ffn_tile_rows_alt(dm);
   }
   int32_t* cc = (int32_t*)(ws + L.chunk_counts);
   const size_t lds = sizeof(unsigned long long) * kWaves * (size_t)dm.E;

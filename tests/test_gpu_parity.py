@@ -117,16 +117,16 @@ SMALL_CASES = [
     ("tall_tiles", 400, 512, 8, 4, 256, 256, syn.BF16, 1, 0.0),
     ("tall_tiles_one_row_tile", 200, 512, 8, 4, 256, 256, syn.BF16, 0, 0.0),
     ("tall_tiles_skewed", 700, 512, 16, 4, 256, 0, syn.BF16, 0, 1.2),
-    # 192-row wide tiles (>= 256 rows per expert on average): ~350-row experts as two row tiles of
-    # 5 and 6 sub-tiles; a shared expert wider than the routed ones over three row tiles (5, 6, 6);
-    # Zipf-skewed loads from every token down to a few rows; k = E, so that every group holds T
-    # rows: 576 as three full tiles, 257 as two (4 and 5 sub-tiles, one row in the last), 384 as two
-    # full tiles
+    # 192-row tiles, taken per group where they need fewer row tiles than 160-row ones (here
+    # ~350-row experts as two 192-row tiles, larger ones as three 160-row tiles, both in one
+    # launch); a shared expert wider than the routed ones; Zipf-skewed loads from every token down
+    # to a few rows; k = E, so that every group holds T rows: 576 as three full 192-row tiles, 161
+    # as one (six sub-tiles, one row in the last), 384 as two full ones
     ("wide_tiles", 700, 512, 8, 4, 256, 256, syn.BF16, 1, 0.0),
     ("wide_tiles_wide_shared", 513, 1024, 4, 2, 256, 512, syn.BF16, 1, 0.0),
     ("wide_tiles_skewed", 2000, 512, 16, 4, 256, 0, syn.BF16, 0, 1.2),
     ("wide_tiles_576", 576, 512, 4, 4, 256, 256, syn.BF16, 1, 0.0),
-    ("wide_tiles_257", 257, 512, 4, 4, 256, 512, syn.BF16, 1, 0.0),
+    ("wide_tiles_161", 161, 512, 4, 4, 256, 512, syn.BF16, 1, 0.0),
     ("wide_tiles_384", 384, 1024, 4, 4, 512, 256, syn.BF16, 0, 0.0),
 ]
 

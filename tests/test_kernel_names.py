@@ -27,7 +27,7 @@ EXPECTED = {
     "tiny": ("ffn_f32_kernel<true>", "ffn_f32_kernel<false>"),
     "mid": ("ffn_mfma_tall_kernel<true, 3>", "ffn_mfma_tall_kernel<false, 3>"),
     "decode": ("ffn_mfma_stream_kernel<true, 4, 4>", "ffn_mfma_stream_kernel<false, 2, 3>"),
-    "prefill": ("ffn_mfma_wide_kernel<true, 3>", "ffn_mfma_wide_kernel<false, 3>"),
+    "prefill": ("ffn_mfma_tall_kernel<true, 3>", "ffn_mfma_tall_kernel<false, 3>"),
     "skew": ("ffn_mfma_tall_kernel<true, 3>", "ffn_mfma_tall_kernel<false, 3>"),
 }
 
