@@ -480,14 +480,14 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[SUB][2]) {
 }  // namespace tall
 
 // ------------------------------------------------------------------------------------------------
-// Wide tiles for groups of ~250 rows and more: 192 x 512 on eight wavefronts in two wave rows of
-// four. Wave (wm, wn) holds the 32-row sub-tiles wm, wm + 2, wm + 4 (a partly filled tile keeps
-// its live rows spread over both wave rows, so over every SIMD) and columns 128 wn .. +128
-// (gate/up: gate columns 64 wn .. +64 and the up columns with the same indices), 192 accumulators
-// per lane, two wavefronts per SIMD. Against the 160-row tiles: an expert of 321 .. 384 rows takes
-// two row tiles instead of three, so its weight panels cross from L2 into LDS twice, and per FLOP
-// the CU moves 7.0 instead of 8.0 KB per MFLOP from L2 into LDS -- the prefill GEMMs run
-// power-limited, with the clock set mostly by that traffic.
+// 192-row tiles, for the groups that need fewer row tiles of 192 than of 160 rows, at most two
+// (161 .. 192 and 321 .. 384 rows): 192 x 512 on eight wavefronts in two wave rows of four. Wave
+// (wm, wn) holds the 32-row sub-tiles wm, wm + 2, wm + 4 (a partly filled tile keeps its live rows
+// spread over both wave rows, so over every SIMD) and columns 128 wn .. +128 (gate/up: gate
+// columns 64 wn .. +64 and the up columns with the same indices), 192 accumulators per lane, two
+// wavefronts per SIMD. Against 160-row tiles such a group's weight panels cross from L2 into LDS
+// once fewer, and per FLOP the CU moves 7.0 instead of 8.0 KB per MFLOP from L2 into LDS -- the
+// prefill GEMMs run power-limited, with the clock set mostly by that traffic.
 //   LDS per stage: A [192 rows][32 K] (12 instructions of 16 rows; wave w issues w and w + 8 when
 //   < 12) in the swizzle of the 128-row tiles, then the B tile of four 128-column blocks (wave w
 //   fills rows 16 (w % 2) .. +16 of block w / 2).
