@@ -547,6 +547,9 @@ GRAPH_CASES = [
     ("bf16_skinny", syn.MoEConfig("graph_skinny", T=1, d=2048, E=32, k=6, I=512, Is=512, dtype=syn.BF16, seed=75)),
     ("bf16_skinny_many_experts", syn.MoEConfig("graph_skinny_e96", T=2, d=2048, E=96, k=6, I=512, Is=512,
                                                dtype=syn.BF16, seed=76)),
+    # ~350 rows per expert: the tall kernel with 160- and 192-row tiles in one launch
+    ("bf16_tall_tiles", syn.MoEConfig("graph_tall", T=700, d=512, E=8, k=4, I=256, Is=256, dtype=syn.BF16,
+                                      seed=77)),
     ("bf16_mid_width", syn.MoEConfig("graph_mid", T=300, d=2048, E=64, k=8, I=512, Is=512, dtype=syn.BF16, seed=72)),
     ("fp8", syn.MoEConfig("graph_fp8", T=40, d=1024, E=32, k=4, I=256, Is=256, dtype=syn.BF16, seed=73)),
     ("block", syn.MoEConfig("graph_block", T=200, d=512, E=24, k=4, I=256, Is=128, dtype=syn.BF16, seed=74)),
