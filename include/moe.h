@@ -253,8 +253,9 @@ moe_status moe_forward_noalloc(const moe_dims* dims, const void* x, const float*
  * Returns MOE_ERR_INVALID_ARG for an unknown kernel id or a NULL event. */
 typedef enum {
   MOE_KERNEL_NONE = 0,
-  MOE_KERNEL_ROUTER = 1,       /* router logits GEMM (+ top-k kernel) */
-  MOE_KERNEL_PERMUTE = 2,      /* the three dispatch kernels */
+  MOE_KERNEL_ROUTER = 1,       /* router logits GEMM (+ top-k kernel, except as below) */
+  MOE_KERNEL_PERMUTE = 2,      /* the dispatch kernels; for 1 <= T <= 4 with E > 64 and the
+                                  vector router, one kernel doing top-k and dispatch */
   MOE_KERNEL_FFN_GATE_UP = 3,  /* grouped gate/up GEMM with fused silu*mul */
   MOE_KERNEL_FFN_DOWN = 4,     /* grouped down GEMM */
   MOE_KERNEL_COMBINE = 5       /* weighted combine + shared add */

@@ -42,13 +42,13 @@ using stream::f32x16_t;
 __global__ void __launch_bounds__(1024)
 build_tiles_kernel(const int32_t* __restrict__ offsets, int64_t T, int E, int has_shared, int BM, int BM2,
                    int32_t* __restrict__ tile_group, int32_t* __restrict__ tile_m0, int32_t* __restrict__ tile_count,
-                   int32_t* __restrict__ split_cnt, int64_t n_cnt) {
+                   int32_t* __restrict__ split_cnt, int64_t cnt_each, int per_tile) {
   __shared__ int s_rows[kMaxGroups];
   __shared__ int s_w[17];
   const int G = E + has_shared;
   for (int g = threadIdx.x; g < G; g += 1024) s_rows[g] = g < E ? offsets[g + 1] - offsets[g] : (int)T;
   __syncthreads();
-  build_tile_list(s_rows, G, BM, BM2, s_w, tile_group, tile_m0, tile_count, split_cnt, n_cnt);
+  build_tile_list(s_rows, G, BM, BM2, s_w, tile_group, tile_m0, tile_count, split_cnt, cnt_each, per_tile);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -958,7 +958,8 @@ hipError_t launch_build_tiles(const moe_dims& dm, const Layout& L, const int32_t
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, dm.T, dm.E, dm.I_shared > 0 ? 1 : 0,
                      bm > 0 ? bm : ffn_tile_rows(dm), bm > 0 ? 0 : ffn_tile_rows_alt(dm),
                      (int32_t*)(ws + L.tile_group), (int32_t*)(ws + L.tile_m0),
-                     (int32_t*)(ws + L.tile_count), (int32_t*)(ws + L.ffn_cnt), 2 * L.ffn_cnt_each);
+                     (int32_t*)(ws + L.tile_count), (int32_t*)(ws + L.ffn_cnt), L.ffn_cnt_each,
+                     L.ffn_cnt_per_tile);
   return hipGetLastError();
 }
 

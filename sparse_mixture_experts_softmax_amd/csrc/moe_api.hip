@@ -125,6 +125,9 @@ Layout make_layout(const moe_dims& dm) {
   L.router_splits = (int)splits;
   L.router_kchunk = (int)kchunk;
   L.nchunks = (T + kPermuteChunk - 1) / kPermuteChunk;
+  // a handful of tokens: the top-k picks go straight from LDS into the dispatch (one launch and
+  // one dependent global round trip fewer, on a path that is latency-bound)
+  L.route_fused = !L.router_mfma && T >= 1 && T <= 4 && dm.E > 64;
   const int smallest_bm = kF32BM;
   L.max_tiles = Tk / smallest_bm + dm.E + T / smallest_bm + 2;
   L.ldh = dm.I > dm.I_shared ? dm.I : dm.I_shared;
@@ -164,6 +167,7 @@ Layout make_layout(const moe_dims& dm) {
   // (group, column block)
   const int64_t per_tile = P.skinny ? std::max(P.cb1, P.cb2) : 0;
   L.ffn_cnt_each = L.max_tiles * per_tile;
+  L.ffn_cnt_per_tile = (int)per_tile;
   L.ffn_cnt = take((size_t)2 * L.ffn_cnt_each * 4);
   L.hnorm = take((size_t)T * dm.d * esz);
   L.total = off;
@@ -198,6 +202,7 @@ const char* moe_kernel_name(const moe_dims* dims, int32_t kernel, int32_t fp8) {
     case MOE_KERNEL_ROUTER:
       return L.router_mfma ? "router_mfma_kernel" : dm.T <= 64 ? "router_small_kernel" : "router_logits_kernel";
     case MOE_KERNEL_PERMUTE:
+      if (L.route_fused) return "route_dispatch_kernel";
       return L.nchunks == 1 ? "permute_one_chunk_kernel" : "permute_count_kernel";
     case MOE_KERNEL_FFN_GATE_UP:
       return fp8 ? ffn_fp8_kernel_name(dm, true) : ffn_kernel_name(dm, true);
@@ -382,11 +387,17 @@ moe_status forward_rows(const moe_dims& dm, const Layout& L, const void* xin, co
   g_prof = Prof();
   hipError_t e;
   if ((e = prof.begin(MOE_KERNEL_ROUTER, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
-  e = launch_router(dm, L, xin, w_router, router_bias, idx, tw, topk_gap, w, stream);
+  if (L.route_fused)
+    e = launch_router_logits(dm, L, xin, w_router, w, stream);
+  else
+    e = launch_router(dm, L, xin, w_router, router_bias, idx, tw, topk_gap, w, stream);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/router");
   if ((e = prof.end(MOE_KERNEL_ROUTER, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
   if ((e = prof.begin(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
-  e = launch_permute(dm, L, idx, offsets, sorted, slot, w, stream, !fp8);
+  if (L.route_fused)
+    e = launch_topk_dispatch(dm, L, router_bias, idx, tw, topk_gap, offsets, sorted, slot, w, stream, !fp8);
+  else
+    e = launch_permute(dm, L, idx, offsets, sorted, slot, w, stream, !fp8);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/permute");
   if ((e = prof.end(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
   if (fp8)

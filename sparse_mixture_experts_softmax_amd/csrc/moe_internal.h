@@ -57,6 +57,7 @@ struct Layout {
   int router_splits;    // K splits of the router logits GEMM (partial sums summed by top-k)
   int router_kchunk;    // vector path: hidden rows per split; MFMA path: 32-wide K steps per split
   int64_t nchunks;      // permute chunks
+  int route_fused;      // few tokens (T <= 4, E > 64, vector router): top-k and dispatch in one kernel
   int64_t max_tiles;    // upper bound on grouped-GEMM row tiles (any BM >= 64)
   int ldh;              // row stride of H = max(I, I_shared)
   int64_t rows_total;   // T*k + (I_shared ? T : 0)
@@ -67,6 +68,7 @@ struct Layout {
   size_t ffn_cnt;       // arrival counters of the skinny down product's K split
   size_t hnorm;         // moe_forward_block: the normalised rows [T, d] the router and experts read
   int64_t ffn_cnt_each; // counters per product
+  int ffn_cnt_per_tile; // counters per row tile (the widest group's column blocks)
   size_t total;
 };
 
@@ -164,11 +166,12 @@ constexpr int32_t kTileRows192 = 1 << 30;
 // rows fit fewer tiles of BM2 rows than of BM, and at most two, takes those, its entries flagged
 // kTileRows192 (larger groups measured faster on the 160-row tiles, more of them or not). One
 // workgroup of 1024 threads; s_rows and s_w (17 ints) are LDS arrays (G <= 2048 groups). Also
-// zeroes the split-K arrival counters.
+// zeroes the split-K arrival counters of the listed tiles: per_tile for each tile, in two banks
+// cnt_each apart.
 __device__ inline void build_tile_list(const int* s_rows, int G, int BM, int BM2, int* s_w, int32_t* tile_group,
-                                       int32_t* tile_m0, int32_t* tile_count, int32_t* split_cnt, int64_t n_cnt) {
+                                       int32_t* tile_m0, int32_t* tile_count, int32_t* split_cnt, int64_t cnt_each,
+                                       int per_tile) {
   const int tid = threadIdx.x;
-  for (int64_t i = tid; i < n_cnt; i += 1024) split_cnt[i] = 0;
   // tile heights and counts of groups 2 tid and 2 tid + 1, and their exclusive prefix
   int bm[2], cnts[2];
 #pragma unroll
@@ -194,11 +197,41 @@ __device__ inline void build_tile_list(const int* s_rows, int G, int BM, int BM2
       }
   }
   if (tid == 1023) *tile_count = excl + cnts[0] + cnts[1];
+  const int64_t n = (int64_t)s_w[16] * per_tile;  // the scan's total: tiles listed
+  for (int64_t i = tid; i < n; i += 1024) {
+    split_cnt[i] = 0;
+    split_cnt[cnt_each + i] = 0;
+  }
 }
 
 // ------------------------------------------------------------------------------------------
 // launchers (enqueue only; return hipSuccess or the launch error)
 // ------------------------------------------------------------------------------------------
+// where the dispatch also writes the grouped GEMM's tile list (tile_group null: it does not)
+struct TileListArgs {
+  int32_t* tile_group;
+  int32_t* tile_m0;
+  int32_t* tile_count;
+  int32_t* split_cnt;
+  int64_t cnt_each;
+  int per_tile;
+  int64_t T;
+  int has_shared;
+  int BM;
+  int BM2;  // second tile height a group may take (0: none)
+};
+TileListArgs tile_list_args(const moe_dims& dm, const Layout& L, char* ws, bool with_tiles);
+
+// router logits only: the per-split partial sums in the workspace (top-k adds them)
+hipError_t launch_router_logits(const moe_dims& dm, const Layout& L, const void* x, const float* w_router, char* ws,
+                                hipStream_t s);
+
+// L.route_fused: top-k and dispatch (and with_tiles, the tile list) in one launch, on the partial
+// logits launch_router_logits left in the workspace
+hipError_t launch_topk_dispatch(const moe_dims& dm, const Layout& L, const float* bias, int32_t* topk_idx,
+                                float* topk_w, float* topk_gap, int32_t* offsets, int32_t* sorted_token,
+                                int32_t* slot_of, char* ws, hipStream_t s, bool with_tiles);
+
 // probs: when non-null, every expert's softmax probability [T, E] (for the router statistics)
 hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, const float* w_router,
                          const float* bias, int32_t* topk_idx, float* topk_w, float* topk_gap, char* ws,

@@ -25,19 +25,6 @@ namespace {
 
 constexpr int kWaves = kPermuteChunk / 64;
 
-// where the scan also writes the grouped GEMM's tile list (tile_group null: it does not)
-struct TileListArgs {
-  int32_t* tile_group;
-  int32_t* tile_m0;
-  int32_t* tile_count;
-  int32_t* split_cnt;
-  int64_t n_cnt;
-  int64_t T;
-  int has_shared;
-  int BM;
-  int BM2;  // second tile height a group may take (0: none)
-};
-
 __global__ void __launch_bounds__(kPermuteChunk)
 permute_count_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E, int k, int32_t* __restrict__ rank,
                      int32_t* __restrict__ chunk_counts) {
@@ -135,7 +122,7 @@ permute_scan_kernel(int32_t* __restrict__ chunk_counts, int64_t nchunks, int E, 
     if (tid == 0 && tl.has_shared) s_rows[E] = (int)tl.T;
     __syncthreads();
     build_tile_list(s_rows, E + tl.has_shared, tl.BM, tl.BM2, s_w, tl.tile_group, tl.tile_m0, tl.tile_count, tl.split_cnt,
-                    tl.n_cnt);
+                    tl.cnt_each, tl.per_tile);
   }
 }
 
@@ -210,26 +197,32 @@ permute_one_chunk_kernel(const int32_t* __restrict__ topk_idx, int64_t T, int E,
     if (tid == 0 && tl.has_shared) s_rows[E] = (int)tl.T;
     __syncthreads();
     build_tile_list(s_rows, E + tl.has_shared, tl.BM, tl.BM2, s_w, tl.tile_group, tl.tile_m0, tl.tile_count, tl.split_cnt,
-                    tl.n_cnt);
+                    tl.cnt_each, tl.per_tile);
   }
 }
 
 }  // namespace
 
-hipError_t launch_permute(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, int32_t* offsets,
-                          int32_t* sorted_token, int32_t* slot_of, char* ws, hipStream_t s, bool with_tiles) {
+TileListArgs tile_list_args(const moe_dims& dm, const Layout& L, char* ws, bool with_tiles) {
   TileListArgs tl{};
   if (with_tiles) {
     tl.tile_group = (int32_t*)(ws + L.tile_group);
     tl.tile_m0 = (int32_t*)(ws + L.tile_m0);
     tl.tile_count = (int32_t*)(ws + L.tile_count);
     tl.split_cnt = (int32_t*)(ws + L.ffn_cnt);
-    tl.n_cnt = 2 * L.ffn_cnt_each;
+    tl.cnt_each = L.ffn_cnt_each;
+    tl.per_tile = L.ffn_cnt_per_tile;
     tl.T = dm.T;
     tl.has_shared = dm.I_shared > 0 ? 1 : 0;
     tl.BM = ffn_tile_rows(dm);
     tl.BM2 = ffn_tile_rows_alt(dm);
   }
+  return tl;
+}
+
+hipError_t launch_permute(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, int32_t* offsets,
+                          int32_t* sorted_token, int32_t* slot_of, char* ws, hipStream_t s, bool with_tiles) {
+  const TileListArgs tl = tile_list_args(dm, L, ws, with_tiles);
   int32_t* cc = (int32_t*)(ws + L.chunk_counts);
   const size_t lds = sizeof(unsigned long long) * kWaves * (size_t)dm.E;
   if (L.nchunks == 1) {

@@ -249,7 +249,8 @@ router_small_kernel(const XT* __restrict__ x, const float* __restrict__ wr, floa
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = 0.f;
 
-  constexpr int NX = TT * kSmallRows / 4 / 256;  // 4-value x chunks per thread and pass
+  constexpr int NXC = TT * kSmallRows / 4;  // 4-value x chunks per pass
+  constexpr int NX = (NXC + 255) / 256;      // per thread
   for (int k0 = kbeg; k0 < kend; k0 += kSmallRows) {
     const int kn = min(kSmallRows, kend - k0);  // a multiple of 8
     // the pass's x values and weights are all requested before any is used: one memory round trip
@@ -260,7 +261,7 @@ router_small_kernel(const XT* __restrict__ x, const float* __restrict__ wr, floa
       const int t = i / (kSmallRows / 4);
       const int r4 = (i % (kSmallRows / 4)) * 4;
       xv[u][0] = xv[u][1] = xv[u][2] = xv[u][3] = 0.f;
-      if (t < T && r4 < kn) load_x4<XT>(x + (int64_t)t * d + k0 + r4, xv[u]);
+      if (i < NXC && t < T && r4 < kn) load_x4<XT>(x + (int64_t)t * d + k0 + r4, xv[u]);
     }
     float w[64];
 #pragma unroll
@@ -276,7 +277,7 @@ router_small_kernel(const XT* __restrict__ x, const float* __restrict__ wr, floa
       const int i = tid + 256 * u;
       const int t = i / (kSmallRows / 4);
       const int r4 = (i % (kSmallRows / 4)) * 4;
-      *(float4*)&xs[t * kSmallRows + r4] = make_float4(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
+      if (i < NXC) *(float4*)&xs[t * kSmallRows + r4] = make_float4(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
     }
     __syncthreads();
 #pragma unroll
@@ -311,36 +312,44 @@ template <typename XT>
 void launch_router_small(const XT* x, const float* wr, float* part, int64_t T, int d, int E, int splits, int kchunk,
                          hipStream_t s) {
   const dim3 grid((unsigned)((E + 63) / 64), (unsigned)splits);
-  if (T <= 8) hipLaunchKernelGGL((router_small_kernel<XT, 8>), grid, dim3(256), 0, s, x, wr, part, T, d, E, kchunk);
+  if (T <= 1) hipLaunchKernelGGL((router_small_kernel<XT, 1>), grid, dim3(256), 0, s, x, wr, part, T, d, E, kchunk);
+  else if (T <= 2) hipLaunchKernelGGL((router_small_kernel<XT, 2>), grid, dim3(256), 0, s, x, wr, part, T, d, E, kchunk);
+  else if (T <= 8) hipLaunchKernelGGL((router_small_kernel<XT, 8>), grid, dim3(256), 0, s, x, wr, part, T, d, E, kchunk);
   else if (T <= 16) hipLaunchKernelGGL((router_small_kernel<XT, 16>), grid, dim3(256), 0, s, x, wr, part, T, d, E, kchunk);
   else if (T <= 32) hipLaunchKernelGGL((router_small_kernel<XT, 32>), grid, dim3(256), 0, s, x, wr, part, T, d, E, kchunk);
   else hipLaunchKernelGGL((router_small_kernel<XT, 64>), grid, dim3(256), 0, s, x, wr, part, T, d, E, kchunk);
 }
 
-// Maximum over the 64 lanes of a wavefront, uniform result. Within each row of 16 lanes the
-// maximum spreads by DPP lane moves (swap neighbours, swap pairs, rotate by 4, rotate by 8);
-// the four row maxima are then read as scalars.
-__device__ __forceinline__ float dpp_max(float x, int ctrl) {
-  // ctrl is one of the four row-local moves below; every lane's source lane exists
-  int y = 0;
-  switch (ctrl) {
-    case 0xB1: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false); break;  // quad [1,0,3,2]
-    case 0x4E: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false); break;  // quad [2,3,0,1]
-    case 0x124: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false); break; // row_ror:4
-    default: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false); break;    // row_ror:8
-  }
-  return fmaxf(x, __int_as_float(y));
+// Row-local DPP lane moves (every lane's source lane exists): 0xB1 quad [1,0,3,2], 0x4E quad
+// [2,3,0,1], 0x124 row_ror:4, 0x128 row_ror:8. After the four, with a commutative combine, each
+// lane of a row of 16 holds the combination of the whole row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+__device__ __forceinline__ float row_lane(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Maximum over the 64 lanes of a wavefront, uniform result: the maximum spreads within each row
+// of 16 lanes by the four moves, then the four row maxima are read as scalars.
 __device__ __forceinline__ float wave_max(float x) {
-  x = dpp_max(x, 0xB1);
-  x = dpp_max(x, 0x4E);
-  x = dpp_max(x, 0x124);
-  x = dpp_max(x, 0x128);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  x = fmaxf(x, dpp_move<0xB1>(x));
+  x = fmaxf(x, dpp_move<0x4E>(x));
+  x = fmaxf(x, dpp_move<0x124>(x));
+  x = fmaxf(x, dpp_move<0x128>(x));
+  return fmaxf(fmaxf(row_lane(x, 0), row_lane(x, 16)), fmaxf(row_lane(x, 32), row_lane(x, 48)));
+}
+
+// Sum over the 64 lanes of a wavefront, uniform result: row sums by the same moves (each lane
+// of lanes 0, 16, 32, 48 ends with one fixed association of its row), then the four row sums
+// added in row order. Lane moves instead of LDS swizzles: no LDS round trip per step.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_move<0xB1>(x);
+  x += dpp_move<0x4E>(x);
+  x += dpp_move<0x124>(x);
+  x += dpp_move<0x128>(x);
+  return ((row_lane(x, 0) + row_lane(x, 16)) + row_lane(x, 32)) + row_lane(x, 48);
 }
 
 // One wavefront per token, 4 tokens per 256-thread workgroup.
@@ -414,15 +423,9 @@ router_topk_kernel(const float* __restrict__ part, int splits, const float* __re
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
     if (lane + 64 * j < E) z += expf(v[j] - m);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+  z = wave_sum(z);
   const float p_mine = lane < k ? expf(my_v - m) : 0.f;
-  float denom = z;
-  if (renorm) {
-    denom = p_mine;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) denom += __shfl_xor(denom, off, 64);
-  }
+  const float denom = renorm ? wave_sum(p_mine) : z;
   if (lane < k) {
     topk_idx[t * k + lane] = my_i;
     topk_w[t * k + lane] = p_mine / denom;
@@ -442,49 +445,52 @@ router_topk_kernel(const float* __restrict__ part, int splits, const float* __re
 
 // Top-k for few tokens, four wavefronts per token. With one wavefront per token (above) a lone
 // token's time is set by its serial rounds over E/64 values per lane and by its split loads. Here
-// wavefront w holds experts 256 j + 64 w + lane (j < NJ2, all split loads of a logit in flight
-// 16 at a time), picks its own best k+1 by the same rule (largest logit, lowest index among
-// equals), the four lists go to LDS, and wavefront 0 picks the token's k+1 from those candidates:
-// the same selection. The softmax normaliser is summed per wavefront, then over the four in order.
-__device__ __forceinline__ int wave_min_int(int x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = min(x, __shfl_xor(x, off, 64));
-  return x;
-}
+// wavefront w of the token's 256 threads holds experts 256 j + 64 w + lane (j < NJ2, the split
+// loads of all its logits in flight, up to 64 per lane at a time) and picks its own best k+1 by the same
+// rule (largest logit, lowest index among equals). The four lists go to LDS, where each
+// candidate's rank among all of them is counted in one pass (how many candidates beat it by that
+// rule); the candidates ranked below k+1 are the token's picks, in order. The softmax normaliser
+// is summed per wavefront, then over the four in order.
+struct TopkGroupLds {
+  float c_v[4 * (kMaxK + 1)];  // the four wavefronts' candidate lists
+  int c_i[4 * (kMaxK + 1)];
+  float f_v[kMaxK + 1];  // the token's picks by rank (k + 1 when k < E)
+  int f_i[kMaxK + 1];
+  float s_z[4];
+};
 
-template <int NJ2>
-__global__ void __launch_bounds__(256)
-router_topk_wide_kernel(const float* __restrict__ part, int splits, const float* __restrict__ bias, int64_t T, int E,
-                        int k, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                        float* __restrict__ topk_gap, float* __restrict__ probs) {
-  constexpr int MC = 4 * (kMaxK + 1);
+// Token t on the 256 threads r = 0 .. 255 of a group, B split loads per logit in flight. Every
+// thread of the workgroup must call it (it holds three workgroup barriers); `active` false leaves
+// the group's outputs untouched. Leaves the picks in sm.f_i / sm.f_v.
+template <int NJ2, int B>
+__device__ __forceinline__ void topk_wide_token(const float* __restrict__ part, int splits,
+                                                const float* __restrict__ bias, int64_t T, int E, int k, int renorm,
+                                                int64_t t, bool active, int r, TopkGroupLds& sm,
+                                                int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                float* __restrict__ topk_gap, float* __restrict__ probs) {
   constexpr int NONE = 0x7fffffff;
-  __shared__ float c_v[MC];
-  __shared__ int c_i[MC];
-  __shared__ float s_z[4];
-  __shared__ float s_m;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int64_t t = blockIdx.x;
+  const int wave = r >> 6;
+  const int lane = r & 63;
 
   float v[NJ2];
 #pragma unroll
   for (int j = 0; j < NJ2; ++j) v[j] = 0.f;
-  for (int sp0 = 0; sp0 < splits; sp0 += 16) {
-    float q[NJ2][16];
+  if (active)
+    for (int sp0 = 0; sp0 < splits; sp0 += B) {
+      float q[NJ2][B];
 #pragma unroll
-    for (int j = 0; j < NJ2; ++j) {
-      const int e = 256 * j + 64 * wave + lane;
+      for (int j = 0; j < NJ2; ++j) {
+        const int e = 256 * j + 64 * wave + lane;
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        q[j][u] = (e < E && sp0 + u < splits) ? part[((int64_t)(sp0 + u) * T + t) * E + e] : 0.f;
+        for (int u = 0; u < B; ++u)
+          q[j][u] = (e < E && sp0 + u < splits) ? part[((int64_t)(sp0 + u) * T + t) * E + e] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < NJ2; ++j)
+#pragma unroll
+        for (int u = 0; u < B; ++u)
+          if (sp0 + u < splits) v[j] += q[j][u];
     }
-#pragma unroll
-    for (int j = 0; j < NJ2; ++j)
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (sp0 + u < splits) v[j] += q[j][u];
-  }
 #pragma unroll
   for (int j = 0; j < NJ2; ++j) {
     const int e = 256 * j + 64 * wave + lane;
@@ -497,7 +503,7 @@ router_topk_wide_kernel(const float* __restrict__ part, int splits, const float*
   float my_v = -INFINITY;
   int my_i = NONE;
 #pragma unroll 1
-  for (int r = 0; r < rounds; ++r) {
+  for (int rd = 0; rd < rounds; ++rd) {
     float lv = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NJ2; ++j)
@@ -511,84 +517,60 @@ router_topk_wide_kernel(const float* __restrict__ part, int splits, const float*
       if (bi == NONE && b != 0ull) bi = 256 * j + 64 * wave + (__ffsll(b) - 1);
     }
     if (bi != NONE && (bi & 63) == lane) taken |= 1u << (bi >> 8);
-    if (lane == r) {
+    if (lane == rd) {
       my_v = mv;
       my_i = bi;
     }
   }
   if (lane < rounds) {
-    c_v[wave * rounds + lane] = my_v;
-    c_i[wave * rounds + lane] = my_i;
+    sm.c_v[wave * rounds + lane] = my_v;
+    sm.c_i[wave * rounds + lane] = my_i;
   }
   __syncthreads();
 
-  // wavefront 0: the token's best `rounds` among the 4 * rounds candidates (two per lane)
-  float fv = -INFINITY;
-  int fi = NONE;
-  if (wave == 0) {
-    const int nc = 4 * rounds;
-    float cv[2];
-    int ci[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = lane + 64 * h;
-      cv[h] = c < nc ? c_v[c] : -INFINITY;
-      ci[h] = c < nc ? c_i[c] : NONE;
+  // rank of candidate c among the nc = 4 * rounds: the candidates with a larger logit, or an equal
+  // logit and a lower expert index (NONE entries, equal among themselves, by position). The ranks
+  // are a permutation of 0 .. nc-1, and the ones below `rounds` are the token's picks in order:
+  // every valid expert outside the lists is beaten by `rounds` candidates of its own wavefront.
+  {
+    const int nc = 4 * rounds;  // <= 68: one candidate per thread
+    const int c = r;
+    const float cv = c < nc ? sm.c_v[c] : -INFINITY;
+    const int ci = c < nc ? sm.c_i[c] : NONE;
+    int rank = 0;
+#pragma unroll 4
+    for (int c2 = 0; c2 < nc; ++c2) {
+      const float v2 = sm.c_v[c2];
+      const int i2 = sm.c_i[c2];
+      rank += (v2 > cv || (v2 == cv && (i2 < ci || (i2 == ci && c2 < c)))) ? 1 : 0;
     }
-    uint32_t tk = 0;
-#pragma unroll 1
-    for (int r = 0; r < rounds; ++r) {
-      float lv = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        if (ci[h] != NONE && !((tk >> h) & 1u)) lv = fmaxf(lv, cv[h]);
-      const float mv = wave_max(lv);
-      int li = NONE;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        if (ci[h] != NONE && !((tk >> h) & 1u) && cv[h] == mv) li = min(li, ci[h]);
-      const int bi = wave_min_int(li);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        if (ci[h] == bi) tk |= 1u << h;
-      if (lane == r) {
-        fv = mv;
-        fi = bi;
-      }
+    if (c < nc && rank < rounds) {
+      sm.f_v[rank] = cv;
+      sm.f_i[rank] = ci;
     }
-    if (lane == 0) s_m = fv;
   }
   __syncthreads();
 
   // softmax over all E logits: per-wavefront sums, then the four in order
-  const float m = s_m;
+  const float m = sm.f_v[0];
   float z = 0.f;
 #pragma unroll
   for (int j = 0; j < NJ2; ++j)
     if (256 * j + 64 * wave + lane < E) z += expf(v[j] - m);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
-  if (lane == 0) s_z[wave] = z;
+  z = wave_sum(z);
+  if (lane == 0) sm.s_z[wave] = z;
   __syncthreads();
-  z = ((s_z[0] + s_z[1]) + s_z[2]) + s_z[3];
+  if (!active) return;
+  z = ((sm.s_z[0] + sm.s_z[1]) + sm.s_z[2]) + sm.s_z[3];
   if (wave == 0) {
+    const float fv = lane < rounds ? sm.f_v[lane] : -INFINITY;
     const float p_mine = lane < k ? expf(fv - m) : 0.f;
-    float denom = z;
-    if (renorm) {
-      denom = p_mine;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) denom += __shfl_xor(denom, off, 64);
-    }
+    const float denom = renorm ? wave_sum(p_mine) : z;
     if (lane < k) {
-      topk_idx[t * k + lane] = fi;
+      topk_idx[t * k + lane] = sm.f_i[lane];
       topk_w[t * k + lane] = p_mine / denom;
     }
-    if (topk_gap) {
-      const float g = k < E ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fv), k - 1)) -
-                                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fv), k))
-                            : INFINITY;
-      if (lane == 0) topk_gap[t] = g;
-    }
+    if (topk_gap && lane == 0) topk_gap[t] = k < E ? sm.f_v[k - 1] - sm.f_v[k] : INFINITY;
   }
   if (probs) {
 #pragma unroll
@@ -597,6 +579,65 @@ router_topk_wide_kernel(const float* __restrict__ part, int splits, const float*
       if (e < E) probs[t * E + e] = expf(v[j] - m) / z;
     }
   }
+}
+
+template <int NJ2>
+__global__ void __launch_bounds__(256)
+router_topk_wide_kernel(const float* __restrict__ part, int splits, const float* __restrict__ bias, int64_t T, int E,
+                        int k, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                        float* __restrict__ topk_gap, float* __restrict__ probs) {
+  __shared__ TopkGroupLds sm;
+  topk_wide_token<NJ2, NJ2 >= 4 ? 16 : 32>(part, splits, bias, T, E, k, renorm, blockIdx.x, true, threadIdx.x, sm, topk_idx, topk_w,
+                       topk_gap, probs);
+}
+
+// Top-k and the whole dispatch of a few tokens (T <= 4, E > 64) in one workgroup of 1024 threads:
+// threads 256 g .. 256 g + 255 pick token g's experts (the device code above), then the T*k picks
+// are counted, scanned and scattered from LDS: the same offsets, slots and tile list as the
+// dispatch kernels (stable: token-ascending within an expert; a token's experts are distinct).
+template <int NJ2>
+__global__ void __launch_bounds__(1024)
+route_dispatch_kernel(const float* __restrict__ part, int splits, const float* __restrict__ bias, int64_t T, int E,
+                      int k, int renorm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                      float* __restrict__ topk_gap, int32_t* __restrict__ offsets, int32_t* __restrict__ slot_of,
+                      int32_t* __restrict__ sorted_token, TileListArgs tl) {
+  __shared__ TopkGroupLds sm[4];
+  __shared__ int s_rows[kMaxGroups];
+  __shared__ int s_off[kMaxGroups];
+  __shared__ int s_w[17];
+  const int tid = threadIdx.x;
+  const int g = tid >> 8;
+  topk_wide_token<NJ2, NJ2 >= 4 ? 8 : 16>(part, splits, bias, T, E, k, renorm, g, g < T, tid & 255, sm[g], topk_idx, topk_w, topk_gap,
+                       nullptr);
+  __syncthreads();  // every group's picks in LDS
+
+  const int nt = (int)T;
+  int c = 0;
+  if (tid < E)
+    for (int t = 0; t < nt; ++t)
+      for (int j = 0; j < k; ++j) c += sm[t].f_i[j] == tid ? 1 : 0;
+  const int excl = block_exclusive_scan_1024t(c, s_w, &s_w[16]);
+  if (tid < E) {
+    offsets[tid] = excl;
+    s_off[tid] = excl;
+    s_rows[tid] = c;
+  }
+  if (tid == 0) offsets[E] = s_w[16];
+  if (tid == 0 && tl.tile_group && tl.has_shared) s_rows[E] = (int)T;
+  __syncthreads();
+  if (tid < nt * k) {
+    const int t = tid / k;
+    const int e = sm[t].f_i[tid - t * k];
+    int rank = 0;  // earlier tokens holding e
+    for (int t2 = 0; t2 < t; ++t2)
+      for (int j = 0; j < k; ++j) rank += sm[t2].f_i[j] == e ? 1 : 0;
+    const int slot = s_off[e] + rank;
+    slot_of[tid] = slot;
+    sorted_token[slot] = t;
+  }
+  if (tl.tile_group)
+    build_tile_list(s_rows, E + tl.has_shared, tl.BM, tl.BM2, s_w, tl.tile_group, tl.tile_m0, tl.tile_count,
+                    tl.split_cnt, tl.cnt_each, tl.per_tile);
 }
 
 template <int NJ2>
@@ -681,9 +722,8 @@ router_stats_final_kernel(const double* __restrict__ part_p, const int32_t* __re
 
 }  // namespace
 
-hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, const float* w_router,
-                         const float* bias, int32_t* topk_idx, float* topk_w, float* topk_gap, char* ws,
-                         hipStream_t s, float* probs) {
+hipError_t launch_router_logits(const moe_dims& dm, const Layout& L, const void* x, const float* w_router, char* ws,
+                                hipStream_t s) {
   float* part = (float*)(ws + L.logits);
   if (L.router_mfma) {
     bf16_t* planes = (bf16_t*)(ws + L.router_planes);
@@ -703,20 +743,44 @@ hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, con
     else
       launch_router_small<bf16_t>((const bf16_t*)x, w_router, part, dm.T, dm.d, dm.E, L.router_splits,
                                   L.router_kchunk, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
   } else {
-  const dim3 grid((unsigned)((dm.E + kRouterTileE - 1) / kRouterTileE),
-                  (unsigned)((dm.T + kRouterTileT - 1) / kRouterTileT), (unsigned)L.router_splits);
-  if (dm.dtype == MOE_F32)
-    hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, s, (const float*)x, w_router, part, dm.T,
-                       dm.d, dm.E, L.router_kchunk);
-  else
-    hipLaunchKernelGGL(router_logits_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x, w_router, part, dm.T,
-                       dm.d, dm.E, L.router_kchunk);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)((dm.E + kRouterTileE - 1) / kRouterTileE),
+                    (unsigned)((dm.T + kRouterTileT - 1) / kRouterTileT), (unsigned)L.router_splits);
+    if (dm.dtype == MOE_F32)
+      hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, s, (const float*)x, w_router, part, dm.T,
+                         dm.d, dm.E, L.router_kchunk);
+    else
+      hipLaunchKernelGGL(router_logits_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x, w_router, part,
+                         dm.T, dm.d, dm.E, L.router_kchunk);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_dispatch(const moe_dims& dm, const Layout& L, const float* bias, int32_t* topk_idx,
+                                float* topk_w, float* topk_gap, int32_t* offsets, int32_t* sorted_token,
+                                int32_t* slot_of, char* ws, hipStream_t s, bool with_tiles) {
+  if (!L.route_fused) return hipErrorInvalidValue;
+  const float* part = (const float*)(ws + L.logits);
+  const TileListArgs tl = tile_list_args(dm, L, ws, with_tiles);
+  const int nj2 = (dm.E + 255) / 256;
+  if (nj2 <= 1)
+    hipLaunchKernelGGL(route_dispatch_kernel<1>, dim3(1), dim3(1024), 0, s, part, L.router_splits, bias, dm.T, dm.E,
+                       dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, offsets, slot_of, sorted_token, tl);
+  else if (nj2 <= 2)
+    hipLaunchKernelGGL(route_dispatch_kernel<2>, dim3(1), dim3(1024), 0, s, part, L.router_splits, bias, dm.T, dm.E,
+                       dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, offsets, slot_of, sorted_token, tl);
+  else
+    hipLaunchKernelGGL(route_dispatch_kernel<4>, dim3(1), dim3(1024), 0, s, part, L.router_splits, bias, dm.T, dm.E,
+                       dm.k, dm.renormalize, topk_idx, topk_w, topk_gap, offsets, slot_of, sorted_token, tl);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const moe_dims& dm, const Layout& L, const void* x, const float* w_router,
+                         const float* bias, int32_t* topk_idx, float* topk_w, float* topk_gap, char* ws,
+                         hipStream_t s, float* probs) {
+  hipError_t e = launch_router_logits(dm, L, x, w_router, ws, s);
+  if (e != hipSuccess) return e;
+  const float* part = (const float*)(ws + L.logits);
   const int nj = (dm.E + 63) / 64;
   const int sp = L.router_splits;
   if (dm.T <= kTopkWideMaxT && dm.E > 64) {

@@ -128,6 +128,13 @@ SMALL_CASES = [
     ("wide_tiles_576", 576, 512, 4, 4, 256, 256, syn.BF16, 1, 0.0),
     ("wide_tiles_161", 161, 512, 4, 4, 256, 512, syn.BF16, 1, 0.0),
     ("wide_tiles_384", 384, 1024, 4, 4, 512, 256, syn.BF16, 0, 0.0),
+    # T <= 4 with E > 64: top-k and dispatch in one launch (four wavefronts per token, the T*k
+    # picks scattered from LDS): 1024 experts (four logits per lane) with k = 16 and three tokens;
+    # 65 experts (wavefronts holding one expert or none) with 4 * 16 = 64 pairs, fp32; four tokens
+    # on the MFMA gate/up product's K split
+    ("fused_route_E1024_T3", 3, 256, 1024, 16, 64, 64, syn.BF16, 1, 0.0),
+    ("fused_route_E65_T4_f32", 4, 128, 65, 16, 32, 0, syn.F32, 0, 0.0),
+    ("fused_route_E200_T4", 4, 1024, 200, 8, 256, 256, syn.BF16, 1, 0.0),
 ]
 
 
@@ -212,11 +219,13 @@ def test_permute_skewed_with_invalid_indices(torch, E, T):
 # --------------------------------------------------------------------------------------------
 # the four step entry points compose to moe_forward, bit for bit; permute is a stable sort
 # --------------------------------------------------------------------------------------------
-# the grouped GEMMs' three bf16 paths: MFMA tiles (T = 600), MFMA with K split (T = 5), skinny (T = 2)
-@pytest.mark.parametrize("T,d,I,Is", [(600, 256, 128, 64), (5, 2048, 512, 512), (2, 512, 256, 256)])
-def test_steps_compose_and_permute_is_stable_sort(torch, T, d, I, Is):
+# the grouped GEMMs' three bf16 paths: MFMA tiles (T = 600), MFMA with K split (T = 5), skinny (T = 2);
+# with E > 64 and T <= 4 the forward runs top-k and dispatch as one launch, the steps as two
+@pytest.mark.parametrize("T,d,I,Is,E", [(600, 256, 128, 64, 48), (5, 2048, 512, 512, 48), (2, 512, 256, 256, 48),
+                                        (2, 512, 256, 256, 96), (4, 1024, 256, 128, 300)])
+def test_steps_compose_and_permute_is_stable_sort(torch, T, d, I, Is, E):
     import sparse_mixture_experts_softmax_amd as moe
-    cfg = syn.MoEConfig("steps", T=T, d=d, E=48, k=6, I=I, Is=Is, dtype=syn.BF16, seed=3)
+    cfg = syn.MoEConfig("steps", T=T, d=d, E=E, k=6, I=I, Is=Is, dtype=syn.BF16, seed=3)
     h = host_inputs(cfg)
     dev = device_from_host(h, cfg)
     dims = moe.dims_for(dev["x"], dev["w_router"], dev["wg"], dev["wg_s"], cfg.k, True)
@@ -458,6 +467,36 @@ def test_router_stats_match_oracle(torch, cfg):
     err = np.max(np.abs(g - rpm))
     assert err <= 1e-5 * rpm.max(), (err, rpm.max())
     _say(cfg.name, "flagged", int((~ok).sum()), "prob_mean max err", err)
+
+
+# --------------------------------------------------------------------------------------------
+# exact ties: a zero router makes the logits the bias itself, bias[e] = -(e % 64) / 4, so experts
+# 64 apart tie and every tie class spans all four wavefronts of the few-token top-k. The pages'
+# rule as read (largest logit, the lower expert index among equals, kept in that order) fixes
+# the indices, their order and the weights even where the k-th and (k+1)-th logits are equal.
+# Few-token top-k (T <= 64, E > 64; k = 16 with 68 merge candidates) and one wavefront per token.
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k,renorm", [(3, 300, 7, 1), (2, 1024, 16, 0), (1, 512, 10, 1), (70, 300, 7, 1),
+                                          (40, 64, 8, 0)])
+def test_router_exact_ties_lower_index_first(torch, T, E, k, renorm):
+    import sparse_mixture_experts_softmax_amd as moe
+    from moe_testlib import to_device
+    cfg = syn.MoEConfig("ties", T=T, d=256, E=E, k=k, I=64, Is=0, dtype=syn.BF16, renorm=renorm, seed=41)
+    _say("case", "ties", T, E, k, renorm)
+    x = syn.host_x(cfg)
+    wr = np.zeros((cfg.d, E), np.float32)
+    bias = (-(np.arange(E) % 64) * 0.25).astype(np.float32)
+    dims = moe.MoeDims(T, cfg.d, E, k, cfg.I, 0, cfg.dtype, renorm)
+    idx, w, gap = moe.moe_router_topk(dims, to_device(x, torch_dtype(cfg)), to_device(wr, torch.float32),
+                                      to_device(bias, torch.float32))
+    torch.cuda.synchronize()
+    ridx, rw, rgap, _ = oracle.router(x, wr, k, renorm=bool(renorm), bias=bias)
+    # the tie rule by brute force: by descending bias, then ascending index
+    order = np.lexsort((np.arange(E), -bias.astype(np.float64)))[:k]
+    assert np.array_equal(ridx, np.tile(order, (T, 1)))
+    assert np.array_equal(to_host(idx), ridx)
+    assert np.max(np.abs(to_host(w).astype(np.float64) - rw)) <= 1e-6
+    assert np.array_equal(to_host(gap).astype(np.float64), rgap)
 
 
 # --------------------------------------------------------------------------------------------

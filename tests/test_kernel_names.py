@@ -52,6 +52,10 @@ def test_few_token_and_fp8_kernels(lib):
     assert moe.moe_kernel_name(_dims(pre), moe.KERNEL_ROUTER) == "router_mfma_kernel"
     assert moe.moe_kernel_name(_dims(cfg), moe.KERNEL_ROUTER) == "router_small_kernel"
     assert moe.moe_kernel_name(_dims(cfg), moe.KERNEL_PERMUTE) == "permute_one_chunk_kernel"
+    # up to four tokens (E > 64): top-k and dispatch in one launch
+    assert moe.moe_kernel_name(_dims(cfg, T=1), moe.KERNEL_PERMUTE) == "route_dispatch_kernel"
+    assert moe.moe_kernel_name(_dims(cfg, T=4), moe.KERNEL_PERMUTE) == "route_dispatch_kernel"
+    assert moe.moe_kernel_name(_dims(cfg, T=5), moe.KERNEL_PERMUTE) == "permute_one_chunk_kernel"
     assert moe.moe_kernel_name(_dims(pre), moe.KERNEL_COMBINE) == "combine_kernel"
 
 
