@@ -351,6 +351,107 @@ def workload_name(cfg, block=False, fp8=False):
         ", RMSNorm in front and residual add" if block else ", FP8 e4m3 expert weights" if fp8 else "")
 
 
+def _csv_rows(directory, suffix):
+    """Rows of every rocprofv3 CSV under `directory` whose file name ends in `suffix`."""
+    import csv
+    rows = []
+    for base, _, files in os.walk(directory):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                with open(os.path.join(base, f), newline="") as fh:
+                    rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit("no *%s under %s" % (suffix, directory))
+    return rows
+
+
+def _short_kernel_name(name):
+    """A kernel's demangled name without return type, argument list and clone suffix."""
+    name = name.replace(" [clone .kd]", "").strip()
+    if name.startswith("void "):
+        name = name[5:]
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):  # the argument list is the first '(' outside template brackets
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    return name[:cut]
+
+
+def _per_dispatch(rows, counter):
+    """{dispatch id: (kernel, grid size, value)} of one counter in a counter-collection CSV."""
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = r["Dispatch_Id"]
+        prev = out.get(key, (None, 0, 0.0))[2]
+        out[key] = (_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]), prev + float(r["Counter_Value"]))
+    return out
+
+
+def summarize_traffic(workload, fetch_dir, write_dir, commands):
+    """HBM bytes per launch of the gate/up GEMM from two rocprofv3 --pmc runs of bench.py
+    --copy-calibration (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
+    same counter reads for the 1 GiB device copy in the same process. Prints the JSON record that
+    bench.py reads back as `roofline.traffic`."""
+    import synthetic as syn
+
+    cfg = syn.CONFIGS[workload]
+    kname = kernel_label(cfg, False).split(" (")[0]
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        disp = _per_dispatch(_csv_rows(d, "counter_collection.csv"), counter)
+        kv = [v for (n, _, v) in disp.values() if n == kname]
+        copies = [(g, v) for (n, g, v) in disp.values() if "copyBuffer" in n]
+        if not kv or not copies:
+            raise SystemExit("%s: no dispatch of %s or of the copy kernel" % (counter, kname))
+        gmax = max(g for g, _ in copies)
+        cv = [v for g, v in copies if g == gmax]
+        res[counter] = (sum(kv) / len(kv), len(kv), sum(cv) / len(cv), len(cv))
+    nbytes = 1 << 30
+    fscale = nbytes / 1024.0 / res["FETCH_SIZE"][2]
+    wscale = nbytes / 1024.0 / res["WRITE_SIZE"][2]
+    fetch_b = res["FETCH_SIZE"][0] * 1024.0 * fscale
+    write_b = res["WRITE_SIZE"][0] * 1024.0 * wscale
+    # the algorithmic bytes depend on the routing (experts touched): taken from the bench line
+    # that the profiled run printed, saved as bench.json beside the FETCH_SIZE results
+    algo = None
+    line = os.path.join(fetch_dir, "bench.json")
+    if os.path.exists(line):
+        algo = json.load(open(line))["roofline"]["algorithmic_bytes"]
+    rec = {"workload": workload_name(cfg), "commands": commands, "kernel": kname + " (grouped gate/up GEMM)",
+           "dispatches": res["FETCH_SIZE"][1], "copy_dispatches": res["FETCH_SIZE"][3],
+           "fetch_kib_per_dispatch": res["FETCH_SIZE"][0], "write_kib_per_dispatch": res["WRITE_SIZE"][0],
+           "copy_calibration": {"bytes_copied": nbytes, "fetch_kib": res["FETCH_SIZE"][2],
+                                "write_kib": res["WRITE_SIZE"][2], "fetch_scale": fscale, "write_scale": wscale},
+           "bytes_per_launch": fetch_b + write_b, "fetch_bytes_per_launch": fetch_b,
+           "write_bytes_per_launch": write_b,
+           "algorithmic_bytes_per_launch": algo,
+           "kernel_source_sha256": kernel_source_hash()}
+    print(json.dumps(rec, indent=1))
+
+
+def summarize_trace(title, trace_dir, command):
+    """Per-kernel table of a rocprofv3 --kernel-trace --stats run (its kernel_stats CSV)."""
+    rows = _csv_rows(trace_dir, "kernel_stats.csv")
+    agg = {}
+    for r in rows:
+        n = _short_kernel_name(r["Name"])
+        c, t = agg.get(n, (0, 0.0))
+        agg[n] = (c + int(r["Calls"]), t + float(r["TotalDurationNs"]))
+    total = sum(t for _, t in agg.values())
+    print("# rocprofv3 kernel trace, %s" % title)
+    print("# command (repo root): %s" % command)
+    print("%-52s %8s %12s %12s %8s" % ("kernel", "calls", "avg_us", "total_ms", "pct"))
+    for n, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        print("%-52s %8d %12.1f %12.3f %8.3g" % (n[:52], c, t / c / 1e3, t / 1e6, 100.0 * t / total))
+
+
 DECODE_STEPS = 50  # the decode leg's timed steps (its median is over 50 runs)
 
 
@@ -373,7 +474,20 @@ def main():
                     help="only measure reference points (vendor bf16 GEMM, device copy) and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the token-count sweep T = 1 .. 512 at the large layer shape, one line per T")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
+                    help="print the gate/up HBM-traffic record from two rocprofv3 --pmc runs (no GPU use)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TITLE", "TRACE_DIR"),
+                    help="print the per-kernel table of a rocprofv3 --kernel-trace --stats run (no GPU use)")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --summarize-*: the profiler command(s) that made the run, for the record")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, commands=args.command)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, command="; ".join(args.command))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
