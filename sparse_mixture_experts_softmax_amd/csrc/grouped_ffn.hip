@@ -1026,17 +1026,17 @@ FfnPlan ffn_plan(const moe_dims& dm) {
   P.ks1 = P.ks2 = P.kc1 = P.kc2 = 0;
   if (P.skinny) {
     const int64_t groups = (Tk < dm.E ? Tk : dm.E) + has_shared;
-    auto split = [&](int K, int cb, int& ks, int& kc) {
-      int64_t want = 1024 / (groups * cb);
+    auto split = [&](int K, int cb, int64_t target, int kr, int& ks, int& kc) {
+      int64_t want = target / (groups * cb);
       const int64_t most = (K + 255) / 256;  // at least 256 K rows per split
       if (want > most) want = most;
       if (want < (K + kSkinnyMaxKC - 1) / kSkinnyMaxKC) want = (K + kSkinnyMaxKC - 1) / kSkinnyMaxKC;
       if (want < 1) want = 1;
-      kc = (int)(((K + want - 1) / want + 7) / 8 * 8);
+      kc = (int)(((K + want - 1) / want + kr - 1) / kr * kr);  // whole LDS stages
       ks = (K + kc - 1) / kc;
     };
-    split(dm.d, P.cb1, P.ks1, P.kc1);
-    split(ldh, P.cb2, P.ks2, P.kc2);
+    split(dm.d, P.cb1, kSkinnyWG1, kSkinnyMat1 / 512, P.ks1, P.kc1);
+    split(ldh, P.cb2, kSkinnyWG2, kSkinnyMat2 / 512, P.ks2, P.kc2);
   }
   return P;
 }
@@ -1044,7 +1044,7 @@ FfnPlan ffn_plan(const moe_dims& dm) {
 hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
                               const int32_t* sorted_token, const void* wg, const void* wu, const void* wd,
                               const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
-                              hipStream_t s, const Prof* prof, bool tiles_ready) {
+                              hipStream_t s, const Prof* prof, bool tiles_ready, CombineFuse* combine) {
   const Prof none;
   if (!prof) prof = &none;
   int32_t* tg = (int32_t*)(ws + L.tile_group);
@@ -1065,7 +1065,8 @@ hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x
   char* H = ws + L.H;
 
   if (P.skinny)
-    return launch_ffn_skinny(dm, L, P, x, offsets, sorted_token, wg, wu, wd, wg_s, wu_s, wd_s, y, ws, s, prof);
+    return launch_ffn_skinny(dm, L, P, x, offsets, sorted_token, wg, wu, wd, wg_s, wu_s, wd_s, y, ws, s, prof,
+                             combine);
   if (dm.dtype == MOE_BF16) {
     MfmaArgs a;
     a.offsets = offsets;

@@ -3,21 +3,23 @@
 // With T <= 2 every group (a routed expert, or the shared expert) holds at most T rows, so the
 // products are weight streams: ~1 GB of weights for a handful of rows at the large shape, and
 // under one FMA per weight byte per row. A 32 x 32 MFMA tile would be almost all padding; here the
-// weights come in with plain 16-byte vector loads and the dot products run on the vector ALUs in
-// fp32, which leaves the memory pipe to the weight stream alone.
+// weights stream into LDS by DMA and the dot products run on the vector ALUs in fp32.
 //
 // One workgroup (256 threads) per (group, 256-column block, K split):
 //   - the group's rows of A (x rows gathered through sorted_token for the gate/up product, H rows
-//     for the down product) over the split's K range are staged in LDS as fp32;
-//   - thread (wave w, lane l) owns columns n0 + 8 (l % 32) .. +7 and the K rows
-//     k0 + 2w + l / 32 + 8 i, so each wave load covers two weight rows of 512 contiguous bytes; each
-//     thread issues eight rows (sixteen for gate and up) of loads at a time;
+//     for the down product) over the split's K range are DMA'd into LDS as bf16;
+//   - the weight rows of the split pass through a ring of LDS stages (direct global-to-LDS loads,
+//     S - 1 stages in flight while one is multiplied); thread (wave w, lane l) owns columns
+//     n0 + 8 (l % 32) .. +7 and the K rows 2w + l / 32 + 8 i of each stage;
 //   - sums in fixed order: each thread over its K rows in ascending order, then the two lane
 //     halves, then the four waves in order, then the K splits in split order (gate/up: a small
 //     follow-up kernel adds the splits' fp32 partials; down: the last split to arrive, by an
 //     arrival counter per (group, column block), adds them, as the MFMA kernels' split K does);
-//   - the gate/up product ends in silu(g) * u rounded to bf16 (H), the down product in bf16 Y rows.
+//   - the gate/up product ends in silu(g) * u rounded to bf16 (H), the down product in bf16 Y rows;
+//     in a forward, the down product's last group per column block also performs the combine
+//     (weighted sum of the token's expert rows, shared row, optional residual) for those columns.
 #include "moe_internal.h"
+#include "stream_gemm.h"
 
 namespace moe {
 namespace {
@@ -40,20 +42,66 @@ struct SkinnyArgs {
   float* part;  // ks > 1: fp32 partial rows part[split][row][part_ld]
   int64_t part_ld, part_sstride;
   int32_t* cnt;  // ks > 1: arrival counter per (tile, column block), zero on entry
+  // down product with the combine (fout non-null): the block's output rows [T, d], the routing,
+  // the residual rows (or null), and one arrival counter per column block, zero on entry
+  bf16_t* fout;
+  const int32_t* slot_of;
+  const float* topk_w;
+  const bf16_t* resid;
+  int32_t* ccnt;
 };
 
-constexpr int kU = 8;  // K rows of loads in flight per thread (per weight matrix)
-
-// 16 bytes of weights with the non-temporal hint: each weight byte is read once, and marking the
-// stream so (rather than letting it displace cached lines) took the T = 1 gate/up product at the
-// large shape from 150 to 134 us and the down product from 68 to 65 us
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_weights16(const bf16_t* q) {
-  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)q);
-  return make_uint4(v[0], v[1], v[2], v[3]);
+// Columns n0 .. n0 + 255 of the block's output for every token (T <= 2), as combine_kernel sums
+// them: out = sum_j w[t, j] * y[slot_of[t k + j]] in the order j = 0 .. k-1 (fp32, fused
+// multiply-add from zero), then the shared expert's row, then the residual row, rounded once.
+// The expert rows were stored by other workgroups with device-scope stores; they are read the
+// same way. Thread (t, c): token t = tid / 128, columns n0 + 2c and n0 + 2c + 1.
+__device__ __forceinline__ void combine_columns(const SkinnyArgs& p, int n0) {
+  const int t = threadIdx.x >> 7;
+  if (t >= p.T) return;
+  const int64_t col = n0 + 2 * (threadIdx.x & 127);
+  const int k = p.k;
+  uint32_t yv[kMaxK];
+  float w[kMaxK];
+  bool on[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    on[j] = false;
+    if (j < k) {
+      const int slot = p.slot_of[t * k + j];
+      w[j] = p.topk_w[t * k + j];
+      on[j] = slot >= 0;
+      if (on[j])
+        yv[j] = __hip_atomic_load((const uint32_t*)(p.out + (int64_t)slot * p.d + col), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  uint32_t ys = 0, rv = 0;
+  if (p.Is > 0)
+    ys = __hip_atomic_load((const uint32_t*)(p.out + (p.T * k + t) * p.d + col), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  if (p.resid) rv = *(const uint32_t*)(p.resid + t * p.d + col);
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (on[j]) {
+      a0 = fmaf(w[j], bf16lo_to_f32(yv[j]), a0);
+      a1 = fmaf(w[j], bf16hi_to_f32(yv[j]), a1);
+    }
+  if (p.Is > 0) {
+    a0 += bf16lo_to_f32(ys);
+    a1 += bf16hi_to_f32(ys);
+  }
+  if (p.resid) {
+    a0 += bf16lo_to_f32(rv);
+    a1 += bf16hi_to_f32(rv);
+  }
+  *(uint32_t*)(p.fout + t * p.d + col) = pack_bf16x2(a0, a1);
 }
 
-__device__ __forceinline__ void fma8(float (&acc)[8], float a, const uint4& w) {
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void fma8(float (&acc)[8], float a, const u32x4_t& w) {
   acc[0] += a * bf16lo_to_f32(w.x);
   acc[1] += a * bf16hi_to_f32(w.x);
   acc[2] += a * bf16lo_to_f32(w.y);
@@ -64,15 +112,38 @@ __device__ __forceinline__ void fma8(float (&acc)[8], float a, const uint4& w) {
   acc[7] += a * bf16hi_to_f32(w.w);
 }
 
+// The weights stream into an LDS ring with gfx950's direct global-to-LDS loads (16 bytes per
+// lane, no registers held in flight), with the non-temporal hint, since no other workgroup reads
+// these bytes. Each stage holds KR rows of every weight matrix of the 256-column block (512 bytes
+// per row, rows one after another): one DMA instruction of a wavefront moves two rows (lane l:
+// row l / 32, chunk l % 32). At the large shape this took the one-token layer from 0.214 to
+// 0.202 ms against plain 16-byte vector loads of the same stream; 512-column blocks (1 KB runs
+// per row) measured slower for both products (gate/up 114 -> 123 us, down 69 -> 73 us).
+// Thread mapping: chunk c = tid % 32 (columns 8c .. 8c + 7 of the block), K lane kl = tid / 32
+// (rows kl, kl + 8, ... of each stage).
 template <bool GATED, int R>
 __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
+  constexpr int NC = 256;            // columns of the block
   constexpr int NM = GATED ? 2 : 1;  // weight matrices
-  __shared__ float s_a[R][kSkinnyMaxKC];
-  __shared__ float s_red[4][R][NM][256];
+  constexpr int ROWB = NC * 2;       // bytes of one weight row of the column block
+  constexpr int KR = (GATED ? kSkinnyMat1 : kSkinnyMat2) / ROWB;
+  constexpr int S = GATED ? kSkinnyS1 : kSkinnyS2;
+  constexpr int CPRL = NC / 8;       // 16-byte chunks per row
+  constexpr int NKL = 256 / CPRL;    // K lanes of the workgroup
+  constexpr int MAT = KR * ROWB;     // one matrix's rows of a stage
+  constexpr int STAGE = NM * MAT;
+  constexpr int IPM = MAT / 1024 / 4;  // DMA instructions per wavefront, matrix and stage
+  constexpr int D = NM * IPM;          // per wavefront and stage
+  constexpr int CPT = NC / 64;         // output columns per thread in the epilogue (4)
+  static_assert(KR % NKL == 0 && IPM >= 1 && MAT % 4096 == 0, "stage rows");
+  static_assert(S >= 2 && S <= 7 && 7 * D < 64, "ring depth");
+  static_assert(4 * R * NM * NC * 4 <= S * STAGE, "the wave sums fit the ring");
+  __shared__ __attribute__((aligned(1024))) char s_ring[S * STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t s_a[R][kSkinnyMaxKC];
   __shared__ int s_last;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int per_tile = p.n_cblk * p.ks;
   const int mt = blockIdx.x / per_tile;
@@ -84,11 +155,13 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
   const Group G = group_info(g, p.offsets, p.T, p.k, p.E, p.I, p.Is);
   const int K = GATED ? p.d : G.n_inter;
   const int N = GATED ? G.n_inter : p.d;
-  const int n0 = cb * 256;
+  const int n0 = cb * NC;
   if (n0 >= N) return;  // the whole (tile, column block) leaves: its counter is not used
   const int rows = G.rows;  // <= R
   const int k0 = split * p.kc;
   const int k1 = min(K, k0 + p.kc);  // k1 <= k0: an empty split (partials of zero)
+  // K and kc are multiples of KR, so the split is whole stages
+  const int nst = k1 > k0 ? (k1 - k0) / KR : 0;
 
   const bf16_t* W0;
   const bf16_t* W1 = nullptr;
@@ -98,66 +171,60 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
   } else {
     W0 = G.shared ? p.w0_s : p.w0 + (size_t)g * p.I * p.d;
   }
-  const int cth = lane & 31;
-  const int kl = 2 * wave + (lane >> 5);
-  const int64_t col = n0 + 8 * cth;
-  const bf16_t* w0p = W0 + col;
-  const bf16_t* w1p = GATED ? W1 + col : nullptr;
-  // this thread's K rows k0 + kl + 8 i, i < steps, in batches of kU rows. k1 - k0 is a multiple of
-  // 8 (K and kc are), so every thread of the workgroup has the same count.
-  const int steps = k1 > k0 ? (k1 - k0) / 8 : 0;
-  auto load = [&](uint4 (&buf)[NM][kU], int b) {
-    const int kb = k0 + kl + 8 * kU * b;
+  const int cth = tid % CPRL;
+  const int kl = tid / CPRL;
+
+  // DMA: wave-uniform bases at (k0, n0) of each matrix, per-lane offsets below 2^32 (kc rows of at
+  // most 16 KB)
+  const char* wb0 = stream::uniform_ptr((const char*)(W0 + (int64_t)k0 * N + n0));
+  const char* wb1 = GATED ? stream::uniform_ptr((const char*)(W1 + (int64_t)k0 * N + n0)) : nullptr;
+  const uint32_t pitch = (uint32_t)N * 2u;
+  constexpr int RPI = 1024 / ROWB;  // rows per DMA instruction
+  const uint32_t loff = (uint32_t)(lane / CPRL) * pitch + (uint32_t)(lane % CPRL) * 16u;
+  stream::lds_char* ring = (stream::lds_char*)s_ring;
+  const uint32_t ring_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ring);
+  auto issue = [&](int st) {  // stage st into slot st % S
+    const uint32_t dst = ring_base + (uint32_t)(st % S) * STAGE;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      buf[0][u] = load_weights16(w0p + (int64_t)(kb + 8 * u) * N);
-      if (GATED) buf[NM - 1][u] = load_weights16(w1p + (int64_t)(kb + 8 * u) * N);
+    for (int q = 0; q < IPM; ++q) {
+      const int i = wave * IPM + q;  // rows RPI i .. RPI i + RPI - 1 of the stage
+      const uint32_t voff = (uint32_t)(st * KR + RPI * i) * pitch + loff;
+      stream::dma16<true>(wb0, voff, dst + i * 1024);
+      if (GATED) stream::dma16<true>(wb1, voff, dst + MAT + i * 1024);
     }
-    __builtin_amdgcn_sched_barrier(0);  // the batch's loads go out before the work that follows
   };
 
-  // A rows of this split as fp32 (rows past the group's are zero). The source rows are resolved
-  // once; the A chunks (8 values, 16 bytes) then load without branches, all in flight together.
+  // A rows of this split, bf16, DMA'd into s_a ahead of the ring's first stages (rows past the
+  // group's repeat its first row; their sums are never stored). Instruction ia of the workgroup
+  // loads 64 chunks of 8 values of row ia / na; lanes past the split's K read the row's first
+  // chunk into the unused tail of s_a. No register loads are in flight, so every wait below is an
+  // explicit DMA count.
   const int64_t a_ld = GATED ? p.d : p.ldh;
+  const int cpr = (k1 - k0) / 8;   // A chunks per row
+  const int na = (cpr + 63) / 64;  // A instructions per row
+  const uint32_t sa_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(stream::lds_char*)&s_a[0][0]);
   int64_t srow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int rr = r < rows ? r : 0;  // a group holds >= 1 row
     srow[r] = GATED ? (G.shared ? (int64_t)rr : (int64_t)p.sorted_token[G.row0 + rr]) : G.row0 + rr;
   }
-  const int cpr = p.kc / 8;  // A chunks per row
-  uint4 av[R];               // R * cpr <= R * 256 chunks over 256 threads
-  auto load_a = [&]() {
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const int i = tid + 256 * j;
-      const int r = i / cpr;
-      const int c = i - r * cpr;
+  if (nst > 0)
+    for (int ia = wave; ia < R * na; ia += 4) {
+      const int r = ia / na;
+      const int q = ia - r * na;
       int64_t sr = srow[0];
 #pragma unroll
-      for (int q = 1; q < R; ++q)
-        if (r == q) sr = srow[q];
-      const bool valid = r < rows && k0 + 8 * c < k1;
-      av[j] = *(const uint4*)(p.a_src + (valid ? sr * a_ld + k0 + 8 * c : 0));
-      if (!valid) av[j] = make_uint4(0u, 0u, 0u, 0u);
+      for (int u = 1; u < R; ++u)
+        if (r == u) sr = srow[u];
+      const int c = 64 * q + lane;
+      const uint32_t voff = (uint32_t)((sr * a_ld + k0 + (c < cpr ? 8 * c : 0)) * 2);
+      stream::dma16(p.a_src, voff, __builtin_amdgcn_readfirstlane(sa_base + r * (kSkinnyMaxKC * 2) + q * 1024));
     }
-  };
-  auto stage_a = [&]() {  // then the LDS barrier alone: weight loads stay in flight
+  const int pro = nst < S ? nst : S;
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const int i = tid + 256 * j;
-      const int r = i / cpr;
-      const int c = i - r * cpr;
-      if (r < R) {
-        float* d = &s_a[r][8 * c];
-        *(float4*)d = make_float4(bf16lo_to_f32(av[j].x), bf16hi_to_f32(av[j].x), bf16lo_to_f32(av[j].y),
-                                  bf16hi_to_f32(av[j].y));
-        *(float4*)(d + 4) = make_float4(bf16lo_to_f32(av[j].z), bf16hi_to_f32(av[j].z), bf16lo_to_f32(av[j].w),
-                                        bf16hi_to_f32(av[j].w));
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
+  for (int st = 0; st < S; ++st)
+    if (st < pro) issue(st);
 
   float acc[NM][R][8];
 #pragma unroll
@@ -166,56 +233,33 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[m][r][c] = 0.f;
-  auto compute = [&](const uint4 (&buf)[NM][kU], int b) {
-    const int ko = kl + 8 * kU * b;  // offset of the batch's first row from k0
+  for (int st = 0; st < nst; ++st) {
+    // this wave's DMAs of stage st have landed once at most the later stages' are pending; after
+    // the barrier every wave's have, and every wave is done with stage st - 1 (its LDS reads
+    // returned), whose slot then takes stage st - 1 + S
+    stream::wait_groups<D>(min(st == 0 ? S - 1 : S - 2, nst - 1 - st));
+    stream::barrier_after_lds_reads();
+    if (st >= 1 && st - 1 + S < nst) issue(st - 1 + S);
+    const stream::lds_char* sl = ring + (st % S) * STAGE + cth * 16;
+    u32x4_t wv[NM][KR / NKL];
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
+    for (int u = 0; u < KR / NKL; ++u)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        wv[m][u] = *(const __attribute__((address_space(3))) u32x4_t*)(sl + m * MAT + (kl + NKL * u) * ROWB);
+#pragma unroll
+    for (int u = 0; u < KR / NKL; ++u)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float a = s_a[r][ko + 8 * u];
+        const float a = __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, s_a[r][st * KR + kl + NKL * u]) << 16);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) fma8(acc[m][r], a, buf[m][u]);
+        for (int m = 0; m < NM; ++m) fma8(acc[m][r], a, wv[m][u]);
       }
-  };
-  auto tail = [&](int from) {  // rows past the whole batches, one at a time
-    for (int i = from; i < steps; ++i) {
-      const int kk = k0 + kl + 8 * i;
-      uint4 wv[NM];
-      wv[0] = load_weights16(w0p + (int64_t)kk * N);
-      if (GATED) wv[NM - 1] = load_weights16(w1p + (int64_t)kk * N);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float a = s_a[r][kk - k0];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) fma8(acc[m][r], a, wv[m]);
-      }
-    }
-  };
-
-  if (steps >= kU) {
-    // Straight-line streaming: every batch load is unconditional, so the compiler's waits before
-    // a batch's FMAs count exactly that batch. The A loads go out before the first batch: waiting
-    // for them (loads complete in order) leaves the batch in flight behind the staging. One batch
-    // per thread at a time keeps the registers low enough for five workgroups per CU, whose loads
-    // together keep the memory pipe full.
-    const int nbw = steps / kU;  // whole batches
-    uint4 buf[NM][kU];
-    load_a();
-    load(buf, 0);
-    stage_a();
-    compute(buf, 0);
-    for (int b = 1; b < nbw; ++b) {
-      load(buf, b);
-      compute(buf, b);
-    }
-    tail(nbw * kU);
-  } else {
-    load_a();
-    stage_a();
-    tail(0);
   }
+  __syncthreads();  // every wave is done with the ring: it now holds the K lanes' sums
+  float (*s_red)[R][NM][NC] = (float (*)[R][NM][NC])s_ring;
 
-  // the lane halves hold the even and odd K lanes of the same columns; then the waves via LDS
+  // the lane halves hold K lanes 2w and 2w + 1 of the same columns; then the waves via LDS
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -233,21 +277,21 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
       }
   __syncthreads();
 
-  // thread -> row r = tid / 64, columns c4 .. c4 + 3 of the block
+  // thread -> row r = tid / 64, columns cc .. cc + CPT - 1 of the block
   const int r = tid >> 6;
-  const int c4 = (tid & 63) * 4;
-  float v[NM][4];
+  const int cc = (tid & 63) * CPT;
+  float v[NM][CPT];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) v[m][c] = 0.f;
+    for (int c = 0; c < CPT; ++c) v[m][c] = 0.f;
   if (r < R)
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[m][c] += s_red[w][r][m][c4 + c];
+        for (int c = 0; c < CPT; ++c) v[m][c] += s_red[w][r][m][cc + c];
   const bool mine = r < rows;
 
   if (GATED && p.ks > 1) {
@@ -256,22 +300,25 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
     // here spares every workgroup the store-acknowledge, counter and reload round trips of the
     // last-arriver sum (T = 1 at the large shape: ~17 us of the product's ~135 us).
     if (mine) {
-      float* q = p.part + (int64_t)split * p.part_sstride + (G.row0 + r) * p.part_ld + n0 + c4;
-      *(float4*)q = make_float4(v[0][0], v[0][1], v[0][2], v[0][3]);
-      *(float4*)(q + p.ldh) = make_float4(v[NM - 1][0], v[NM - 1][1], v[NM - 1][2], v[NM - 1][3]);
+      float* q = p.part + (int64_t)split * p.part_sstride + (G.row0 + r) * p.part_ld + n0 + cc;
+#pragma unroll
+      for (int c = 0; c < CPT; c += 4) {
+        *(float4*)(q + c) = make_float4(v[0][c], v[0][c + 1], v[0][c + 2], v[0][c + 3]);
+        *(float4*)(q + p.ldh + c) = make_float4(v[NM - 1][c], v[NM - 1][c + 1], v[NM - 1][c + 2], v[NM - 1][c + 3]);
+      }
     }
     return;
   }
   if (p.ks > 1) {
     // fp32 partials with device-scope relaxed stores (coherent across the XCDs' L2s); the last
     // split to arrive adds them in split order
-    auto pcol = [&](int m, int c) { return (GATED ? (int64_t)m * p.ldh : 0) + n0 + c4 + c; };
+    auto pcol = [&](int m, int c) { return (GATED ? (int64_t)m * p.ldh : 0) + n0 + cc + c; };
     float* mine_part = p.part + (int64_t)split * p.part_sstride;
     if (mine)
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < CPT; ++c)
           __hip_atomic_store(&mine_part[(G.row0 + r) * p.part_ld + pcol(m, c)], v[m][c], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores are complete
@@ -285,7 +332,7 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < CPT; ++c) {
           const int64_t at = (G.row0 + r) * p.part_ld + pcol(m, c);
           float sum = 0.f;
           for (int sp = 0; sp < p.ks; ++sp)
@@ -295,17 +342,32 @@ __global__ void __launch_bounds__(256, 2) ffn_skinny_kernel(SkinnyArgs p) {
           v[m][c] = sum;
         }
   }
-  if (!mine) return;
-  uint2 o;
-  if (GATED) {
-    o.x = pack_bf16x2(silu_f32(v[0][0]) * v[NM - 1][0], silu_f32(v[0][1]) * v[NM - 1][1]);
-    o.y = pack_bf16x2(silu_f32(v[0][2]) * v[NM - 1][2], silu_f32(v[0][3]) * v[NM - 1][3]);
-    *(uint2*)(p.out + (G.row0 + r) * p.ldh + n0 + c4) = o;
-  } else {
-    o.x = pack_bf16x2(v[0][0], v[0][1]);
-    o.y = pack_bf16x2(v[0][2], v[0][3]);
-    *(uint2*)(p.out + (G.row0 + r) * p.d + n0 + c4) = o;
+  if (!GATED && p.fout) {
+    // Y rows with device-scope stores; the last group to finish this column block (by the
+    // counter, after every thread's stores completed) then writes the block's output columns
+    if (mine) {
+      uint32_t* q = (uint32_t*)(p.out + (G.row0 + r) * p.d + n0 + cc);
+#pragma unroll
+      for (int c = 0; c < CPT; c += 2)
+        __hip_atomic_store(q + c / 2, pack_bf16x2(v[0][c], v[0][c + 1]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(&p.ccnt[cb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               *p.tile_count - 1;
+    __syncthreads();
+    if (s_last) combine_columns(p, n0);
+    return;
   }
+  if (!mine) return;
+  uint32_t o[CPT / 2];
+#pragma unroll
+  for (int c = 0; c < CPT; c += 2)
+    o[c / 2] = GATED ? pack_bf16x2(silu_f32(v[0][c]) * v[NM - 1][c], silu_f32(v[0][c + 1]) * v[NM - 1][c + 1])
+                     : pack_bf16x2(v[0][c], v[0][c + 1]);
+  bf16_t* dst = p.out + (G.row0 + r) * (GATED ? (int64_t)p.ldh : (int64_t)p.d) + n0 + cc;
+  *(uint2*)dst = make_uint2(o[0], o[1]);
 }
 
 template <int R>
@@ -329,8 +391,8 @@ void launch_pair(const SkinnyArgs& a1, const SkinnyArgs& a2, unsigned grid1, uns
 hipError_t launch_ffn_skinny(const moe_dims& dm, const Layout& L, const FfnPlan& P, const void* x,
                              const int32_t* offsets, const int32_t* sorted_token, const void* wg, const void* wu,
                              const void* wd, const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
-                             hipStream_t s, const Prof* prof) {
-  SkinnyArgs a;
+                             hipStream_t s, const Prof* prof, CombineFuse* combine) {
+  SkinnyArgs a{};
   a.offsets = offsets;
   a.sorted_token = sorted_token;
   a.tile_group = (const int32_t*)(ws + L.tile_group);
@@ -375,6 +437,16 @@ hipError_t launch_ffn_skinny(const moe_dims& dm, const Layout& L, const FfnPlan&
   a2.part_ld = P.part_cols2;
   a2.part_sstride = L.rows_total * P.part_cols2;
   a2.cnt = cnt + L.ffn_cnt_each;
+  if (combine && dm.T <= 2) {
+    // the gate/up product uses no arrival counters: the first bank (zeroed for every listed
+    // tile, at least one column block's worth) holds one per column block of the output
+    a2.fout = (bf16_t*)combine->out;
+    a2.slot_of = combine->slot_of;
+    a2.topk_w = combine->topk_w;
+    a2.resid = (const bf16_t*)combine->residual;
+    a2.ccnt = cnt;
+    combine->done = true;
+  }
   const unsigned grid1 = (unsigned)(max_mt * P.cb1 * P.ks1);
   const unsigned grid2 = (unsigned)(max_mt * P.cb2 * P.ks2);
   hipError_t e = hipSuccess;

@@ -160,7 +160,8 @@ Layout make_layout(const moe_dims& dm) {
   const FfnPlan P = ffn_plan(dm);
   size_t part = 0;
   if (P.s1 > 1) part = (size_t)P.s1 * L.rows_total * P.part_cols1 * 4;
-  if (P.skinny && P.ks1 > 1) part = std::max(part, (size_t)P.ks1 * L.rows_total * P.part_cols1 * 4);
+  // (gate/up partial rows for at least 8 splits: the FP8 skinny product sizes its split by them)
+  if (P.skinny) part = std::max(part, (size_t)std::max(P.ks1, 8) * L.rows_total * P.part_cols1 * 4);
   if (P.skinny && P.ks2 > 1) part = std::max(part, (size_t)P.ks2 * L.rows_total * P.part_cols2 * 4);
   L.ffn_part = take(part);
   // arrival counters of the skinny down product's K split (last-arriver sum), one per
@@ -400,13 +401,15 @@ moe_status forward_rows(const moe_dims& dm, const Layout& L, const void* xin, co
     e = launch_permute(dm, L, idx, offsets, sorted, slot, w, stream, !fp8);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/permute");
   if ((e = prof.end(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
+  CombineFuse fuse{out, slot, tw, residual, false};
   if (fp8)
     e = launch_grouped_ffn_fp8(dm, L, xin, offsets, sorted, *fp8, y, w, stream, &prof);
   else
-    e = launch_grouped_ffn(dm, L, xin, offsets, sorted, wg, wu, wd, wg_s, wu_s, wd_s, y, w, stream, &prof, true);
+    e = launch_grouped_ffn(dm, L, xin, offsets, sorted, wg, wu, wd, wg_s, wu_s, wd_s, y, w, stream, &prof, true,
+                           &fuse);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/grouped_ffn");
   if ((e = prof.begin(MOE_KERNEL_COMBINE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
-  e = launch_combine(dm, y, slot, tw, residual, out, stream);
+  if (!fuse.done) e = launch_combine(dm, y, slot, tw, residual, out, stream);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
   if ((e = prof.end(MOE_KERNEL_COMBINE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
   return MOE_OK;

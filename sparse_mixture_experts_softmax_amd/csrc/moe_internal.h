@@ -48,6 +48,15 @@ constexpr int kF32BM = 64;             // fp32 grouped GEMM tile rows
 constexpr int kF32BN = 64;             // fp32 grouped GEMM tile columns
 constexpr int kSkinnyMaxT = 2;         // skinny grouped GEMMs up to this many tokens
 constexpr int kSkinnyMaxKC = 2048;     // skinny grouped GEMMs: most K rows per split
+// skinny grouped GEMMs (256-column blocks, 512-byte weight rows), gate/up (1) and down (2): bytes
+// of one weight matrix per LDS stage (16 and 32 rows), stages in the ring, and the workgroups the
+// K split aims at (two per CU: all resident at once)
+constexpr int kSkinnyMat1 = 8192;
+constexpr int kSkinnyS1 = 4;
+constexpr int kSkinnyMat2 = 16384;
+constexpr int kSkinnyS2 = 4;
+constexpr int kSkinnyWG1 = 512;
+constexpr int kSkinnyWG2 = 512;
 
 // ------------------------------------------------------------------------------------------
 // workspace layout: a pure function of the dims
@@ -246,22 +255,35 @@ hipError_t launch_router_stats(const moe_dims& dm, const Layout& L, const int32_
 hipError_t launch_permute(const moe_dims& dm, const Layout& L, const int32_t* topk_idx, int32_t* offsets,
                           int32_t* sorted_token, int32_t* slot_of, char* ws, hipStream_t s, bool with_tiles = false);
 
+// The combine a forward may hand to the grouped GEMMs: with one or two tokens the skinny down
+// product's last workgroup per column block sums the expert rows into `out` (combine_kernel's
+// arithmetic, same order) and sets `done`, so that no combine launch follows.
+struct CombineFuse {
+  void* out;
+  const int32_t* slot_of;
+  const float* topk_w;
+  const void* residual;  // the block's input row added last, or null
+  bool done;
+};
+
 hipError_t launch_grouped_ffn(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
                               const int32_t* sorted_token, const void* wg, const void* wu, const void* wd,
                               const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
-                              hipStream_t s, const Prof* prof = nullptr, bool tiles_ready = false);
+                              hipStream_t s, const Prof* prof = nullptr, bool tiles_ready = false,
+                              CombineFuse* combine = nullptr);
 
 // gate/up product with K split: H rows from the splits' fp32 partials (gate at column c, up at
 // ldh + c of part[split][row], row pitch part_ld), added in split order, then silu(gate) * up
 hipError_t launch_gate_up_finish(const float* part, int64_t sstride, int64_t part_ld, int ks, int64_t Tk,
                                  int64_t rows_total, int I, int Is, int ldh, bf16_t* H, hipStream_t s);
 
-// few tokens (plan.skinny): both products on the vector ALUs with the weights streamed by plain
-// 16-byte loads; tile list and counters as for launch_grouped_ffn
+// few tokens (plan.skinny): both products on the vector ALUs with the weights streamed into an
+// LDS ring by DMA; tile list and counters as for launch_grouped_ffn; with `combine`, the down
+// product also writes the block's output
 hipError_t launch_ffn_skinny(const moe_dims& dm, const Layout& L, const FfnPlan& P, const void* x,
                              const int32_t* offsets, const int32_t* sorted_token, const void* wg, const void* wu,
                              const void* wd, const void* wg_s, const void* wu_s, const void* wd_s, void* y, char* ws,
-                             hipStream_t s, const Prof* prof);
+                             hipStream_t s, const Prof* prof, CombineFuse* combine);
 
 // names of the grouped GEMM kernels these dims launch (static strings)
 const char* ffn_kernel_name(const moe_dims& dm, bool gate_up);

@@ -379,6 +379,9 @@ BLOCK_CASES = [
     syn.CONFIGS["tiny"],
     syn.MoEConfig("block_ragged", T=300, d=264, E=40, k=3, I=136, Is=72, dtype=syn.BF16, seed=12),
     syn.MoEConfig("block_mid_shape", T=700, d=2048, E=256, k=8, I=512, Is=512, dtype=syn.BF16, seed=13),
+    # one and two tokens: the skinny products, the residual added by the down product's last workgroups
+    syn.MoEConfig("block_one_token", T=1, d=2048, E=128, k=8, I=512, Is=512, dtype=syn.BF16, seed=17),
+    syn.MoEConfig("block_two_tokens", T=2, d=1024, E=40, k=5, I=768, Is=256, dtype=syn.BF16, seed=18),
 ]
 
 
@@ -404,11 +407,17 @@ def test_block_forward_matches_oracle(torch, cfg):
     _say(cfg.name, st)
 
 
-def test_block_steps_compose_bit_for_bit(torch):
+# one and two tokens: the skinny down product writes the block's output itself (the combine with
+# the residual folded into its last workgroup per column block)
+@pytest.mark.parametrize("cfg", [
+    syn.MoEConfig("block_steps", T=333, d=512, E=24, k=4, I=256, Is=128, dtype=syn.BF16, seed=14),
+    syn.MoEConfig("block_steps_T1", T=1, d=2048, E=96, k=6, I=512, Is=512, dtype=syn.BF16, seed=15),
+    syn.MoEConfig("block_steps_T2", T=2, d=1024, E=48, k=8, I=256, Is=768, dtype=syn.BF16, seed=16),
+], ids=lambda c: c.name)
+def test_block_steps_compose_bit_for_bit(torch, cfg):
     # rmsnorm -> router -> dispatch -> experts -> combine with the residual == the one-call block
     import sparse_mixture_experts_softmax_amd as moe
     from moe_testlib import to_device
-    cfg = syn.MoEConfig("block_steps", T=333, d=512, E=24, k=4, I=256, Is=128, dtype=syn.BF16, seed=14)
     h = host_inputs(cfg)
     dev = device_from_host(h, cfg)
     dg = to_device(syn.host_gamma(cfg), torch_dtype(cfg))
@@ -592,6 +601,8 @@ GRAPH_CASES = [
     ("bf16_mid_width", syn.MoEConfig("graph_mid", T=300, d=2048, E=64, k=8, I=512, Is=512, dtype=syn.BF16, seed=72)),
     ("fp8", syn.MoEConfig("graph_fp8", T=40, d=1024, E=32, k=4, I=256, Is=256, dtype=syn.BF16, seed=73)),
     ("block", syn.MoEConfig("graph_block", T=200, d=512, E=24, k=4, I=256, Is=128, dtype=syn.BF16, seed=74)),
+    ("block_one_token", syn.MoEConfig("graph_block_T1", T=1, d=2048, E=64, k=8, I=512, Is=512, dtype=syn.BF16,
+                                      seed=78)),
 ]
 
 
@@ -603,14 +614,14 @@ def test_forward_replays_in_a_hip_graph(torch, kind, cfg):
     h = host_inputs(cfg)
     dev = device_from_host(h, cfg)
     dims = moe.dims_for(dev["x"], dev["w_router"], dev["wg"], dev["wg_s"], cfg.k, True)
-    gamma = to_device(syn.host_gamma(cfg), torch_dtype(cfg)) if kind == "block" else None
+    gamma = to_device(syn.host_gamma(cfg), torch_dtype(cfg)) if kind.startswith("block") else None
     experts = moe.Fp8Experts(dev["wg"], dev["wu"], dev["wd"], dev["wg_s"], dev["wu_s"], dev["wd_s"]) \
         if kind == "fp8" else None
 
     def call(x, ws):
         if kind == "fp8":
             return moe.moe_forward_fp8(x, dev["w_router"], experts, cfg.k, router_bias=dev["bias"], ws=ws, dims=dims)
-        if kind == "block":
+        if kind.startswith("block"):
             return moe.moe_forward_block(x, gamma, dev["w_router"], dev["wg"], dev["wu"], dev["wd"], dev["wg_s"],
                                          dev["wu_s"], dev["wd_s"], cfg.k, ws=ws, dims=dims)
         return moe.moe_forward(x, dev["w_router"], dev["wg"], dev["wu"], dev["wd"], dev["wg_s"], dev["wu_s"],
