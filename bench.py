@@ -367,7 +367,7 @@ def _csv_rows(directory, suffix):
 
 def _short_kernel_name(name):
     """A kernel's demangled name without return type, argument list and clone suffix."""
-    name = name.replace(" [clone .kd]", "").strip()
+    name = name.replace(" [clone .kd]", "").replace("(anonymous namespace)::", "").replace("moe::", "").strip()
     if name.startswith("void "):
         name = name[5:]
     depth, cut = 0, len(name)

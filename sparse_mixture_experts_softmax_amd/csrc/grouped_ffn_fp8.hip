@@ -311,7 +311,10 @@ __global__ void __launch_bounds__(256, 2) ffn_fp8_stream_kernel(Fp8Args p) {
 // split sit in LDS as fp32. Column scales are powers of two, so scaling each split's sums is
 // exact: the gate/up product's splits go out scaled, as fp32 partial rows that
 // gate_up_finish_kernel adds in split order and finishes with silu * up (H directly with a single
-// split); the down product runs unsplit (K = I <= 2048) and writes Y.
+// split); the down product runs unsplit (K = I <= 2048) and writes Y -- in a forward, with
+// device-scope stores, and the last group to finish each panel then performs the combine for its
+// columns. (A variant that streamed the code tiles into an LDS ring by DMA, as the bf16 skinny
+// kernels do, measured slower here: one-token layer 0.132 -> 0.137 ms.)
 // ------------------------------------------------------------------------------------------
 struct Fp8SkinnyArgs {
   const bf16_t* a_src;  // gate/up: x [T, d]; down: H [rows_total, ldh]
@@ -334,6 +337,13 @@ struct Fp8SkinnyArgs {
   int ks, kc;  // K splits, K rows per split (multiple of 32, <= kSkinnyMaxKC)
   float* part;  // gate/up with ks > 1: scaled fp32 partial rows part[split][row][part_ld]
   int64_t part_ld, part_sstride;
+  // down product with the combine (fout non-null): the block's output rows [T, d], the routing,
+  // the residual rows (or null), and one arrival counter per panel, zero on entry
+  bf16_t* fout;
+  const int32_t* slot_of;
+  const float* topk_w;
+  const bf16_t* resid;
+  int32_t* ccnt;
 };
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -357,6 +367,7 @@ __global__ void __launch_bounds__(256, 2) ffn_fp8_skinny_kernel(Fp8SkinnyArgs p)
   constexpr int NM = GATED ? 2 : 1;  // code matrices
   constexpr int KU = 8;              // code tiles in flight per thread and matrix
   __shared__ __attribute__((aligned(16))) float s_a[R][kSkinnyMaxKC];
+  __shared__ int s_last;
   const int tid = threadIdx.x;
 
   const int per_tile = p.n_cblk * p.ks;
@@ -494,8 +505,31 @@ __global__ void __launch_bounds__(256, 2) ffn_fp8_skinny_kernel(Fp8SkinnyArgs p)
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[m][r] += __shfl_xor(acc[m][r], 1, 64);
-  if (tid & 1) return;
   const int n = n0 + col;
+  if (!GATED && p.fout) {
+    // Y with device-scope stores, two columns per store (thread 4j holds columns 2j and 2j + 1);
+    // the last group to finish this panel (by the counter, after every thread's stores
+    // completed) then performs the combine for its 128 columns
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float y0 = acc[0][r] * S0[n];
+      const float y1 = __shfl_down(y0, 2, 64);
+      if ((tid & 3) == 0 && r < rows)
+        __hip_atomic_store((uint32_t*)(p.out + (G.row0 + r) * (int64_t)p.d + n), pack_bf16x2(y0, y1),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(&p.ccnt[cb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               *p.tile_count - 1;
+    __syncthreads();
+    const int t = tid >> 6;  // 64 column pairs per token
+    if (s_last && t < p.T)
+      combine_pair(p.out, p.fout, p.slot_of, p.topk_w, p.resid, p.T, p.d, p.k, p.Is > 0, t, n0 + 2 * (tid & 63));
+    return;
+  }
+  if (tid & 1) return;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (r >= rows) break;
@@ -617,10 +651,11 @@ int fp8_skinny_splits(const moe_dims& dm, const Layout& L) {
   return (int)((dm.d + kc - 1) / kc);
 }
 
-// one or two tokens: the skinny code streams; the down product runs unsplit
+// one or two tokens: the skinny code streams; the down product runs unsplit (and, with `combine`,
+// also writes the block's output)
 hipError_t launch_fp8_skinny(const moe_dims& dm, const Layout& L, int ks, const void* x, const int32_t* offsets,
                              const int32_t* sorted_token, const Fp8Weights& W, void* y, char* ws, hipStream_t s,
-                             const Prof* prof) {
+                             const Prof* prof, CombineFuse* combine) {
   const int has_shared = dm.I_shared > 0 ? 1 : 0;
   const int64_t Tk = dm.T * dm.k;
   const int64_t groups = (Tk < dm.E ? Tk : dm.E) + has_shared;  // tiles: one per group with rows
@@ -683,6 +718,16 @@ hipError_t launch_fp8_skinny(const moe_dims& dm, const Layout& L, int ks, const 
   a.ks = 1;
   a.kc = L.ldh;
   a.part = nullptr;
+  if (combine) {
+    // one arrival counter per 128-column panel: the first bank of the split-K counters, which the
+    // gate/up product does not use (the layout sizes and the tile list zeroes at least d / 128)
+    a.fout = (bf16_t*)combine->out;
+    a.slot_of = combine->slot_of;
+    a.topk_w = combine->topk_w;
+    a.resid = (const bf16_t*)combine->residual;
+    a.ccnt = (int32_t*)(ws + L.ffn_cnt);
+    combine->done = true;
+  }
   if ((e = prof->begin(MOE_KERNEL_FFN_DOWN, s)) != hipSuccess) return e;
   const dim3 grid2((unsigned)(groups * a.n_cblk));
   if (dm.T <= 1) hipLaunchKernelGGL((ffn_fp8_skinny_kernel<false, 1>), grid2, dim3(256), 0, s, a);
@@ -704,7 +749,7 @@ const char* ffn_fp8_kernel_name(const moe_dims& dm, bool gate_up) {
 
 hipError_t launch_grouped_ffn_fp8(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
                                   const int32_t* sorted_token, const Fp8Weights& W, void* y, char* ws, hipStream_t s,
-                                  const Prof* prof) {
+                                  const Prof* prof, CombineFuse* combine) {
   const Prof none;
   if (!prof) prof = &none;
   // five stages of 16 KB (80 KB of LDS, still two workgroups per CU): with the non-temporal code
@@ -716,7 +761,8 @@ hipError_t launch_grouped_ffn_fp8(const moe_dims& dm, const Layout& L, const voi
   hipError_t e = launch_build_tiles(dm, L, offsets, ws, s, SBM);
   if (e != hipSuccess) return e;
   const int ks_skinny = fp8_skinny_splits(dm, L);
-  if (ks_skinny > 0) return launch_fp8_skinny(dm, L, ks_skinny, x, offsets, sorted_token, W, y, ws, s, prof);
+  if (ks_skinny > 0)
+    return launch_fp8_skinny(dm, L, ks_skinny, x, offsets, sorted_token, W, y, ws, s, prof, combine);
   const int has_shared = dm.I_shared > 0 ? 1 : 0;
   const int64_t Tk = dm.T * dm.k;
   const int64_t max_mt = Tk / SBM + (Tk < dm.E ? Tk : dm.E) + (has_shared ? dm.T / SBM + 1 : 0);

@@ -51,52 +51,13 @@ struct SkinnyArgs {
   int32_t* ccnt;
 };
 
-// Columns n0 .. n0 + 255 of the block's output for every token (T <= 2), as combine_kernel sums
-// them: out = sum_j w[t, j] * y[slot_of[t k + j]] in the order j = 0 .. k-1 (fp32, fused
-// multiply-add from zero), then the shared expert's row, then the residual row, rounded once.
-// The expert rows were stored by other workgroups with device-scope stores; they are read the
-// same way. Thread (t, c): token t = tid / 128, columns n0 + 2c and n0 + 2c + 1.
+// Columns n0 .. n0 + 255 of the block's output for every token (T <= 2): thread (t, c), token
+// t = tid / 128, columns n0 + 2c and n0 + 2c + 1.
 __device__ __forceinline__ void combine_columns(const SkinnyArgs& p, int n0) {
   const int t = threadIdx.x >> 7;
   if (t >= p.T) return;
-  const int64_t col = n0 + 2 * (threadIdx.x & 127);
-  const int k = p.k;
-  uint32_t yv[kMaxK];
-  float w[kMaxK];
-  bool on[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    on[j] = false;
-    if (j < k) {
-      const int slot = p.slot_of[t * k + j];
-      w[j] = p.topk_w[t * k + j];
-      on[j] = slot >= 0;
-      if (on[j])
-        yv[j] = __hip_atomic_load((const uint32_t*)(p.out + (int64_t)slot * p.d + col), __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  uint32_t ys = 0, rv = 0;
-  if (p.Is > 0)
-    ys = __hip_atomic_load((const uint32_t*)(p.out + (p.T * k + t) * p.d + col), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-  if (p.resid) rv = *(const uint32_t*)(p.resid + t * p.d + col);
-  float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    if (on[j]) {
-      a0 = fmaf(w[j], bf16lo_to_f32(yv[j]), a0);
-      a1 = fmaf(w[j], bf16hi_to_f32(yv[j]), a1);
-    }
-  if (p.Is > 0) {
-    a0 += bf16lo_to_f32(ys);
-    a1 += bf16hi_to_f32(ys);
-  }
-  if (p.resid) {
-    a0 += bf16lo_to_f32(rv);
-    a1 += bf16hi_to_f32(rv);
-  }
-  *(uint32_t*)(p.fout + t * p.d + col) = pack_bf16x2(a0, a1);
+  combine_pair(p.out, p.fout, p.slot_of, p.topk_w, p.resid, p.T, p.d, p.k, p.Is > 0, t,
+               n0 + 2 * (threadIdx.x & 127));
 }
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));

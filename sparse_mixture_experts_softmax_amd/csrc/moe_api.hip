@@ -166,7 +166,9 @@ Layout make_layout(const moe_dims& dm) {
   L.ffn_part = take(part);
   // arrival counters of the skinny down product's K split (last-arriver sum), one per
   // (group, column block)
-  const int64_t per_tile = P.skinny ? std::max(P.cb1, P.cb2) : 0;
+  // (at one or two tokens at least d / 128: the FP8 skinny down product's per-panel counters)
+  int64_t per_tile = P.skinny ? std::max(P.cb1, P.cb2) : 0;
+  if (T >= 1 && T <= kSkinnyMaxT) per_tile = std::max<int64_t>(per_tile, dm.d / 128);
   L.ffn_cnt_each = L.max_tiles * per_tile;
   L.ffn_cnt_per_tile = (int)per_tile;
   L.ffn_cnt = take((size_t)2 * L.ffn_cnt_each * 4);
@@ -403,7 +405,7 @@ moe_status forward_rows(const moe_dims& dm, const Layout& L, const void* xin, co
   if ((e = prof.end(MOE_KERNEL_PERMUTE, stream)) != hipSuccess) return hip_fail(e, "moe_forward/profile");
   CombineFuse fuse{out, slot, tw, residual, false};
   if (fp8)
-    e = launch_grouped_ffn_fp8(dm, L, xin, offsets, sorted, *fp8, y, w, stream, &prof);
+    e = launch_grouped_ffn_fp8(dm, L, xin, offsets, sorted, *fp8, y, w, stream, &prof, &fuse);
   else
     e = launch_grouped_ffn(dm, L, xin, offsets, sorted, wg, wu, wd, wg_s, wu_s, wd_s, y, w, stream, &prof, true,
                            &fuse);

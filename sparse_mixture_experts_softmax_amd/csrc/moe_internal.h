@@ -58,6 +58,51 @@ constexpr int kSkinnyS2 = 4;
 constexpr int kSkinnyWG1 = 512;
 constexpr int kSkinnyWG2 = 512;
 
+// The combine for one token t and the two output columns col, col + 1, as combine_kernel sums
+// them: out = sum_j w[t, j] * y[slot_of[t k + j]] in the order j = 0 .. k-1 (fp32, fused
+// multiply-add from zero), then the shared expert's row T k + t, then the residual row, rounded
+// once. Used by the few-token down products that perform the combine themselves: the expert rows
+// y were stored by other workgroups with device-scope stores, and are read the same way.
+__device__ inline void combine_pair(const bf16_t* y, bf16_t* out, const int32_t* slot_of, const float* topk_w,
+                                    const bf16_t* resid, int64_t T, int d, int k, bool has_shared, int64_t t,
+                                    int64_t col) {
+  uint32_t yv[kMaxK];
+  float w[kMaxK];
+  bool on[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    on[j] = false;
+    if (j < k) {
+      const int slot = slot_of[t * k + j];
+      w[j] = topk_w[t * k + j];
+      on[j] = slot >= 0;
+      if (on[j])
+        yv[j] = __hip_atomic_load((const uint32_t*)(y + (int64_t)slot * d + col), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  uint32_t ys = 0, rv = 0;
+  if (has_shared)
+    ys = __hip_atomic_load((const uint32_t*)(y + (T * k + t) * d + col), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (resid) rv = *(const uint32_t*)(resid + t * d + col);
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (on[j]) {
+      a0 = fmaf(w[j], bf16lo_to_f32(yv[j]), a0);
+      a1 = fmaf(w[j], bf16hi_to_f32(yv[j]), a1);
+    }
+  if (has_shared) {
+    a0 += bf16lo_to_f32(ys);
+    a1 += bf16hi_to_f32(ys);
+  }
+  if (resid) {
+    a0 += bf16lo_to_f32(rv);
+    a1 += bf16hi_to_f32(rv);
+  }
+  *(uint32_t*)(out + t * d + col) = pack_bf16x2(a0, a1);
+}
+
 // ------------------------------------------------------------------------------------------
 // workspace layout: a pure function of the dims
 // ------------------------------------------------------------------------------------------
@@ -308,7 +353,7 @@ struct Fp8Weights {
 bool fp8_shape_ok(const moe_dims& dm);
 hipError_t launch_grouped_ffn_fp8(const moe_dims& dm, const Layout& L, const void* x, const int32_t* offsets,
                                   const int32_t* sorted_token, const Fp8Weights& W, void* y, char* ws, hipStream_t s,
-                                  const Prof* prof = nullptr);
+                                  const Prof* prof = nullptr, CombineFuse* combine = nullptr);
 // w [batch, K, N] (dtype) -> q [batch, N, K] e4m3, scale [batch, N]
 hipError_t launch_quantize_fp8(const void* w, int dtype, int64_t batch, int K, int N, uint8_t* q, float* scale,
                                hipStream_t s);
