@@ -452,16 +452,16 @@ router_topk_kernel(const float* __restrict__ part, int splits, const float* __re
 // rule); the candidates ranked below k+1 are the token's picks, in order. The softmax normaliser
 // is summed per wavefront, then over the four in order.
 struct TopkGroupLds {
-  float c_v[4 * (kMaxK + 1)];  // the four wavefronts' candidate lists
-  int c_i[4 * (kMaxK + 1)];
+  uint2 cand[4 * (kMaxK + 1)];  // the four wavefronts' candidate lists: (logit bits, expert)
   float f_v[kMaxK + 1];  // the token's picks by rank (k + 1 when k < E)
   int f_i[kMaxK + 1];
   float s_z[4];
 };
 
 // Token t on the 256 threads r = 0 .. 255 of a group, B split loads per logit in flight. Every
-// thread of the workgroup must call it (it holds three workgroup barriers); `active` false leaves
-// the group's outputs untouched. Leaves the picks in sm.f_i / sm.f_v.
+// thread of the workgroup must call it (it holds three workgroup barriers); a group with `active`
+// false only meets the barriers (its wavefronts would otherwise take issue slots from the active
+// groups' on the same SIMDs) and leaves its outputs untouched. Leaves the picks in sm.f_i / sm.f_v.
 template <int NJ2, int B>
 __device__ __forceinline__ void topk_wide_token(const float* __restrict__ part, int splits,
                                                 const float* __restrict__ bias, int64_t T, int E, int k, int renorm,
@@ -503,7 +503,7 @@ __device__ __forceinline__ void topk_wide_token(const float* __restrict__ part, 
   float my_v = -INFINITY;
   int my_i = NONE;
 #pragma unroll 1
-  for (int rd = 0; rd < rounds; ++rd) {
+  for (int rd = 0; rd < (active ? rounds : 0); ++rd) {
     float lv = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NJ2; ++j)
@@ -522,43 +522,53 @@ __device__ __forceinline__ void topk_wide_token(const float* __restrict__ part, 
       my_i = bi;
     }
   }
-  if (lane < rounds) {
-    sm.c_v[wave * rounds + lane] = my_v;
-    sm.c_i[wave * rounds + lane] = my_i;
-  }
+  if (active && lane < rounds) sm.cand[wave * rounds + lane] = make_uint2(__float_as_uint(my_v), (uint32_t)my_i);
   __syncthreads();
 
   // rank of candidate c among the nc = 4 * rounds: the candidates with a larger logit, or an equal
   // logit and a lower expert index (NONE entries, equal among themselves, by position). The ranks
   // are a permutation of 0 .. nc-1, and the ones below `rounds` are the token's picks in order:
   // every valid expert outside the lists is beaten by `rounds` candidates of its own wavefront.
-  {
-    const int nc = 4 * rounds;  // <= 68: one candidate per thread
-    const int c = r;
-    const float cv = c < nc ? sm.c_v[c] : -INFINITY;
-    const int ci = c < nc ? sm.c_i[c] : NONE;
-    int rank = 0;
-#pragma unroll 4
-    for (int c2 = 0; c2 < nc; ++c2) {
-      const float v2 = sm.c_v[c2];
-      const int i2 = sm.c_i[c2];
-      rank += (v2 > cv || (v2 == cv && (i2 < ci || (i2 == ci && c2 < c)))) ? 1 : 0;
+  // Four threads per candidate (a quad of lanes): thread (c, w2) counts the candidates of
+  // wavefront w2's list that beat c, all of that list's reads in flight together, and the quad
+  // adds its four counts with DPP lane moves. (One thread per candidate reading all 4 (k + 1)
+  // entries in turn took ~4 us at k = 10.)
+  const int nc = 4 * rounds;  // <= 68 candidates, <= 272 threads: two passes at most
+  if (active)
+    for (int q = r; q < 4 * nc; q += 256) {
+      const int c = q >> 2, w2 = q & 3;
+      const uint2 me = sm.cand[c];
+      const float cv = __uint_as_float(me.x);
+      const int ci = (int)me.y;
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < kMaxK + 1; ++u)
+        if (u < rounds) {
+          const int c2 = w2 * rounds + u;
+          const uint2 o = sm.cand[c2];
+          const float v2 = __uint_as_float(o.x);
+          const int i2 = (int)o.y;
+          cnt += (v2 > cv || (v2 == cv && (i2 < ci || (i2 == ci && c2 < c)))) ? 1 : 0;
+        }
+      cnt += __builtin_amdgcn_update_dpp(0, cnt, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+      cnt += __builtin_amdgcn_update_dpp(0, cnt, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+      if (w2 == 0 && cnt < rounds) {
+        sm.f_v[cnt] = cv;
+        sm.f_i[cnt] = ci;
+      }
     }
-    if (c < nc && rank < rounds) {
-      sm.f_v[rank] = cv;
-      sm.f_i[rank] = ci;
-    }
-  }
   __syncthreads();
 
   // softmax over all E logits: per-wavefront sums, then the four in order
-  const float m = sm.f_v[0];
-  float z = 0.f;
+  float m = 0.f, z = 0.f;
+  if (active) {
+    m = sm.f_v[0];
 #pragma unroll
-  for (int j = 0; j < NJ2; ++j)
-    if (256 * j + 64 * wave + lane < E) z += expf(v[j] - m);
-  z = wave_sum(z);
-  if (lane == 0) sm.s_z[wave] = z;
+    for (int j = 0; j < NJ2; ++j)
+      if (256 * j + 64 * wave + lane < E) z += expf(v[j] - m);
+    z = wave_sum(z);
+    if (lane == 0) sm.s_z[wave] = z;
+  }
   __syncthreads();
   if (!active) return;
   z = ((sm.s_z[0] + sm.s_z[1]) + sm.s_z[2]) + sm.s_z[3];
@@ -607,7 +617,9 @@ route_dispatch_kernel(const float* __restrict__ part, int splits, const float* _
   __shared__ int s_w[17];
   const int tid = threadIdx.x;
   const int g = tid >> 8;
-  topk_wide_token<NJ2, NJ2 >= 4 ? 8 : 16>(part, splits, bias, T, E, k, renorm, g, g < T, tid & 255, sm[g], topk_idx, topk_w, topk_gap,
+  // (E <= 256: all 32 split partials in flight at once, one memory round trip; more registers
+  // per logit would spill at 1024 threads)
+  topk_wide_token<NJ2, NJ2 >= 4 ? 8 : NJ2 == 2 ? 16 : 32>(part, splits, bias, T, E, k, renorm, g, g < T, tid & 255, sm[g], topk_idx, topk_w, topk_gap,
                        nullptr);
   __syncthreads();  // every group's picks in LDS
 
@@ -615,7 +627,8 @@ route_dispatch_kernel(const float* __restrict__ part, int splits, const float* _
   int c = 0;
   if (tid < E)
     for (int t = 0; t < nt; ++t)
-      for (int j = 0; j < k; ++j) c += sm[t].f_i[j] == tid ? 1 : 0;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) c += (j < k && sm[t].f_i[j] == tid) ? 1 : 0;
   const int excl = block_exclusive_scan_1024t(c, s_w, &s_w[16]);
   if (tid < E) {
     offsets[tid] = excl;
