@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include "moe.h"
+#include "moe_internal.h"
 
 static int failures = 0;
 #define CHECK(cond, ...)              \
@@ -51,6 +52,27 @@ int main() {
         CHECK(st == MOE_OK, "workspace_size T=%lld d=%d E=%d: %s", (long long)T, s.d, s.E, moe_last_error());
         CHECK(bytes % 256 == 0, "workspace size %zu not a multiple of 256", bytes);
       }
+  // few-token plans: the skinny kernels stream whole LDS stages (16 gate/up or 32 down weight
+  // rows) of K splits that fit their A rows' room, and the counter banks hold a counter per
+  // column block of either product (and per FP8 panel of the output) for every listed tile
+  int skinny_plans = 0;
+  for (const Shape& s : shapes)
+    for (int64_t T : Ts) {
+      moe_dims m = dims(T, s.d, s.E, s.k, s.I, s.Is, MOE_BF16);
+      const moe::FfnPlan P = moe::ffn_plan(m);
+      if (!P.skinny) continue;
+      ++skinny_plans;
+      const moe::Layout L = moe::make_layout(m);
+      const int kr1 = moe::kSkinnyMat1 / 512, kr2 = moe::kSkinnyMat2 / 512;
+      CHECK(P.kc1 > 0 && P.kc1 % kr1 == 0 && P.kc1 <= moe::kSkinnyMaxKC, "skinny gate/up kc %d d=%d", P.kc1, s.d);
+      CHECK(P.kc2 > 0 && P.kc2 % kr2 == 0 && P.kc2 <= moe::kSkinnyMaxKC, "skinny down kc %d d=%d", P.kc2, s.d);
+      CHECK(s.d % kr1 == 0 && s.I % kr2 == 0 && s.Is % kr2 == 0, "skinny K not whole stages d=%d", s.d);
+      CHECK((int64_t)P.ks1 * P.kc1 >= s.d && (int64_t)(P.ks1 - 1) * P.kc1 < s.d, "gate/up splits %d x %d", P.ks1,
+            P.kc1);
+      CHECK(L.ffn_cnt_per_tile >= P.cb1 && L.ffn_cnt_per_tile >= P.cb2 && L.ffn_cnt_per_tile >= s.d / 128,
+            "counters per tile %d (cb %d %d, d %d)", L.ffn_cnt_per_tile, P.cb1, P.cb2, s.d);
+    }
+  CHECK(skinny_plans >= 8, "only %d skinny plans checked", skinny_plans);
   // workspace grows with T at a fixed shape
   {
     size_t prev = 0;
