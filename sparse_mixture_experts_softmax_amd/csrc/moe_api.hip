@@ -94,18 +94,23 @@ Layout make_layout(const moe_dims& dm) {
   const int64_t T = dm.T;
   const int64_t Tk = T * dm.k;
   const size_t esz = dm.dtype == MOE_F32 ? 4 : 2;
-  // Router. bf16 x with enough tokens: MFMA on 128 x 256 tiles over K' = 3d (W_r split into
-  // three bf16 parts). Otherwise fp32 vector ALUs on 64 x 64 tiles. Either way the K dimension
+  // Router. bf16 x with enough tokens: MFMA on 128 x 256 or 128 x 512 tiles over K' = 3d (W_r
+  // split into three bf16 parts). Otherwise fp32 vector ALUs on 64 x 64 tiles. Either way the K dimension
   // is split when the (token x expert) tiles alone would leave most of the 256 CUs idle.
   L.router_mfma = dm.dtype == MOE_BF16 && T >= 256 && dm.E % 256 == 0 && dm.d % 32 == 0 &&
                   (uint64_t)T * dm.d * 2 < (1ull << 32);
   int64_t splits, kchunk;
+  L.router_wn = 2;
   if (L.router_mfma) {
-    const int64_t base_tiles = ((T + 127) / 128) * (dm.E / 256);
+    // 128 x 512 tiles (one workgroup per CU) where the experts divide them: the long K' = 3d
+    // loop moves fewer L2 -> LDS bytes per FLOP than on 128 x 256 tiles
+    L.router_wn = dm.E % 512 == 0 ? 4 : 2;
+    const int64_t base_tiles = ((T + 127) / 128) * (dm.E / (128 * L.router_wn));
     const int64_t ksteps = 3 * (int64_t)dm.d / 32;
     // one workgroup per CU for few tiles (more splits only add partial sums for the top-k to
-    // read); two per CU (a second split) once the tiles alone cover half the CUs
-    const int64_t target = base_tiles >= 128 ? 512 : 256;
+    // read); with 128 x 256 tiles two per CU (a second split) once the tiles alone cover half
+    // the CUs
+    const int64_t target = L.router_wn == 2 && base_tiles >= 128 ? 512 : 256;
     splits = (target + base_tiles - 1) / base_tiles;
     if (splits > 8) splits = 8;
     if (splits > ksteps / 8) splits = ksteps / 8 > 0 ? ksteps / 8 : 1;
@@ -203,7 +208,9 @@ const char* moe_kernel_name(const moe_dims* dims, int32_t kernel, int32_t fp8) {
   const Layout L = make_layout(dm);
   switch (kernel) {
     case MOE_KERNEL_ROUTER:
-      return L.router_mfma ? "router_mfma_kernel" : dm.T <= 64 ? "router_small_kernel" : "router_logits_kernel";
+      return L.router_mfma ? (L.router_wn == 4 ? "router_mfma_kernel<4>" : "router_mfma_kernel<2>")
+             : dm.T <= 64  ? "router_small_kernel"
+                           : "router_logits_kernel";
     case MOE_KERNEL_PERMUTE:
       if (L.route_fused) return "route_dispatch_kernel";
       return L.nchunks == 1 ? "permute_one_chunk_kernel" : "permute_count_kernel";

@@ -108,6 +108,7 @@ __device__ inline void combine_pair(const bf16_t* y, bf16_t* out, const int32_t*
 // ------------------------------------------------------------------------------------------
 struct Layout {
   int router_mfma;      // 1: bf16 x with the 3-way bf16 split of W_r on MFMA; 0: fp32 vector ALUs
+  int router_wn;        // MFMA router: wave columns of its tile (2: 128 x 256, 4: 128 x 512)
   int router_splits;    // K splits of the router logits GEMM (partial sums summed by top-k)
   int router_kchunk;    // vector path: hidden rows per split; MFMA path: 32-wide K steps per split
   int64_t nchunks;      // permute chunks

@@ -57,40 +57,47 @@ router_split_kernel(const float* __restrict__ w, bf16_t* __restrict__ planes, in
   *(uint2*)(planes + 2 * n + i) = make_uint2(p2[0], p2[1]);
 }
 
-// Logits on MFMA: 128 tokens x 256 experts per workgroup, K' = 3d split into `splits` chunks of
-// `ksteps` 32-wide steps. grid = splits * token tiles * expert tiles.
-__global__ void __launch_bounds__(256, 2)
+// Logits on MFMA: 128 tokens x 128 WN experts per workgroup (the streaming tile of stream_gemm.h:
+// WN = 2, four wavefronts, three stages, two workgroups per CU; WN = 4, eight wavefronts, four
+// stages, one per CU, fewer L2 -> LDS bytes per FLOP on the long K' = 3d loop), K' split into
+// `splits` chunks of `ksteps` 32-wide steps. grid = splits * token tiles * expert tiles.
+template <int WN>
+__global__ void __launch_bounds__(128 * WN, WN == 2 ? 2 : 1)
 router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ planes, float* __restrict__ part,
                    int64_t T, int d, int E, int ksteps) {
   using namespace stream;
-  __shared__ __attribute__((aligned(1024))) char smem[3 * Geo<2>::STAGE];
+  using GEO = Geo<WN>;
+  constexpr int S = WN == 2 ? 3 : 4;
+  constexpr int COLS = 128 * WN;
+  constexpr int NT = 128 * WN;  // threads
+  __shared__ __attribute__((aligned(1024))) char smem[S * GEO::STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int n_et = E / 256;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int n_et = E / COLS;
   const int n_mt = (int)((T + 127) / 128);
   const int et = blockIdx.x % n_et;
   const int mt = (blockIdx.x / n_et) % n_mt;
   const int split = blockIdx.x / (n_et * n_mt);
   const int64_t t0 = (int64_t)mt * 128;
-  const int e0 = et * 256;
+  const int e0 = et * COLS;
   const int dk = d / 32;  // K steps per plane
   const int kt0 = split * ksteps;
   const int nk = min(ksteps, 3 * dk - kt0);
 
-  uint32_t a_off[Geo<2>::A_DMA];
+  uint32_t a_off[GEO::A_DMA];
 #pragma unroll
-  for (int i = 0; i < Geo<2>::A_DMA; ++i) {
-    const int64_t row = min(t0 + a_dma_row<2>(wave, i, lane), T - 1);
+  for (int i = 0; i < GEO::A_DMA; ++i) {
+    const int64_t row = min(t0 + a_dma_row<WN>(wave, i, lane), T - 1);
     a_off[i] = (uint32_t)(row * d * 2) + a_dma_chunk_bytes(lane);
   }
   const char* xb = uniform_ptr((const char*)x);
   auto a_base = [=](int kt) { return xb + ((kt0 + kt) % dk) * (SBK * 2); };
   const int64_t pitch = (int64_t)E * 2;
-  const char* pb = uniform_ptr((const char*)planes + (int64_t)(e0 + 128 * b_dma_block<2>(wave)) * 2 +
-                               ((int64_t)kt0 * SBK + b_dma_row0<2>(wave, 0)) * pitch);
+  const char* pb = uniform_ptr((const char*)planes + (int64_t)(e0 + 128 * b_dma_block<WN>(wave)) * 2 +
+                               ((int64_t)kt0 * SBK + b_dma_row0<WN>(wave, 0)) * pitch);
   auto b_base = [=](int kt, int i) { return pb + (int64_t)kt * SBK * pitch + i * 4 * pitch; };
   const uint32_t b_off = b_dma_lane_offset(lane, (uint32_t)pitch);
   int bcol[4];
@@ -100,14 +107,15 @@ router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ plan
 
   f32x16_t acc[2][4];
   zero(acc);
-  mainloop<2, 3>(nk, nl, (int)min<int64_t>(T - t0, 128), (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
+  mainloop<WN, S>(nk, nl, (int)min<int64_t>(T - t0, 128), (lds_char*)smem, a_base, a_off, b_base, b_off, bcol, acc);
 
   // Partial logits through LDS, 64 tile rows at a time (sub-tile u of both wave rows: tile rows
   // 64u .. 64u+63), so that each lane stores whole 16-byte runs of a row instead of single floats.
-  // Row pitch 1056 bytes: the rows r and r + 4 that the two lane halves write fall on disjoint
-  // banks.
-  constexpr int PITCH = 256 * 4 + 32;
-  static_assert(64 * PITCH <= 3 * Geo<2>::STAGE, "64 staged rows fit the LDS stages");
+  // Row pitch 4 COLS + 32 bytes: the rows r and r + 4 that the two lane halves write fall on
+  // disjoint banks.
+  constexpr int PITCH = COLS * 4 + 32;
+  constexpr int RUNS = COLS / 4;  // 16-byte runs per staged row
+  static_assert(64 * PITCH <= S * GEO::STAGE, "64 staged rows fit the LDS stages");
   float* out = part + (int64_t)split * T * E + e0;
   char* st = smem;
   const int col_in = lane & 31;
@@ -125,9 +133,8 @@ router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ plan
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int q = tid; q < 64 * 64; q += 256) {  // 64 rows x 64 runs of 16 bytes
-      const int row = q >> 6, ch = q & 63;
+    for (int q = tid; q < 64 * RUNS; q += NT) {  // 64 rows x RUNS runs of 16 bytes
+      const int row = q / RUNS, ch = q % RUNS;
       const int64_t t = t0 + 64 * u + row;
       if (t < T) *(float4*)(out + t * E + ch * 4) = *(const float4*)(st + row * PITCH + ch * 16);
     }
@@ -745,9 +752,14 @@ hipError_t launch_router_logits(const moe_dims& dm, const Layout& L, const void*
                        n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t tiles = ((dm.T + 127) / 128) * (dm.E / 256);
-    hipLaunchKernelGGL(router_mfma_kernel, dim3((unsigned)(tiles * L.router_splits)), dim3(256), 0, s,
-                       (const bf16_t*)x, planes, part, dm.T, dm.d, dm.E, L.router_kchunk);
+    const int64_t tiles = ((dm.T + 127) / 128) * (dm.E / (128 * L.router_wn));
+    const dim3 grid((unsigned)(tiles * L.router_splits));
+    if (L.router_wn == 4)
+      hipLaunchKernelGGL(router_mfma_kernel<4>, grid, dim3(512), 0, s, (const bf16_t*)x, planes, part, dm.T, dm.d,
+                         dm.E, L.router_kchunk);
+    else
+      hipLaunchKernelGGL(router_mfma_kernel<2>, grid, dim3(256), 0, s, (const bf16_t*)x, planes, part, dm.T, dm.d,
+                         dm.E, L.router_kchunk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else if (dm.T <= 64) {
     if (dm.dtype == MOE_F32)

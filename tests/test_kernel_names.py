@@ -49,7 +49,7 @@ def test_few_token_and_fp8_kernels(lib):
     assert moe.moe_kernel_name(_dims(cfg, T=2), moe.KERNEL_FFN_DOWN, fp8=True) == "ffn_fp8_skinny_kernel<false, 2>"
     pre = syn.CONFIGS["prefill"]
     assert moe.moe_kernel_name(_dims(pre), moe.KERNEL_FFN_DOWN, fp8=True) == "ffn_fp8_stream_kernel<false, 5, 128>"
-    assert moe.moe_kernel_name(_dims(pre), moe.KERNEL_ROUTER) == "router_mfma_kernel"
+    assert moe.moe_kernel_name(_dims(pre), moe.KERNEL_ROUTER) == "router_mfma_kernel<4>"
     assert moe.moe_kernel_name(_dims(cfg), moe.KERNEL_ROUTER) == "router_small_kernel"
     assert moe.moe_kernel_name(_dims(cfg), moe.KERNEL_PERMUTE) == "permute_one_chunk_kernel"
     # up to four tokens (E > 64): top-k and dispatch in one launch
